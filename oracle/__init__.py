@@ -1,0 +1,52 @@
+"""CPU oracle for scaled dot-product attention (test infrastructure only).
+
+This package is the checker, not the product. Only the test suite, the
+``smoke()`` entry point and the ``cpu_baseline`` leg of the benchmark may
+import it. The GPU library never imports, links or calls anything in here, and
+nothing in here imports the GPU library: the two share no code.
+
+Source of the method: the codelab "Accelerate attention on GPU with cuDNN and
+TransformerEngine" (JAX on GPU, lab 5), cited below as [Attention codelab §n]
+where n is the codelab step:
+
+* §1 "How attention works": the formula softmax(Q K^T / sqrt(d_k)) V and its
+  four steps (score, scale + softmax whose weights sum to 1, attend, output
+  shaped like Q).
+* §3 "Create Q, K, V test arrays": the (B, T, N, H) / (B, S, K, H) layout.
+* §4 "Implement attention from scratch": the unfused reference computation.
+* §7 "Add a causal mask": each position attends only to itself and earlier
+  positions (a lower-triangular mask).
+* §9 "Compare MHA, GQA and MQA": K/V heads are broadcast over query heads when
+  there are fewer of them; GQA with 2 KV heads each serving 4 query heads.
+* §10 "TransformerEngine and FP8": E4M3 (4 exponent, 3 mantissa bits) for the
+  forward pass with per-tensor amax scaling.
+
+Every function is pinned by tests in ``tests/test_oracle.py`` and
+``tests/test_codecs.py`` to facts that do not come from the oracle itself
+(closed forms, invariants, brute force, library routines, hand-derived golden
+values). No function here is "parity unpinned".
+"""
+
+from .attention import attention_weights, sdpa, sdpa_rows, brute_sdpa, kv_head_of
+from .codecs import (
+    bf16_bits_to_f64,
+    f16_bits_to_f64,
+    e4m3_bits_to_f64,
+    f64_to_bf16_bits,
+    f64_to_e4m3_bits,
+    e4m3_amax_scale,
+)
+
+__all__ = [
+    "attention_weights",
+    "sdpa",
+    "sdpa_rows",
+    "brute_sdpa",
+    "kv_head_of",
+    "bf16_bits_to_f64",
+    "f16_bits_to_f64",
+    "e4m3_bits_to_f64",
+    "f64_to_bf16_bits",
+    "f64_to_e4m3_bits",
+    "e4m3_amax_scale",
+]

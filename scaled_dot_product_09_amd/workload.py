@@ -1,0 +1,140 @@
+"""Seeded synthetic inputs and the named workloads (no attention arithmetic).
+
+This module draws the inputs that both the GPU library and the CPU oracle
+receive. It holds none of the attention computation: it only draws random
+numbers, rounds them to the input number format with torch's own converters,
+and counts the work of each workload.
+
+Input recipe (the codelab "Accelerate attention on GPU with cuDNN and
+TransformerEngine" draws Q, K and V as i.i.d. standard normals in float32 in
+§3, §8, §9 and §10, then casts with ``astype(bfloat16)`` in §6):
+
+* Q, K, V i.i.d. N(0, 1), drawn as float32 from
+  ``numpy.random.Generator(PCG64)`` seeded by ``SeedSequence(seed).spawn(3)``
+  (child streams 0, 1, 2 for Q, K, V);
+* bfloat16 / float16 inputs: round to nearest even (torch's ``.to(dtype)``);
+* E4M3 inputs: per-tensor scale s = 448 / amax(|x|) in float32 (amax == 0
+  gives s = 1), codes = round-to-nearest-even of x * s as ``float8_e4m3fn``,
+  and the dequantisation factor 1 / s, also float32, goes to the kernel.
+
+Layout is contiguous (B, S, H, D), as in §3 of the codelab.
+"""
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "PAGE_SHAPES", "draw_normal", "make_inputs", "metric_flops", "io_bytes"]
+
+DTYPES = ("f32", "bf16", "f16", "e4m3")
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16,
+               "e4m3": torch.float8_e4m3fn}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "f16": 2, "e4m3": 1}
+E4M3_MAX = 448.0
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    Skv: int
+    D: int
+    causal: bool
+    seed: int
+    note: str = field(default="", compare=False)
+
+    @property
+    def scale(self):
+        """1 / sqrt(D), the codelab's default scale (§4)."""
+        return 1.0 / float(np.sqrt(self.D))
+
+    @property
+    def out_dtype(self):
+        return "bf16" if self.dtype == "e4m3" else self.dtype
+
+
+def _mqa_seq(S):
+    return Workload(f"bf16_mqa_b1_hq32_hkv1_s{S}_d128_causal", "bf16", 1, 32, 1, S, S, 128, True, S,
+                    "MQA sequence sweep; seed = S, following the codelab's key(seq_len) (§8)")
+
+
+def _mqa_batch(B):
+    return Workload(f"bf16_mqa_b{B}_hq32_hkv1_s1024_d128_causal_bsweep", "bf16", B, 32, 1, 1024, 1024, 128,
+                    True, B + 100, "MQA batch sweep; seed = B + 100, following the codelab's key(bs + 100) (§8)")
+
+
+WORKLOADS = {w.name: w for w in [
+    Workload("f32_mha_b1_h2_s128_d64", "f32", 1, 2, 2, 128, 128, 64, False, 0,
+             "fp32 correctness case; seed 0 as the codelab's key(0) (§3)"),
+    Workload("bf16_mha_b4_h16_s2048_d64_causal", "bf16", 4, 16, 16, 2048, 2048, 64, True, 2048,
+             "MHA causal, head dim 64"),
+    Workload("bf16_gqa_b2_hq32_hkv8_s4096_d128_causal", "bf16", 2, 32, 8, 4096, 4096, 128, True, 42,
+             "headline: GQA, 4 query heads per KV head; seed 42 as the codelab's GQA cell (§9)"),
+    _mqa_seq(1024), _mqa_seq(4096), _mqa_seq(16384),
+    _mqa_batch(1), _mqa_batch(8), _mqa_batch(32),
+    Workload("e4m3_mha_b4_h16_s4096_d128_causal", "e4m3", 4, 16, 16, 4096, 4096, 128, True, 9000,
+             "FP8 E4M3 inputs, bf16 output; seed 9000 as the codelab's FP8 cell (§10)"),
+]}
+
+HEADLINE = "bf16_gqa_b2_hq32_hkv8_s4096_d128_causal"
+
+# Shapes the codelab itself runs: the default (B=4, T=S=128, N=8, H=64) of §3
+# and the MHA / GQA / MQA example of §9 (q (2,64,8,64), k/v with 8, 2, 1 heads).
+PAGE_SHAPES = [
+    Workload("page_default_f32", "f32", 4, 8, 8, 128, 128, 64, False, 0),
+    Workload("page_default_bf16", "bf16", 4, 8, 8, 128, 128, 64, False, 0),
+    Workload("page_default_bf16_causal", "bf16", 4, 8, 8, 128, 128, 64, True, 0),
+    Workload("page_mha", "bf16", 2, 8, 8, 64, 64, 64, False, 42),
+    Workload("page_gqa", "bf16", 2, 8, 2, 64, 64, 64, False, 42),
+    Workload("page_mqa", "bf16", 2, 8, 1, 64, 64, 64, False, 42),
+]
+
+
+def draw_normal(seed, shapes):
+    """float32 N(0,1) arrays of the given shapes from seed's child streams."""
+    children = np.random.SeedSequence(seed).spawn(len(shapes))
+    return [np.random.Generator(np.random.PCG64(c)).standard_normal(s, dtype=np.float32)
+            for c, s in zip(children, shapes)]
+
+
+def _quantise_e4m3(x32):
+    amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0)
+    s = np.float32(1.0) if amax == 0 else np.float32(np.float32(E4M3_MAX) / amax)
+    codes = torch.from_numpy(x32 * s).to(torch.float8_e4m3fn)
+    return codes, float(np.float32(1.0) / s)
+
+
+def make_inputs(w, *, seed=None, shapes=None):
+    """Draw (q, k, v, descales) for workload ``w`` as CPU torch tensors.
+
+    ``shapes`` overrides the (B, Sq, Hq, D) / (B, Skv, Hkv, D) shapes (used by
+    tests on reduced sizes). ``descales`` is (1, 1, 1) except for E4M3 inputs.
+    """
+    seed = w.seed if seed is None else seed
+    if shapes is None:
+        shapes = [(w.B, w.Sq, w.Hq, w.D), (w.B, w.Skv, w.Hkv, w.D), (w.B, w.Skv, w.Hkv, w.D)]
+    x = draw_normal(seed, shapes)
+    if w.dtype == "e4m3":
+        qs, ks, vs = (_quantise_e4m3(a) for a in x)
+        return qs[0], ks[0], vs[0], (qs[1], ks[1], vs[1])
+    t = [torch.from_numpy(a).to(TORCH_DTYPE[w.dtype]) for a in x]
+    return t[0], t[1], t[2], (1.0, 1.0, 1.0)
+
+
+def metric_flops(B, Hq, Sq, Skv, D, causal):
+    """Attention forward FLOPs as the metric counts them: 4 B Hq Sq Skv D,
+    halved for a causal mask (QK^T and PV, 2 flops per multiply-add)."""
+    f = 4.0 * B * Hq * Sq * Skv * D
+    return f / 2 if causal else f
+
+
+def io_bytes(w):
+    """Algorithmic HBM bytes of one call: Q, K, V read once, O written once."""
+    e = ELEM_BYTES[w.dtype]
+    o = ELEM_BYTES[w.out_dtype]
+    return (w.B * w.Sq * w.Hq * w.D * (e + o) + 2 * w.B * w.Skv * w.Hkv * w.D * e)
