@@ -1,0 +1,194 @@
+"""Benchmark of the fused attention forward pass on one MI355X.
+
+One step is one call of the whole forward pass (score, mask, online
+softmax, weighted sum of V, output) over one batch of synthetic inputs that
+already sit in device memory. Default workload: GQA bf16, B=2, Hq=32, Hkv=8,
+S=4096, D=128, causal. Throughput is attention TFLOP/s with the causal
+FLOPs counted as half (4 B Hq Sq Skv D / 2), next to the MI355X dense bf16
+matrix-core peak, and next to the fp64 CPU oracle timed on a bounded sample of
+the same workload on this host's cores.
+
+Prints ONE JSON line on stdout. ``--sweep-out FILE`` additionally writes one
+JSON line per named workload (sequence and batch sweeps included) to FILE.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s and % of MFMA peak at S=4096 causal GQA bf16"
+# MI355X published dense peaks (TFLOP/s) by arithmetic type of the products.
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "f32": 157.3}
+PEAK_KIND = {"bf16": "mfma", "f16": "mfma", "e4m3": "mfma", "f32": "alu"}
+N_BUFFER_SETS = 4   # rotating input sets, so one call's inputs are not cache-warm from the last
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "scaled_dot_product_09_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload_name):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    counters, or None if there are none for this workload or the kernel
+    sources changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(workload_name)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_hash") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes")
+
+
+def cpu_baseline(w, q, k, v, desc, budget_s):
+    """Time the fp64 oracle (as it stands) on whole heads of the workload until
+    ``budget_s`` seconds of CPU work have accumulated; scale to TFLOP/s with
+    the metric's FLOP count of the heads done."""
+    import numpy as np
+    import oracle
+    from tests.helpers import to_f64
+    from scaled_dot_product_09_amd.workload import metric_flops
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    G = w.Hq // w.Hkv
+    done, elapsed = 0, 0.0
+    for b in range(w.B):
+        for hq in range(w.Hq):
+            g = hq // G
+            qh = to_f64(q[b:b + 1, :, hq:hq + 1], w.dtype, desc[0])
+            kh = to_f64(k[b:b + 1, :, g:g + 1], w.dtype, desc[1])
+            vh = to_f64(v[b:b + 1, :, g:g + 1], w.dtype, desc[2])
+            t0 = time.perf_counter()
+            oracle.sdpa(qh, kh, vh, scale=w.scale, causal=w.causal)
+            elapsed += time.perf_counter() - t0
+            done += 1
+            if elapsed >= budget_s:
+                break
+        if elapsed >= budget_s:
+            break
+    flops = metric_flops(1, done, w.Sq, w.Skv, w.D, w.causal)
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {w.B * w.Hq} (batch, query head) pairs of the same workload, full "
+                      f"Sq x Skv each, fp64 numpy, {elapsed:.1f} s; host has {os.cpu_count()} CPUs"}
+
+
+def time_workload(w, steps, warmup, rotate=True):
+    import torch
+    from scaled_dot_product_09_amd import attn, workload
+    dev = torch.device("cuda:0")
+    q, k, v, desc = workload.make_inputs(w)
+    nsets = N_BUFFER_SETS if rotate else 1
+    sets = []
+    for i in range(nsets):
+        qd, kd, vd = (x.to(dev) for x in (q, k, v))
+        od = torch.empty(q.shape, dtype=torch.bfloat16 if w.dtype == "e4m3" else q.dtype, device=dev)
+        sets.append((qd, kd, vd, od))
+    fp8 = w.dtype == "e4m3"
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        qd, kd, vd, od = sets[i % nsets]
+        attn.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=od,
+                 descales=desc if fp8 else None, stream=stream.cuda_stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        step(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    total = ev[0].elapsed_time(ev[steps])
+    return {"ms_per_step": total / steps, "median_ms": per[len(per) // 2], "min_ms": per[0],
+            "inputs": (q, k, v, desc)}
+
+
+def result_line(w, t, steps, warmup, n_gpus, cpu=None, warm=None):
+    from scaled_dot_product_09_amd.workload import metric_flops, io_bytes
+    flops = metric_flops(w.B, w.Hq, w.Sq, w.Skv, w.D, w.causal)
+    ms = t["ms_per_step"]
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    line = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": n_gpus,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq, "Skv": w.Skv,
+                   "D": w.D, "causal": w.causal, "input_dtype": w.dtype, "output_dtype": w.out_dtype,
+                   "parallelism": "single GPU", "rotating_input_sets": N_BUFFER_SETS},
+        "pct_of_peak": round(100.0 * tflops / peak, 2),
+        "median_ms": round(t["median_ms"], 5), "min_ms": round(t["min_ms"], 5),
+        "roofline": {"bound": PEAK_KIND[w.dtype], "achieved": round(tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                     "traffic": load_traffic(w.name),
+                     "algorithmic_bytes": io_bytes(w)},
+    }
+    if warm is not None:
+        line["warm_single_set_ms"] = round(warm["ms_per_step"], 5)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
+    return line
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None, help="named workload (default: the GQA headline)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--sweep-out", default=None, help="also time every named workload, JSONL to this file")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the attention kernel on a single MI355X "
+              "and has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    from scaled_dot_product_09_amd import workload
+    name = args.workload or workload.HEADLINE
+    w = workload.WORKLOADS[name]
+
+    t = time_workload(w, args.steps, args.warmup, rotate=True)
+    warm = time_workload(w, args.steps, args.warmup, rotate=False)
+    cpu = None
+    if not args.no_cpu:
+        q, k, v, desc = t["inputs"]
+        cpu = cpu_baseline(w, q, k, v, desc, args.cpu_budget)
+    line = result_line(w, t, args.steps, args.warmup, 1, cpu=cpu, warm=warm)
+
+    if args.sweep_out:
+        with open(args.sweep_out, "w") as f:
+            for n, wi in workload.WORKLOADS.items():
+                ti = time_workload(wi, args.steps, args.warmup, rotate=True)
+                f.write(json.dumps(result_line(wi, ti, args.steps, args.warmup, 1)) + "\n")
+                f.flush()
+                print(f"sweep {n}: {ti['ms_per_step']:.4f} ms", file=sys.stderr, flush=True)
+
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -27,7 +27,7 @@ Every function is pinned by tests in ``tests/test_oracle.py`` and
 values). No function here is "parity unpinned".
 """
 
-from .attention import attention_weights, sdpa, sdpa_rows, brute_sdpa, kv_head_of
+from .attention import attention_weights, sdpa, sdpa_rows, sdpa_one_row, brute_sdpa, kv_head_of
 from .codecs import (
     bf16_bits_to_f64,
     f16_bits_to_f64,
@@ -41,6 +41,7 @@ __all__ = [
     "attention_weights",
     "sdpa",
     "sdpa_rows",
+    "sdpa_one_row",
     "brute_sdpa",
     "kv_head_of",
     "bf16_bits_to_f64",

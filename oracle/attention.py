@@ -25,7 +25,7 @@ import math
 
 import numpy as np
 
-__all__ = ["kv_head_of", "attention_weights", "sdpa", "sdpa_rows", "brute_sdpa"]
+__all__ = ["kv_head_of", "attention_weights", "sdpa", "sdpa_rows", "sdpa_one_row", "brute_sdpa"]
 
 
 def kv_head_of(hq, Hq, Hkv):
@@ -123,6 +123,20 @@ def sdpa(q, k, v, *, scale, causal, row_chunk=1024):
     return out
 
 
+def sdpa_one_row(qvec, kh, vh, *, i, scale, causal):
+    """Output vector of one query vector at position ``i`` against one head.
+
+    ``qvec`` is (D,), ``kh`` and ``vh`` are that head's (Skv, D) keys and
+    values; the causal mask uses the query position ``i``. Same definition
+    as :func:`sdpa`, for one row.
+    """
+    qh = np.asarray(qvec, dtype=np.float64).reshape(1, -1)
+    kh = np.asarray(kh, dtype=np.float64)
+    vh = np.asarray(vh, dtype=np.float64)
+    p = _softmax_rows(_scores(qh, kh, scale, causal, i))
+    return (p @ vh)[0]
+
+
 def sdpa_rows(q, k, v, rows, *, scale, causal):
     """Output vectors O[b, i, hq, :] for a list of (b, i, hq) triples.
 
@@ -137,11 +151,7 @@ def sdpa_rows(q, k, v, rows, *, scale, causal):
     res = np.empty((len(rows), D), dtype=np.float64)
     for n, (b, i, hq) in enumerate(rows):
         g = kv_head_of(hq, Hq, Hkv)
-        qh = np.asarray(q[b, i:i + 1, hq, :], dtype=np.float64)
-        kh = np.asarray(k[b, :, g, :], dtype=np.float64)
-        vh = np.asarray(v[b, :, g, :], dtype=np.float64)
-        p = _softmax_rows(_scores(qh, kh, scale, causal, i))
-        res[n] = (p @ vh)[0]
+        res[n] = sdpa_one_row(q[b, i, hq, :], k[b, :, g, :], v[b, :, g, :], i=i, scale=scale, causal=causal)
     return res
 
 

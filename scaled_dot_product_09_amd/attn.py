@@ -1,0 +1,120 @@
+"""Python binding of libattn.so (argument marshalling only).
+
+Every step of the attention forward pass runs in the library's HIP kernels;
+this module only checks tensor metadata, passes device pointers, sizes and
+the current HIP stream through ctypes, and turns error codes into
+exceptions. torch provides device memory and streams, nothing else. There is
+no fallback: if the library is missing or a call is rejected, an exception is
+raised.
+
+The names follow include/attn.h: ``attn_fwd``, ``attn_fwd_fp8``,
+``attn_strerror``; :func:`fwd` is the tensor-level convenience wrapper.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libattn.so")
+
+ATTN_F32, ATTN_BF16, ATTN_F16, ATTN_FP8_E4M3 = 0, 1, 2, 3
+DTYPE_CODE = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16,
+              torch.float8_e4m3fn: ATTN_FP8_E4M3}
+STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_GROUP",
+          -4: "ATTN_ERR_HEAD_DIM", -5: "ATTN_ERR_DTYPE", -6: "ATTN_ERR_ALIGN", -7: "ATTN_ERR_ALIAS",
+          -8: "ATTN_ERR_SCALE", -9: "ATTN_ERR_HIP"}
+EXPORTS = ("attn_fwd", "attn_fwd_fp8", "attn_strerror")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib():
+    """The loaded libattn.so with argument types set (loads it once)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m scaled_dot_product_09_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        L.attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+        L.attn_fwd.restype = i
+        L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, f, f, f, vp]
+        L.attn_fwd_fp8.restype = i
+        L.attn_strerror.argtypes = [i]
+        L.attn_strerror.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def attn_strerror(status):
+    return lib().attn_strerror(int(status)).decode()
+
+
+def attn_fwd(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype, stream):
+    """Raw C call: pointers as ints, returns the status code."""
+    return lib().attn_fwd(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, float(scale), int(causal), int(dtype), stream)
+
+
+def attn_fwd_fp8(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, scale, causal, q_descale, k_descale, v_descale, stream):
+    """Raw C call of the E4M3 entry point, returns the status code."""
+    return lib().attn_fwd_fp8(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, float(scale), int(causal),
+                              float(q_descale), float(k_descale), float(v_descale), stream)
+
+
+def _check(st):
+    if st != 0:
+        raise AttnError(st, attn_strerror(st))
+
+
+def fwd(q, k, v, *, causal=False, scale=None, out=None, descales=None, stream=None):
+    """out = softmax(scale * q k^T [+ causal mask]) v on torch device tensors.
+
+    q: (B, Sq, Hq, D), k and v: (B, Skv, Hkv, D), contiguous, same dtype
+    (float32, bfloat16, float16 or float8_e4m3fn) on one GPU. ``scale``
+    defaults to 1 / sqrt(D). E4M3 inputs need ``descales`` = (q, k, v)
+    dequantisation factors and produce a bfloat16 output. The kernel is
+    enqueued on ``stream`` (default: torch's current stream); nothing is
+    synchronised.
+    """
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4:
+            raise ValueError(f"{name} must be a 4-D torch tensor (B, S, H, D)")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in DTYPE_CODE:
+        raise ValueError(f"unsupported or mixed dtypes {q.dtype}, {k.dtype}, {v.dtype}")
+    if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
+        raise ValueError(f"shape mismatch q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    code = DTYPE_CODE[q.dtype]
+    out_dtype = torch.bfloat16 if code == ATTN_FP8_E4M3 else q.dtype
+    if out is None:
+        out = torch.empty((B, Sq, Hq, D), dtype=out_dtype, device=q.device)
+    elif out.shape != q.shape or out.dtype != out_dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor with q's shape, on q's device, of the output dtype")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    if code == ATTN_FP8_E4M3:
+        if descales is None:
+            raise ValueError("E4M3 inputs need descales=(q_descale, k_descale, v_descale)")
+        st = attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, Sq, Skv, D,
+                          scale, causal, *descales, stream)
+    else:
+        st = attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, Sq, Skv, D,
+                      scale, causal, code, stream)
+    _check(st)
+    return out

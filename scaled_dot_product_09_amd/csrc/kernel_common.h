@@ -1,0 +1,83 @@
+// kernel_common.h — shared device-side definitions of the attention kernels.
+//
+// Parameter block, vector types and the workgroup -> work-item mapping used by
+// every kernel in libattn.so. Only the library's own .hip files include it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+// Everything a forward kernel needs, passed by value as one kernel argument.
+struct FwdParams {
+    const void* q;      // [B][Sq][Hq][D]
+    const void* k;      // [B][Skv][Hkv][D]
+    const void* v;      // [B][Skv][Hkv][D]
+    void* out;          // [B][Sq][Hq][D]
+    int B, Hq, Hkv, Sq, Skv;
+    int G;              // query heads per KV head, Hq / Hkv
+    int gpack;          // query heads of one KV head handled by one workgroup
+    int rows_per_wg;    // query rows per head handled by one workgroup
+    int n_row_blocks;   // ceil(Sq / rows_per_wg)
+    int n_units;        // B * Hkv * (G / gpack): (batch, KV head, head group) units
+    int xcd_remap;      // 1 when n_units % 8 == 0 (see map_workgroup)
+    float scale_log2;   // softmax scale * log2(e) (FP8: times q and k descales)
+    float out_mul;      // factor applied to the normalised output (FP8: v descale)
+};
+
+struct WorkItem {
+    int b, hkv, hq0;    // batch, KV head, first query head of the workgroup
+    int row_base;       // first query row of the workgroup
+};
+
+// Workgroup -> (unit, row block). The hardware hands workgroup i to XCD i % 8
+// (MI355X has 8 XCDs, each with its own L2). When the units split evenly over
+// the XCDs, XCD x gets a contiguous range of units, so every workgroup that
+// reads a given KV head runs on the same XCD and shares its L2. Within an
+// XCD, row blocks go out in order of decreasing causal work (the last row
+// block first) so the short ones fill the tail of the launch.
+__device__ inline WorkItem map_workgroup(const FwdParams& p, bool causal) {
+    const int pid = blockIdx.x;
+    int rb_rank, unit;
+    if (p.xcd_remap) {
+        const int per = p.n_units >> 3;
+        const int xcd = pid & 7;
+        const int slot = pid >> 3;
+        rb_rank = slot / per;
+        unit = xcd * per + (slot - rb_rank * per);
+    } else {
+        rb_rank = pid / p.n_units;
+        unit = pid - rb_rank * p.n_units;
+    }
+    const int rb = causal ? (p.n_row_blocks - 1 - rb_rank) : rb_rank;
+    const int groups = p.G / p.gpack;
+    const int hgrp = unit % groups;
+    const int t = unit / groups;
+    WorkItem w;
+    w.hkv = t % p.Hkv;
+    w.b = t / p.Hkv;
+    w.hq0 = w.hkv * p.G + hgrp * p.gpack;
+    w.row_base = rb * p.rows_per_wg;
+    return w;
+}
+
+// Maximum of a value over lanes l and l ^ 32 of a 64-wide wavefront.
+__device__ inline float xor32_max(float x) {
+    return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+
+__device__ inline float xor32_sum(float x) {
+    return x + __shfl_xor(x, 32, 64);
+}
+
+}  // namespace attn

@@ -1,0 +1,79 @@
+"""Shared test helpers: run the GPU library and the oracle on the same inputs.
+
+The oracle decodes the raw input codes (bf16 / f16 / E4M3 bits) with its own
+codecs; nothing it sees comes from the GPU path. Tolerances are the max-abs
+bounds stated for this attention forward pass: 1e-5 (fp32), 2e-2
+(bf16 / f16), 6e-2 (E4M3 inputs, against the oracle on the dequantised values).
+"""
+
+import numpy as np
+import torch
+
+import oracle
+from scaled_dot_product_09_amd import attn, workload
+
+TOL = {"f32": 1e-5, "bf16": 2e-2, "f16": 2e-2, "e4m3": 6e-2}
+
+
+def to_f64(t, dtype, descale=1.0):
+    """Decode a CPU tensor of input codes into float64 with the oracle's codecs."""
+    t = t.contiguous()
+    if dtype == "f32":
+        return t.numpy().astype(np.float64)
+    if dtype == "bf16":
+        return oracle.bf16_bits_to_f64(t.view(torch.int16).numpy())
+    if dtype == "f16":
+        return oracle.f16_bits_to_f64(t.view(torch.int16).numpy())
+    if dtype == "e4m3":
+        return oracle.e4m3_bits_to_f64(t.view(torch.uint8).numpy()) * np.float64(np.float32(descale))
+    raise ValueError(dtype)
+
+
+def out_to_f64(t):
+    """Decode the GPU output (float32, bf16 or f16 tensor) into float64."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.float32:
+        return t.numpy().astype(np.float64)
+    if t.dtype == torch.bfloat16:
+        return oracle.bf16_bits_to_f64(t.view(torch.int16).numpy())
+    if t.dtype == torch.float16:
+        return oracle.f16_bits_to_f64(t.view(torch.int16).numpy())
+    raise ValueError(t.dtype)
+
+
+def gpu_run(w, q, k, v, desc, *, scale=None, causal=None, out=None):
+    """Run the HIP library on CPU input tensors; returns the output tensor on the GPU."""
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    scale = w.scale if scale is None else scale
+    causal = w.causal if causal is None else causal
+    o = attn.fwd(qd, kd, vd, causal=causal, scale=scale, out=out,
+                 descales=desc if w.dtype == "e4m3" else None)
+    torch.cuda.synchronize()
+    return o
+
+
+def oracle_full(w, q, k, v, desc, *, scale=None, causal=None):
+    scale = w.scale if scale is None else scale
+    causal = w.causal if causal is None else causal
+    return oracle.sdpa(to_f64(q, w.dtype, desc[0]), to_f64(k, w.dtype, desc[1]), to_f64(v, w.dtype, desc[2]),
+                       scale=scale, causal=causal)
+
+
+def oracle_rows(w, q, k, v, desc, rows, *, scale=None, causal=None):
+    """Oracle output vectors for sampled (b, i, hq) rows, decoding only what they need."""
+    scale = w.scale if scale is None else scale
+    causal = w.causal if causal is None else causal
+    Hq, Hkv = q.shape[2], k.shape[2]
+    res = []
+    for (b, i, hq) in rows:
+        g = oracle.kv_head_of(hq, Hq, Hkv)
+        res.append(oracle.sdpa_one_row(to_f64(q[b, i, hq], w.dtype, desc[0]),
+                                       to_f64(k[b, :, g], w.dtype, desc[1]),
+                                       to_f64(v[b, :, g], w.dtype, desc[2]),
+                                       i=i, scale=scale, causal=causal))
+    return np.stack(res)
+
+
+def max_abs_err(got, want):
+    return float(np.max(np.abs(got - want))) if got.size else 0.0

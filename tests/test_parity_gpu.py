@@ -1,0 +1,179 @@
+"""GPU parity: the HIP library against the fp64 oracle, through the C ABI.
+
+Small cases are compared element by element with the full oracle; they span
+several K/V tiles and 32-row blocks and end in ragged tails. The named
+workloads run at their full sizes in the same launch configuration the
+benchmark times, and are checked on sampled output rows that the oracle
+computes one by one, plus invariants that hold at any size (causal row 0 is
+V[0]; GQA equals MHA with KV heads repeated; runs are deterministic; writes
+stay inside the output).
+
+Bounds (max-abs against the oracle on the decoded inputs): 1e-5 fp32,
+2e-2 bf16 / f16, 6e-2 E4M3.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from scaled_dot_product_09_amd import attn, workload
+from scaled_dot_product_09_amd.workload import Workload
+from tests import helpers
+from tests.helpers import TOL
+
+pytestmark = pytest.mark.gpu
+
+
+def W(dtype, B, Hq, Hkv, Sq, Skv, D, causal, seed=7):
+    name = f"{dtype}_b{B}_hq{Hq}_hkv{Hkv}_sq{Sq}_skv{Skv}_d{D}{'_causal' if causal else ''}"
+    return Workload(name, dtype, B, Hq, Hkv, Sq, Skv, D, causal, seed)
+
+
+SMALL = [
+    # fp32: the fp32 workload at full size, the codelab's default shape, ragged and Sq != Skv
+    workload.WORKLOADS["f32_mha_b1_h2_s128_d64"],
+    workload.PAGE_SHAPES[0],
+    W("f32", 1, 4, 2, 77, 77, 128, True),
+    W("f32", 1, 2, 1, 50, 130, 64, False),
+    W("f32", 2, 2, 2, 1, 1, 64, True),
+    # bf16 head dim 64 (BN = 128 key tiles) and 128 (BN = 64)
+    W("bf16", 1, 4, 4, 300, 300, 64, True),
+    W("bf16", 2, 4, 4, 257, 257, 64, False),
+    W("bf16", 1, 8, 2, 520, 520, 128, True),
+    W("bf16", 2, 8, 1, 333, 333, 128, True),
+    W("bf16", 1, 4, 2, 200, 200, 128, True),      # G = 2
+    W("bf16", 1, 6, 2, 150, 150, 64, True),       # G = 3
+    W("bf16", 1, 16, 2, 97, 97, 128, False),      # G = 8
+    W("bf16", 1, 1, 1, 1, 1, 64, True),
+    W("bf16", 1, 2, 2, 31, 31, 128, True),
+    W("bf16", 1, 1, 1, 33, 33, 64, False),
+    W("bf16", 1, 2, 1, 65, 65, 128, True),
+    W("bf16", 1, 1, 1, 129, 129, 64, True),
+    W("bf16", 1, 4, 2, 100, 300, 128, False),     # Sq < Skv
+    W("bf16", 1, 4, 2, 100, 300, 128, True),      # Sq < Skv, top-left causal
+    W("bf16", 1, 4, 2, 300, 100, 64, True),       # Sq > Skv
+    *workload.PAGE_SHAPES[1:],
+    # f16
+    W("f16", 1, 8, 2, 300, 300, 128, True),
+    W("f16", 1, 4, 4, 200, 200, 64, False),
+    # E4M3 inputs, bf16 output
+    W("e4m3", 1, 4, 4, 400, 400, 128, True),
+    W("e4m3", 1, 8, 2, 300, 300, 64, False),
+    W("e4m3", 1, 2, 1, 70, 70, 128, True),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_parity_small(w):
+    print(f"case {w.name}", flush=True)
+    q, k, v, desc = workload.make_inputs(w)
+    got = helpers.out_to_f64(helpers.gpu_run(w, q, k, v, desc))
+    want = helpers.oracle_full(w, q, k, v, desc)
+    assert got.shape == want.shape
+    err = helpers.max_abs_err(got, want)
+    print(f"  max-abs {err:.3e}", flush=True)
+    assert err <= TOL[w.dtype], err
+
+
+def test_scale_zero_and_negative():
+    w = W("bf16", 1, 4, 2, 130, 130, 128, True)
+    q, k, v, desc = workload.make_inputs(w)
+    for scale in (0.0, -0.2):
+        got = helpers.out_to_f64(helpers.gpu_run(w, q, k, v, desc, scale=scale))
+        want = helpers.oracle_full(w, q, k, v, desc, scale=scale)
+        assert helpers.max_abs_err(got, want) <= TOL["bf16"]
+
+
+def _sample_rows(w, rng, n_random=24):
+    rows = set()
+    S = w.Sq
+    fixed_i = [i for i in (0, 1, 2, 31, 32, 63, 64, 127, 128, S // 2, S - 2, S - 1) if 0 <= i < S]
+    for b in {0, w.B - 1}:
+        for hq in {0, w.Hq - 1, w.Hq // 2}:
+            for i in fixed_i:
+                rows.add((b, i, hq))
+    for _ in range(n_random):
+        rows.add((int(rng.integers(w.B)), int(rng.integers(S)), int(rng.integers(w.Hq))))
+    return sorted(rows)
+
+
+FULL = [n for n in workload.WORKLOADS if not n.startswith("f32")]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_parity_full_size_sampled(name):
+    w = workload.WORKLOADS[name]
+    print(f"case {name} (full size, sampled rows)", flush=True)
+    q, k, v, desc = workload.make_inputs(w)
+    o = helpers.gpu_run(w, q, k, v, desc)
+    rows = _sample_rows(w, np.random.default_rng(w.seed))
+    idx = torch.tensor(rows)
+    got_rows = helpers.out_to_f64(o[idx[:, 0], idx[:, 1], idx[:, 2]])
+    want = helpers.oracle_rows(w, q, k, v, desc, rows)
+    err = helpers.max_abs_err(got_rows, want)
+    print(f"  {len(rows)} rows, max-abs {err:.3e}", flush=True)
+    assert err <= TOL[w.dtype], err
+    if w.causal and w.dtype in ("bf16", "f16"):
+        # Causal row 0 sees only key 0: weight exactly 1, so the output is V[0] bit for bit.
+        g = np.arange(w.Hq) // (w.Hq // w.Hkv)
+        v0 = v[:, 0][:, torch.from_numpy(g)]
+        assert torch.equal(o[:, 0].cpu(), v0)
+
+
+def test_gqa_equals_repeated_mha_bitwise():
+    w = W("bf16", 2, 8, 2, 260, 260, 128, True)
+    q, k, v, desc = workload.make_inputs(w)
+    a = helpers.gpu_run(w, q, k, v, desc)
+    kr, vr = (x.repeat_interleave(4, dim=2).contiguous() for x in (k, v))
+    b = helpers.gpu_run(W("bf16", 2, 8, 8, 260, 260, 128, True), q, kr, vr, desc)
+    assert torch.equal(a, b)
+
+
+def test_deterministic_and_canaries():
+    w = workload.WORKLOADS["bf16_gqa_b2_hq32_hkv8_s4096_d128_causal"]
+    q, k, v, desc = workload.make_inputs(w, shapes=[(1, 700, 8, 128), (1, 700, 2, 128), (1, 700, 2, 128)])
+    n, pad = q.numel(), 4096
+    buf = torch.full((n + 2 * pad,), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    out = buf[pad:pad + n].view(q.shape)
+    helpers.gpu_run(w, q, k, v, desc, out=out)
+    first = out.clone()
+    helpers.gpu_run(w, q, k, v, desc, out=out)
+    assert torch.equal(first, out)
+    assert torch.isnan(buf[:pad]).all() and torch.isnan(buf[pad + n:]).all()
+    assert not torch.isnan(out).any()
+
+
+def test_constant_v_gives_constant_output():
+    w = W("bf16", 1, 4, 2, 200, 200, 128, True)
+    q, k, _, desc = workload.make_inputs(w)
+    row = torch.randn(128, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    v = row.expand(1, 200, 2, 128).contiguous()
+    o = helpers.gpu_run(w, q, k, v, desc).cpu().float()
+    r = row.float().expand_as(o)
+    # A convex combination of equal rows: within one bf16 ulp of the row.
+    assert torch.all((o - r).abs() <= r.abs() * 2.0 ** -7)
+
+
+def test_non_default_stream():
+    w = W("bf16", 1, 4, 2, 150, 150, 64, True)
+    q, k, v, desc = workload.make_inputs(w)
+    s = torch.cuda.Stream()
+    qd, kd, vd = (x.cuda() for x in (q, k, v))
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        o = attn.fwd(qd, kd, vd, causal=True)
+    s.synchronize()
+    want = helpers.oracle_full(w, q, k, v, desc)
+    assert helpers.max_abs_err(helpers.out_to_f64(o), want) <= TOL["bf16"]
+
+
+def test_gpu_argument_errors_raise():
+    x = torch.zeros(1, 8, 2, 96, dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(attn.AttnError) as e:
+        attn.fwd(x, x, x)
+    assert e.value.status == -4
+    q = torch.zeros(1, 8, 3, 64, dtype=torch.bfloat16, device="cuda:0")
+    kv = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(attn.AttnError) as e:
+        attn.fwd(q, kv, kv)
+    assert e.value.status == -3
