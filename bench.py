@@ -160,6 +160,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--sweep-out", default=None, help="also time every named workload, JSONL to this file")
+    ap.add_argument("--copy-ref-mib", type=int, default=0,
+                    help="first run a plain device-to-device copy of this many MiB (untimed), a "
+                         "reference dispatch of known size for scaling hardware byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -170,6 +173,15 @@ def main():
     from scaled_dot_product_09_amd import workload
     name = args.workload or workload.HEADLINE
     w = workload.WORKLOADS[name]
+
+    if args.copy_ref_mib:
+        import torch
+        n = args.copy_ref_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     t = time_workload(w, args.steps, args.warmup, rotate=True)
     warm = time_workload(w, args.steps, args.warmup, rotate=False)

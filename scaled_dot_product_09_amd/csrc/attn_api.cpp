@@ -7,6 +7,8 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "../../include/attn.h"
 #include "kernel_common.h"
@@ -15,6 +17,7 @@ namespace attn {
 hipError_t launch_fwd_mfma(const FwdParams& p, int D, bool is_bf16, bool causal, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int D, bool causal, hipStream_t stream);
 hipError_t launch_fwd_fp8(const FwdParams& p, int D, bool causal, hipStream_t stream);
+hipError_t launch_fwd_rb2(const FwdParams& p, int D, int dtype, bool causal, hipStream_t stream);
 }
 
 namespace {
@@ -53,15 +56,16 @@ int validate(const void* q, const void* k, const void* v, const void* out,
 
 attn::FwdParams make_params(const void* q, const void* k, const void* v, void* out,
                             int B, int Hq, int Hkv, int Sq, int Skv, float scale_log2, float out_mul,
-                            bool mfma) {
+                            bool mfma, int rows_per_wave) {
     attn::FwdParams p;
     p.q = q; p.k = k; p.v = v; p.out = out;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Sq = Sq; p.Skv = Skv;
     p.G = Hq / Hkv;
-    // A workgroup of four 32-row waves shares one KV head between gpack query
-    // heads (the largest of 4, 2, 1 dividing G) and 4 / gpack row blocks.
+    // A workgroup of four waves shares one KV head between gpack query heads
+    // (the largest of 4, 2, 1 dividing G) and 4 / gpack row blocks of
+    // rows_per_wave rows each.
     p.gpack = mfma ? ((p.G % 4 == 0) ? 4 : (p.G % 2 == 0) ? 2 : 1) : 1;
-    p.rows_per_wg = 32 * (4 / p.gpack);
+    p.rows_per_wg = rows_per_wave * (4 / p.gpack);
     p.n_row_blocks = (Sq + p.rows_per_wg - 1) / p.rows_per_wg;
     p.n_units = B * Hkv * (p.G / p.gpack);
     p.xcd_remap = (p.n_units % 8 == 0) ? 1 : 0;
@@ -71,6 +75,24 @@ attn::FwdParams make_params(const void* q, const void* k, const void* v, void* o
 }
 
 const float kLog2e = 1.4426950408889634f;
+
+// The kernels never see a zero score multiplier: scale 0 (every visible key
+// weighted equally) is run with multiplier 2^-100 instead. For any score
+// |s| < 2^35, exp2(s * 2^-100) rounds to exactly 1.0f, so the weights, and
+// the result, are those of scale 0; and masked scores (+-inf) still map to
+// -inf, which lets the kernels mask with a single select.
+float nonzero_multiplier(float c) { return c == 0.0f ? 0x1p-100f : c; }
+
+// Matrix-core kernel choice: 32 query rows per wave (two waves per SIMD) by
+// default; 64 rows per wave (one wave per SIMD, half the LDS traffic per
+// flop) only on request, since it measures slower on every shape so far.
+// ATTN_ROWS_PER_WAVE=32 or 64 in the environment selects one explicitly
+// (the tests use it to cover both kernels on every shape).
+int rows_per_wave() {
+    const char* e = getenv("ATTN_ROWS_PER_WAVE");
+    if (e && strcmp(e, "64") == 0) return 64;
+    return 32;
+}
 
 }  // namespace
 
@@ -86,11 +108,18 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out,
     bool noop;
     const int st = validate(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, scale, eb, eb, &noop);
     if (st != ATTN_OK || noop) return st;
-    const attn::FwdParams p = make_params(q, k, v, out, B, Hq, Hkv, Sq, Skv, scale * kLog2e, 1.0f,
-                                          dtype != ATTN_F32);
     hipError_t e;
-    if (dtype == ATTN_F32) e = attn::launch_fwd_f32(p, D, causal != 0, stream);
-    else e = attn::launch_fwd_mfma(p, D, dtype == ATTN_BF16, causal != 0, stream);
+    if (dtype == ATTN_F32) {
+        const attn::FwdParams p = make_params(q, k, v, out, B, Hq, Hkv, Sq, Skv,
+                                              nonzero_multiplier(scale * kLog2e), 1.0f, false, 32);
+        e = attn::launch_fwd_f32(p, D, causal != 0, stream);
+    } else {
+        const int rpw = rows_per_wave();
+        const attn::FwdParams p = make_params(q, k, v, out, B, Hq, Hkv, Sq, Skv,
+                                              nonzero_multiplier(scale * kLog2e), 1.0f, true, rpw);
+        e = rpw == 64 ? attn::launch_fwd_rb2(p, D, dtype, causal != 0, stream)
+                      : attn::launch_fwd_mfma(p, D, dtype == ATTN_BF16, causal != 0, stream);
+    }
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -106,8 +135,11 @@ extern "C" int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o
     if (noop) return ATTN_OK;
     const float sl2 = scale * q_descale * k_descale * kLog2e;
     if (!isfinite(sl2)) return ATTN_ERR_SCALE;
-    const attn::FwdParams p = make_params(q, k, v, out, B, Hq, Hkv, Sq, Skv, sl2, v_descale, true);
-    const hipError_t e = attn::launch_fwd_fp8(p, D, causal != 0, stream);
+    const int rpw = rows_per_wave();
+    const attn::FwdParams p = make_params(q, k, v, out, B, Hq, Hkv, Sq, Skv, nonzero_multiplier(sl2),
+                                          v_descale, true, rpw);
+    const hipError_t e = rpw == 64 ? attn::launch_fwd_rb2(p, D, ATTN_FP8_E4M3, causal != 0, stream)
+                                   : attn::launch_fwd_fp8(p, D, causal != 0, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

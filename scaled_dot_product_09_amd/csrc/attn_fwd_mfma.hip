@@ -14,131 +14,36 @@
 // and P V on the bf16 instruction, because E4M3 weights would cost up to
 // 2^-4 relative error per weight on rows that see only a few keys).
 //
-// Design (one workgroup = 4 wavefronts of 64 lanes):
+// Design (one workgroup = 4 wavefronts of 64 lanes, two workgroups per CU):
 //   * Each wave owns 32 query rows of one query head. A workgroup holds
 //     `gpack` query heads that read the same KV head, 4 / gpack row blocks of
 //     32 rows each, so every K/V tile staged in LDS serves 128 query rows.
+//   * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4,
+//     no register staging), double-buffered: tile j+1 is in flight while
+//     tile j is computed, with one barrier per tile. 16-byte chunks are
+//     XOR-swizzled per row so the operand reads below are bank-conflict free.
 //   * Scores are computed transposed, S^T = K Q^T: lane (h = lane / 32,
 //     n = lane % 32) then holds 16 scores of query n per 32-key block, so a
-//     row's max needs only one exchange between lanes n and n + 32, and its
-//     sum is kept per lane until the end.
+//     row's max needs one exchange between lanes n and n + 32, and its sum
+//     stays per lane until the end.
 //   * O^T = V^T P^T. The score accumulator is used directly as the P operand:
 //     the MFMA sums over k in any order as long as both operands agree, so
-//     V is read from LDS with the same key permutation (V sits in LDS as
-//     [key/4][d][key%4], which makes that read one 8-byte access per 4 keys).
-//   * Online softmax in the exp2 domain with the scale folded into one
-//     multiply; the running max is only raised when it grows by more than 8
-//     (a factor 2^8): numerator and denominator share the stale max, so the
-//     result is the same, and weights up to 256 are harmless in bf16 / f16.
-//   * K/V tiles are double-buffered: the next tile's global loads are issued
-//     before the current tile's math and written to LDS after it, with one
-//     barrier per tile.
+//     the V operand is gathered with the same key order by the gfx950 LDS
+//     transpose read (ds_read_b64_tr_b16) from row-major V.
+//   * Online softmax in the exp2 domain: one FMA (scale folded in) and one
+//     v_exp per score; row max by v_max3; row sums by v_dot2 over the
+//     rounded weights, so the normalisation uses exactly the weights that
+//     multiplied V. The running max is only raised when it grows by more
+//     than 8 (a factor 2^8): numerator and denominator share the stale max,
+//     so the result is unchanged, and weights up to 256 are harmless in
+//     bf16 / f16.
 //   * Causal: tiles wholly above the workgroup's diagonal are never loaded;
-//     32-key blocks wholly above a wave's diagonal skip their MFMAs.
+//     32-key blocks wholly above a wave's diagonal skip their MFMAs; only
+//     blocks crossing the diagonal (or the end of the keys) are masked.
 
-#include "kernel_common.h"
+#include "mfma_common.h"
 
 namespace attn {
-
-typedef uint8_t fp8_t;   // one OCP E4M3 code
-
-__device__ inline uint32_t pack2_bf16(float lo, float hi) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
-}
-
-__device__ inline uint32_t pack2_f16(float lo, float hi) {
-    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
-}
-
-// Per input type: the score product (QK), the weight product (PV) and the
-// conversions around them.
-template <typename T> struct Traits;
-
-template <> struct Traits<__bf16> {
-    static constexpr int IN_BYTES = 2;
-    static constexpr int QK_LANE_BYTES = 16;    // bytes of one operand per lane per k-step
-    static constexpr int QK_K = 16;             // contraction length of one QK MFMA
-    using qk_frag = bf16x8;
-    using pv_frag = bf16x8;
-    using out_t = __bf16;
-    __device__ static inline f32x16 qk(qk_frag a, qk_frag b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
-    __device__ static inline f32x16 pv(pv_frag a, pv_frag b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
-    __device__ static inline uint32_t pack_p(float lo, float hi) { return pack2_bf16(lo, hi); }
-    __device__ static inline uint32_t pack_out(float lo, float hi) { return pack2_bf16(lo, hi); }
-};
-
-template <> struct Traits<_Float16> {
-    static constexpr int IN_BYTES = 2;
-    static constexpr int QK_LANE_BYTES = 16;
-    static constexpr int QK_K = 16;
-    using qk_frag = f16x8;
-    using pv_frag = f16x8;
-    using out_t = _Float16;
-    __device__ static inline f32x16 qk(qk_frag a, qk_frag b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-    }
-    __device__ static inline f32x16 pv(pv_frag a, pv_frag b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-    }
-    __device__ static inline uint32_t pack_p(float lo, float hi) { return pack2_f16(lo, hi); }
-    __device__ static inline uint32_t pack_out(float lo, float hi) { return pack2_f16(lo, hi); }
-};
-
-template <> struct Traits<fp8_t> {
-    static constexpr int IN_BYTES = 1;
-    static constexpr int QK_LANE_BYTES = 32;
-    static constexpr int QK_K = 64;
-    using qk_frag = i32x8;
-    using pv_frag = bf16x8;
-    using out_t = __bf16;
-    __device__ static inline f32x16 qk(qk_frag a, qk_frag b, f32x16 c) {
-        // Both operands E4M3 (format code 0), no block scales.
-        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-    }
-    __device__ static inline f32x16 pv(pv_frag a, pv_frag b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
-    __device__ static inline uint32_t pack_p(float lo, float hi) { return pack2_bf16(lo, hi); }
-    __device__ static inline uint32_t pack_out(float lo, float hi) { return pack2_bf16(lo, hi); }
-};
-
-// Swizzle of 16-byte chunks inside a K row in LDS: chunk c of row r is stored
-// at chunk position c ^ kswz(r). Sixteen consecutive rows read at the same c
-// then land in sixteen different 16-byte bank groups (64 banks x 4 bytes).
-template <int NCK>
-__device__ inline int kswz(int r) {
-    return (r / (16 / NCK)) % NCK;
-}
-
-// Eight consecutive V elements of one key row, as four 32-bit words each
-// holding two 16-bit values of the PV operand type.
-template <typename T>
-__device__ inline u32x4 load_v8(const T* src, bool ok);
-
-template <> __device__ inline u32x4 load_v8<__bf16>(const __bf16* src, bool ok) {
-    return ok ? *(const u32x4*)src : (u32x4){0, 0, 0, 0};
-}
-template <> __device__ inline u32x4 load_v8<_Float16>(const _Float16* src, bool ok) {
-    return ok ? *(const u32x4*)src : (u32x4){0, 0, 0, 0};
-}
-// E4M3 -> bf16 is exact (3 mantissa bits and exponents 2^-9 .. 2^8 all fit).
-template <> __device__ inline u32x4 load_v8<fp8_t>(const fp8_t* src, bool ok) {
-    const u32x2 x = ok ? *(const u32x2*)src : (u32x2){0, 0};
-    u32x4 r;
-    for (int w = 0; w < 2; ++w) {
-        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[w], false);
-        const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[w], true);
-        r[2 * w] = pack2_bf16(a[0], a[1]);
-        r[2 * w + 1] = pack2_bf16(b[0], b[1]);
-    }
-    return r;
-}
 
 template <typename T, int D, int BN, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
@@ -146,22 +51,21 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
     using qk_frag = typename Tr::qk_frag;
     using pv_frag = typename Tr::pv_frag;
     using out_t = typename Tr::out_t;
-    constexpr int ROW_BYTES = D * Tr::IN_BYTES;       // one K / Q row
-    constexpr int NCK = ROW_BYTES / 16;               // 16-byte chunks per K row
+    constexpr int KROWB = D * Tr::IN_BYTES;           // bytes of one K / Q row
+    constexpr int VROWB = D * 2;                      // bytes of one V row in LDS (16-bit)
+    constexpr int NCK = KROWB / 16;                   // 16-byte chunks per K row
+    constexpr int NCV = VROWB / 16;
     constexpr int CH = Tr::QK_LANE_BYTES / 16;        // chunks per lane per k-step
     constexpr int KSTEPS = D / Tr::QK_K;              // k-steps of the score product
     constexpr int NKB = BN / 32;                      // 32-key blocks per tile
     constexpr int NDB = D / 32;                       // 32-wide column blocks of O
-    constexpr int K_LD = (BN * NCK) / 256;            // K chunks staged per thread
-    static_assert(K_LD * 256 == BN * NCK, "K tile must split evenly over 256 threads");
-    static_assert((BN / 4) * (D / 8) == 256, "V tile must be one 4 x 8 unit per thread");
+    constexpr int KTILE = BN * KROWB, VTILE = BN * VROWB;
 
-    __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][BN * ROW_BYTES];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][BN * D];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * (KTILE + VTILE)];   // K0 K1 V0 V1
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;              // which half of the wave
     const int n = lane & 31;              // query column inside the wave's 32 rows
 
@@ -173,8 +77,9 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
     const size_t kstride = (size_t)p.Hkv * D;
 
     const T* qbase = (const T*)p.q + ((size_t)wi.b * Sq * p.Hq + hq) * D;
-    const T* kbase = (const T*)p.k + ((size_t)wi.b * Skv * p.Hkv + wi.hkv) * D;
-    const T* vbase = (const T*)p.v + ((size_t)wi.b * Skv * p.Hkv + wi.hkv) * D;
+    const uint8_t* kbase = (const uint8_t*)((const T*)p.k + ((size_t)wi.b * Skv * p.Hkv + wi.hkv) * D);
+    const uint8_t* vbase = (const uint8_t*)((const T*)p.v + ((size_t)wi.b * Skv * p.Hkv + wi.hkv) * D);
+    const size_t kstride_b = kstride * Tr::IN_BYTES;
 
     // Q^T operand, kept in registers for the whole key loop: lane (h, n) holds
     // bytes [(2 ks + h) * QK_LANE_BYTES, +QK_LANE_BYTES) of row q0 + n.
@@ -202,144 +107,283 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
         const int last_row = min(wi.row_base + p.rows_per_wg, Sq) - 1;
         n_tiles = min(n_tiles, last_row / BN + 1);
     }
+    n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
 
-    // ---- tile staging: global -> registers -> LDS ------------------------
-    u32x4 kreg[K_LD];
-    u32x4 vreg[4];
-    auto load_tile = [&](int j) {
-        const int key0 = j * BN;
-        for (int i = 0; i < K_LD; ++i) {
-            const int id = i * 256 + tid;
-            const int r = id / NCK, c = id % NCK;
-            const int key = key0 + r;
-            kreg[i] = (u32x4){0, 0, 0, 0};
-            if (key < Skv) kreg[i] = *(const u32x4*)((const uint8_t*)(kbase + key * kstride) + c * 16);
-        }
-        const int g = tid / (D / 8), c = tid % (D / 8);
-        for (int r = 0; r < 4; ++r) {
-            const int key = key0 + 4 * g + r;
-            vreg[r] = load_v8<T>(vbase + key * kstride + c * 8, key < Skv);
+    // ---- tile staging ------------------------------------------------------
+    // LDS: two K tiles and two V tiles. The loop below is software-pipelined
+    // one tile deep (the scores of tile j+1 are computed while the weights of
+    // tile j are formed), so K runs one tile ahead of V: iteration j reads
+    // K(j+1) and V(j) and, meanwhile, loads K(j+2) into the K buffer K(j)
+    // used and V(j+1) into the V buffer V(j-1) used.
+    uint8_t* const kbuf0 = lds;
+    uint8_t* const kbuf1 = lds + KTILE;
+    uint8_t* const vbuf0 = lds + 2 * KTILE;
+    uint8_t* const vbuf1 = lds + 2 * KTILE + VTILE;
+    // FP8: V is widened to bf16 in registers (exact) and written to LDS by
+    // the threads; 8 values (one 16-byte chunk) per thread and step.
+    constexpr int V_ST = Tr::V_DMA ? 1 : (BN * D / 8) / 256;
+    u32x2 vstage[V_ST];
+    TileDma<KROWB, BN> kdma;
+    TileDma<VROWB, BN> vdma;
+    kdma.init(wave, lane, (uint32_t)kstride_b, true);
+    if constexpr (Tr::V_DMA) vdma.init(wave, lane, (uint32_t)kstride_b, false);
+    auto issue_k = [&](int j, uint8_t* kt) { kdma.issue(kbase, kstride_b, j * BN, Skv, kt, wave); };
+    auto issue_v = [&](int j, uint8_t* vt) {
+        if constexpr (Tr::V_DMA) {
+            vdma.issue(vbase, kstride_b, j * BN, Skv, vt, wave);
+        } else {
+            for (int u = 0; u < V_ST; ++u) {
+                const int id = u * 256 + tid;
+                const int r = id / (D / 8), c = id % (D / 8);
+                const int key = min(j * BN + r, Skv - 1);
+                vstage[u] = *(const u32x2*)(vbase + key * kstride_b + c * 8);
+            }
         }
     };
-    auto store_tile = [&](int buf) {
-        for (int i = 0; i < K_LD; ++i) {
-            const int id = i * 256 + tid;
-            const int r = id / NCK, c = id % NCK;
-            *(u32x4*)(&lds_k[buf][r * ROW_BYTES + ((c ^ kswz<NCK>(r)) * 16)]) = kreg[i];
+    auto finish_v = [&](uint8_t* vt) {   // FP8 only: widen the staged V and write it
+        if constexpr (!Tr::V_DMA) {
+            for (int u = 0; u < V_ST; ++u) {
+                const int id = u * 256 + tid;
+                const int r = id / (D / 8), c = id % (D / 8);
+                u32x4 w;
+                for (int e = 0; e < 2; ++e) {
+                    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)vstage[u][e], false);
+                    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)vstage[u][e], true);
+                    w[2 * e] = pack2_bf16(a[0], a[1]);
+                    w[2 * e + 1] = pack2_bf16(b[0], b[1]);
+                }
+                *(u32x4*)(vt + r * VROWB + ((c ^ v_swz<NCV>(r)) * 16)) = w;
+            }
         }
-        // V: this thread holds keys 4g..4g+3 at columns 8c..8c+7 (16-bit
-        // values). Write them as [g][d][4 keys]: one column's four keys become
-        // two 32-bit words.
-        const int g = tid / (D / 8), c = tid % (D / 8);
-        u32x4 outw[4];
-        for (int e = 0; e < 4; ++e) {          // column pair (8c + 2e, 8c + 2e + 1)
-            const uint32_t a0 = vreg[0][e], a1 = vreg[1][e], a2 = vreg[2][e], a3 = vreg[3][e];
-            const uint32_t lo01 = __builtin_amdgcn_perm(a1, a0, 0x05040100u);   // column 8c+2e
-            const uint32_t lo23 = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
-            const uint32_t hi01 = __builtin_amdgcn_perm(a1, a0, 0x07060302u);   // column 8c+2e+1
-            const uint32_t hi23 = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
-            outw[e] = (u32x4){lo01, lo23, hi01, hi23};
-        }
-        uint16_t* dst = &lds_v[buf][(g * D + 8 * c) * 4];
-        for (int e = 0; e < 4; ++e) *(u32x4*)(dst + e * 8) = outw[e];
     };
 
     // ---- running softmax state (per lane: query n, partial over its keys) --
     f32x16 oacc[NDB];
     for (int db = 0; db < NDB; ++db)
         for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-    float m_run = -INFINITY;   // running max in the log2 domain (same on both halves)
+    float m_run = -INFINITY;   // running max of scale*log2(e)*score (same on both halves)
     float l_part = 0.f;        // this lane's share of the running denominator
 
     const float c_log2 = p.scale_log2;
+    const bool c_nonneg = c_log2 >= 0.f;
     const int qrow = q0 + n;
     const int wave_last_row = q0 + 31;
 
-    load_tile(0);
-    store_tile(0);
+    // Per-lane constants of the V transpose read (see load_v).
+    const int L16 = lane & 15;                 // lane inside its 16-lane group
+    const int G16 = (lane >> 4) & 1;           // which 16 columns of a 32-column block
+    const int v_row_in = 4 * h + (L16 >> 2);   // key row offset this lane addresses
+    const int v_col_b = 32 * G16 + 8 * (L16 & 3);   // byte offset inside a 64-byte column block
+    // Byte offsets of this lane's operand reads inside a K / V tile. The
+    // swizzle masks depend only on lane bits: K row kb*32 + n has mask
+    // k_swz(n), and the V rows base + 4h + L16/4 (base a multiple of 16) have
+    // mask v_swz(4h + L16/4); so every read below is a lane base plus a
+    // compile-time offset.
+    // K row kb*32 + n, 16-byte chunk (2 ks + h) * CH + t sits at byte
+    // n * KROWB + ((((2 ks + h) * CH + t) ^ k_swz(n)) << 4): the k-step only
+    // flips bits of the chunk index above those of (h, t), so the offset is
+    // k_lane_base ^ (ks * 32 * CH) plus t * 16 (t ^ mask bit, folded below).
+    const int k_sw = k_swz<NCK>(n);
+    const uint32_t k_lane_base0 = n * KROWB + ((((h * CH) ^ k_sw)) << 4);
+    const uint32_t k_lane_base1 = n * KROWB + ((((h * CH + (CH - 1)) ^ k_sw)) << 4);
+    int v_lane_off[NDB];
+    for (int db = 0; db < NDB; ++db) {
+        const int cb = db * 64 + v_col_b;
+        v_lane_off[db] = v_row_in * VROWB + ((((cb >> 4) ^ v_swz<NCV>(v_row_in)) << 4) | (cb & 15));
+    }
 
-    for (int j = 0; j < n_tiles; ++j) {
-        const int buf = j & 1;
-        __syncthreads();
-        if (j + 1 < n_tiles) load_tile(j + 1);
+    // Operand fetches from the LDS tiles (lane-base + compile-time offsets).
+    auto load_k = [&](const uint8_t* kt, int kb, int ks) -> qk_frag {
+        const uint8_t* kr = kt + kb * 32 * KROWB;
+        if constexpr (CH == 1) {
+            return __builtin_bit_cast(qk_frag, *(const u32x4*)(kr + (k_lane_base0 ^ (ks * 32 * CH))));
+        } else {
+            const u32x4 x0 = *(const u32x4*)(kr + (k_lane_base0 ^ (ks * 32 * CH)));
+            const u32x4 x1 = *(const u32x4*)(kr + (k_lane_base1 ^ (ks * 32 * CH)));
+            return __builtin_bit_cast(qk_frag, (i32x8){(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                                                       (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]});
+        }
+    };
+    // V operand of the PV step for keys kb*32 + 16 s2 + {0..15} and output
+    // columns 32 db + {0..31}. Lane (h, n) needs V[key][32 db + n] for keys
+    // base + 4h + {0..3} (frag elements 0..3) and base + 8 + 4h + {0..3}
+    // (elements 4..7). The transpose read hands lane i of a 16-lane group
+    // element i % 4 of the 8 bytes addressed by lanes 4 s + i / 4 (s = 0..3),
+    // so lane L addresses key row base + 4h + L / 4 at columns
+    // 32 db + 16 G16 + 4 (L % 4) .. +3 (v_lane_off holds that offset).
+    auto load_v = [&](const uint8_t* vt, int kb, int s2, int db) -> pv_frag {
+        const uint8_t* a_lo = vt + (kb * 32 + 16 * s2) * VROWB + v_lane_off[db];
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a_lo));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(a_lo + 8 * VROWB));
+        return __builtin_bit_cast(pv_frag, (s16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    };
 
-        // ---- S^T = K Q^T for each 32-key block -------------------------
-        f32x16 s[NKB];
-        bool active[NKB];
-        for (int kb = 0; kb < NKB; ++kb) {
-            const int kstart = j * BN + kb * 32;
-            active[kb] = kstart < Skv && (!CAUSAL || kstart <= wave_last_row);
+    // S^T = K Q^T for one tile (all 32-key blocks), K operands fetched one
+    // k-step ahead.
+    auto qk_tile = [&](const uint8_t* kt, f32x16 (&s)[NKB]) {
+        for (int kb = 0; kb < NKB; ++kb)
             for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-            if (!active[kb]) continue;
-            const int row = kb * 32 + n;                      // lane's key row (A operand)
-            const uint8_t* krow = &lds_k[buf][row * ROW_BYTES];
-            const int sw = kswz<NCK>(row);
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                qk_frag a;
-                if constexpr (CH == 1) {
-                    a = __builtin_bit_cast(qk_frag, *(const u32x4*)(krow + (((2 * ks + h) ^ sw) * 16)));
-                } else {
-                    const u32x4 x0 = *(const u32x4*)(krow + ((((2 * ks + h) * 2) ^ sw) * 16));
-                    const u32x4 x1 = *(const u32x4*)(krow + ((((2 * ks + h) * 2 + 1) ^ sw) * 16));
-                    a = __builtin_bit_cast(qk_frag, (i32x8){(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
-                                                            (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]});
-                }
-                s[kb] = Tr::qk(a, qf[ks], s[kb]);
-            }
+        qk_frag cur[NKB], nxt[NKB];
+        for (int kb = 0; kb < NKB; ++kb) cur[kb] = load_k(kt, kb, 0);
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            if (ks + 1 < KSTEPS)
+                for (int kb = 0; kb < NKB; ++kb) nxt[kb] = load_k(kt, kb, ks + 1);
+            for (int kb = 0; kb < NKB; ++kb) s[kb] = Tr::qk(cur[kb], qf[ks], s[kb]);
+            if (ks + 1 < KSTEPS)
+                for (int kb = 0; kb < NKB; ++kb) cur[kb] = nxt[kb];
         }
+    };
 
-        // ---- scale, mask, online softmax ---------------------------------
-        float mloc = -INFINITY;
+    // Row max of one tile's scores and the lazy rescale of O and l; returns
+    // -m (the exponent offset). Scores of keys past the end or above the
+    // causal diagonal are first replaced by -inf (scale >= 0) or +inf
+    // (scale < 0), so that c * s = -inf for them; the test costs a few
+    // instructions per 32-key block and is skipped (wave-uniformly) wherever
+    // no key of the block is hidden from any row of the wave.
+    auto tile_max = [&](f32x16 (&s)[NKB], int j) -> float {
+        const float masked = c_nonneg ? -INFINITY : INFINITY;
         for (int kb = 0; kb < NKB; ++kb) {
-            if (!active[kb]) continue;
-            const int kstart = j * BN + kb * 32;
-            const bool need_mask = (CAUSAL && kstart + 31 > q0) || (kstart + 32 > Skv);
-            for (int i = 0; i < 16; ++i) {
-                float x = s[kb][i] * c_log2;
-                if (need_mask) {
-                    const int key = kstart + 8 * (i >> 2) + 4 * h + (i & 3);
-                    if (key >= Skv || (CAUSAL && key > qrow)) x = -INFINITY;
-                }
-                s[kb][i] = x;
-                mloc = fmaxf(mloc, x);
+            const int kbase_h = j * BN + kb * 32 + 4 * h;       // key of element i: kbase_h + koff(i)
+            int lim = Skv - 1 - kbase_h;                         // last existing key offset
+            if (CAUSAL) lim = min(lim, qrow - kbase_h);          // last visible key offset
+            if (__builtin_amdgcn_ballot_w64(lim < 27) != 0) {   // 27 = largest koff(i)
+                for (int i = 0; i < 16; ++i)
+                    s[kb][i] = (8 * (i >> 2) + (i & 3) > lim) ? masked : s[kb][i];
             }
         }
-        const float mt = xor32_max(mloc);
+        float mk[NKB];
+        if (c_nonneg) {
+            for (int kb = 0; kb < NKB; ++kb) {
+                float a = fmaxf(s[kb][0], fmaxf(s[kb][1], s[kb][2]));
+                float b = fmaxf(s[kb][3], fmaxf(s[kb][4], s[kb][5]));
+                a = fmaxf(a, fmaxf(s[kb][6], s[kb][7]));
+                b = fmaxf(b, fmaxf(s[kb][8], s[kb][9]));
+                a = fmaxf(a, fmaxf(s[kb][10], s[kb][11]));
+                b = fmaxf(b, fmaxf(s[kb][12], s[kb][13]));
+                a = fmaxf(a, fmaxf(s[kb][14], s[kb][15]));
+                mk[kb] = fmaxf(a, b);
+            }
+        } else {
+            for (int kb = 0; kb < NKB; ++kb) {
+                float a = s[kb][0];
+                for (int i = 1; i < 16; ++i) a = fminf(a, s[kb][i]);
+                mk[kb] = a;
+            }
+        }
+        float mraw = mk[0];
+        for (int kb = 1; kb < NKB; ++kb) mraw = c_nonneg ? fmaxf(mraw, mk[kb]) : fminf(mraw, mk[kb]);
+        // c_log2 is never 0 (the host maps scale 0 to a tiny positive value),
+        // so a fully masked row gives (+-inf) * c = -inf here.
+        const float mt = xor32_max(mraw * c_log2);
         const float mnew = fmaxf(m_run, mt);
-        const bool grow = mnew > m_run + 8.0f;
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-            const float alpha = exp2f(m_run - mnew);          // 0 on the first tile
+        if (__builtin_amdgcn_ballot_w64(mnew > m_run + 8.0f) != 0) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);   // 0 on the first tile
             for (int db = 0; db < NDB; ++db)
                 for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
             l_part *= alpha;
             m_run = mnew;
         }
-        const float muse = (m_run == -INFINITY) ? 0.f : m_run;
+        return (m_run == -INFINITY) ? 0.f : -m_run;
+    };
 
-        // ---- O^T += V^T P^T ---------------------------------------------
-        for (int kb = 0; kb < NKB; ++kb) {
-            if (!active[kb]) continue;
-            uint32_t pw[8];
-            for (int i = 0; i < 8; ++i) {
-                const float p0 = __builtin_amdgcn_exp2f(s[kb][2 * i] - muse);
-                const float p1 = __builtin_amdgcn_exp2f(s[kb][2 * i + 1] - muse);
-                l_part += p0 + p1;
-                pw[i] = Tr::pack_p(p0, p1);
-            }
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const pv_frag pf = __builtin_bit_cast(pv_frag, (u32x4){pw[4 * s2], pw[4 * s2 + 1], pw[4 * s2 + 2], pw[4 * s2 + 3]});
-                const int g1 = (kb * 32 + 16 * s2) / 4 + h;   // keys 4*g1 .. 4*g1+3
-                for (int db = 0; db < NDB; ++db) {
-                    const int d = db * 32 + n;
-                    const u32x2 lo = *(const u32x2*)(&lds_v[buf][(g1 * D + d) * 4]);
-                    const u32x2 hi = *(const u32x2*)(&lds_v[buf][((g1 + 2) * D + d) * 4]);
-                    const pv_frag vf = __builtin_bit_cast(pv_frag, (u32x4){lo[0], lo[1], hi[0], hi[1]});
-                    oacc[db] = Tr::pv(vf, pf, oacc[db]);
-                }
+    // Weights of one 32-key block: P = exp2(c s - m) packed to 16 bits, and
+    // the row-sum update over exactly those rounded weights.
+    auto block_weights = [&](const f32x16& sb, float neg_m, uint32_t (&pw)[8]) {
+        for (int i = 0; i < 8; ++i) {
+            const float x0 = fmaf(sb[2 * i], c_log2, neg_m);
+            const float x1 = fmaf(sb[2 * i + 1], c_log2, neg_m);
+            pw[i] = Tr::pack(__builtin_amdgcn_exp2f(x0), __builtin_amdgcn_exp2f(x1));
+            l_part = Tr::sum2(pw[i], l_part);
+        }
+    };
+
+    // O^T += V^T P^T for one 32-key block, V operands fetched one step ahead.
+    auto block_pv = [&](const uint8_t* vt, int kb, const uint32_t (&pw)[8]) {
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const pv_frag pf = __builtin_bit_cast(pv_frag, (u32x4){pw[4 * s2], pw[4 * s2 + 1],
+                                                                   pw[4 * s2 + 2], pw[4 * s2 + 3]});
+            pv_frag vcur = load_v(vt, kb, s2, 0);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                pv_frag vnxt;
+                if (db + 1 < NDB) vnxt = load_v(vt, kb, s2, db + 1);
+                oacc[db] = Tr::pv(vcur, pf, oacc[db]);
+                if (db + 1 < NDB) vcur = vnxt;
             }
         }
+    };
 
-        if (j + 1 < n_tiles) store_tile(buf ^ 1);
+    // One pipelined iteration. Part 1: max / lazy rescale of tile j (small,
+    // branchy). Part 2, one straight-line block: scores of tile j+1 (when
+    // HAS_NEXT) into s_nxt, weights and PV of tile j from s_cur, so the
+    // matrix-core work of tile j+1 overlaps the exp work of tile j. Buffers:
+    // K(j+1) in kb_next, V(j) in vb_cur; meanwhile K(j+2) goes to kb_cur and
+    // V(j+1) to vb_next. Every wave runs exactly one barrier per iteration.
+    // Tiles above a wave's diagonal are computed like masked tiles (their
+    // weights are all 0); that only happens in workgroups holding several
+    // row blocks of one head.
+    auto iteration = [&](auto has_next_tag, int j, f32x16 (&s_cur)[NKB], f32x16 (&s_nxt)[NKB],
+                         uint8_t* kb_cur, uint8_t* kb_next, uint8_t* vb_cur, uint8_t* vb_next) {
+        constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
+        __syncthreads();
+        if constexpr (HAS_NEXT) {
+            if (j + 2 < n_tiles) issue_k(j + 2, kb_cur);
+            issue_v(j + 1, vb_next);
+        }
+        const float neg_m = tile_max(s_cur, j);
+        // Weights of tile j, pair by pair (pair p covers scores 2p, 2p+1 of
+        // block p / 8), interleaved with the k-steps of tile j+1's scores.
+        uint32_t pw[NKB][8];
+        auto weight_pair = [&](int pp) {
+            const int kb = pp / 8, i = pp % 8;
+            const float x0 = fmaf(s_cur[kb][2 * i], c_log2, neg_m);
+            const float x1 = fmaf(s_cur[kb][2 * i + 1], c_log2, neg_m);
+            pw[kb][i] = Tr::pack(__builtin_amdgcn_exp2f(x0), __builtin_amdgcn_exp2f(x1));
+            l_part = Tr::sum2(pw[kb][i], l_part);
+        };
+        if constexpr (HAS_NEXT) {
+            constexpr int PAIRS = NKB * 8;
+            constexpr int PER_STEP = PAIRS / KSTEPS;
+            static_assert(PER_STEP * KSTEPS == PAIRS, "weight pairs must split evenly over k-steps");
+            for (int kb = 0; kb < NKB; ++kb)
+                for (int i = 0; i < 16; ++i) s_nxt[kb][i] = 0.f;
+            qk_frag cur[NKB], nxt[NKB];
+            for (int kb = 0; kb < NKB; ++kb) cur[kb] = load_k(kb_next, kb, 0);
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                if (ks + 1 < KSTEPS)
+                    for (int kb = 0; kb < NKB; ++kb) nxt[kb] = load_k(kb_next, kb, ks + 1);
+                for (int kb = 0; kb < NKB; ++kb) s_nxt[kb] = Tr::qk(cur[kb], qf[ks], s_nxt[kb]);
+                for (int t = 0; t < PER_STEP; ++t) weight_pair(ks * PER_STEP + t);
+                if (ks + 1 < KSTEPS)
+                    for (int kb = 0; kb < NKB; ++kb) cur[kb] = nxt[kb];
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            for (int pp = 0; pp < NKB * 8; ++pp) weight_pair(pp);
+        }
+        for (int kb = 0; kb < NKB; ++kb) block_pv(vb_cur, kb, pw[kb]);
+        if constexpr (HAS_NEXT) finish_v(vb_next);
+    };
+
+    f32x16 s0[NKB], s1[NKB];
+    issue_k(0, kbuf0);
+    issue_v(0, vbuf0);
+    if (n_tiles > 1) issue_k(1, kbuf1);
+    finish_v(vbuf0);
+    __syncthreads();
+    qk_tile(kbuf0, s0);
+    int j = 0;
+    for (; j + 2 < n_tiles; j += 2) {
+        iteration(std::true_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
+        iteration(std::true_type{}, j + 1, s1, s0, kbuf1, kbuf0, vbuf1, vbuf0);
+    }
+    if (j + 1 < n_tiles) {
+        iteration(std::true_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
+        iteration(std::false_type{}, j + 1, s1, s0, kbuf1, kbuf0, vbuf1, vbuf0);
+    } else {
+        iteration(std::false_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
     }
 
     // ---- epilogue: O = O^T / l, round once, store [b][row][hq][d] ----------
@@ -350,8 +394,8 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
         for (int db = 0; db < NDB; ++db) {
             for (int jj = 0; jj < 4; ++jj) {
                 const int d0 = db * 32 + 8 * jj + 4 * h;
-                const uint32_t w0 = Tr::pack_out(oacc[db][4 * jj + 0] * inv, oacc[db][4 * jj + 1] * inv);
-                const uint32_t w1 = Tr::pack_out(oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv);
+                const uint32_t w0 = Tr::pack(oacc[db][4 * jj + 0] * inv, oacc[db][4 * jj + 1] * inv);
+                const uint32_t w1 = Tr::pack(oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv);
                 *(u32x2*)(orow + d0) = (u32x2){w0, w1};
             }
         }
@@ -371,16 +415,16 @@ static hipError_t launch_typed(const FwdParams& p, bool causal, hipStream_t stre
 // bf16 (is_bf16 = true) or f16 inputs, D = 64 or 128.
 hipError_t launch_fwd_mfma(const FwdParams& p, int D, bool is_bf16, bool causal, hipStream_t stream) {
     if (is_bf16) {
-        return D == 64 ? launch_typed<__bf16, 64, 128>(p, causal, stream)
+        return D == 64 ? launch_typed<__bf16, 64, 64>(p, causal, stream)
                        : launch_typed<__bf16, 128, 64>(p, causal, stream);
     }
-    return D == 64 ? launch_typed<_Float16, 64, 128>(p, causal, stream)
+    return D == 64 ? launch_typed<_Float16, 64, 64>(p, causal, stream)
                    : launch_typed<_Float16, 128, 64>(p, causal, stream);
 }
 
 // E4M3 inputs, bf16 output, D = 64 or 128.
 hipError_t launch_fwd_fp8(const FwdParams& p, int D, bool causal, hipStream_t stream) {
-    return D == 64 ? launch_typed<fp8_t, 64, 128>(p, causal, stream)
+    return D == 64 ? launch_typed<fp8_t, 64, 64>(p, causal, stream)
                    : launch_typed<fp8_t, 128, 64>(p, causal, stream);
 }
 

@@ -1,0 +1,154 @@
+// mfma_common.h — device building blocks shared by the matrix-core kernels.
+//
+// Number formats and their MFMA instructions (Traits), the LDS swizzles and
+// the HBM -> LDS tile copy. Only the library's own .hip files include it.
+#pragma once
+
+#include <type_traits>
+
+#include "kernel_common.h"
+
+namespace attn {
+
+typedef uint8_t fp8_t;   // one OCP E4M3 code
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+#define GLOBAL_PTR(p) ((const __attribute__((address_space(1))) void*)(p))
+
+__device__ inline uint32_t pack2_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
+__device__ inline uint32_t pack2_f16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
+}
+
+// Per input type: the score product (QK), the weight product (PV) and the
+// conversions around them.
+template <typename T> struct Traits;
+
+template <> struct Traits<__bf16> {
+    static constexpr int IN_BYTES = 2;
+    static constexpr int QK_LANE_BYTES = 16;    // bytes of one operand per lane per k-step
+    static constexpr int QK_K = 16;             // contraction length of one QK MFMA
+    static constexpr bool V_DMA = true;         // V goes to LDS unchanged
+    using qk_frag = bf16x8;
+    using pv_frag = bf16x8;
+    using out_t = __bf16;
+    __device__ static inline f32x16 qk(qk_frag a, qk_frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static inline f32x16 pv(pv_frag a, pv_frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static inline uint32_t pack(float lo, float hi) { return pack2_bf16(lo, hi); }
+    // l += lo + hi of a packed pair, summed in fp32.
+    __device__ static inline float sum2(uint32_t w, float l) {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                              (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, l, false);
+    }
+};
+
+template <> struct Traits<_Float16> {
+    static constexpr int IN_BYTES = 2;
+    static constexpr int QK_LANE_BYTES = 16;
+    static constexpr int QK_K = 16;
+    static constexpr bool V_DMA = true;
+    using qk_frag = f16x8;
+    using pv_frag = f16x8;
+    using out_t = _Float16;
+    __device__ static inline f32x16 qk(qk_frag a, qk_frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    __device__ static inline f32x16 pv(pv_frag a, pv_frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    __device__ static inline uint32_t pack(float lo, float hi) { return pack2_f16(lo, hi); }
+    __device__ static inline float sum2(uint32_t w, float l) {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w),
+                                      (f16x2){(_Float16)1.0f, (_Float16)1.0f}, l, false);
+    }
+};
+
+template <> struct Traits<fp8_t> {
+    static constexpr int IN_BYTES = 1;
+    static constexpr int QK_LANE_BYTES = 32;
+    static constexpr int QK_K = 64;
+    static constexpr bool V_DMA = false;        // V is widened to bf16 on its way to LDS
+    using qk_frag = i32x8;
+    using pv_frag = bf16x8;
+    using out_t = __bf16;
+    __device__ static inline f32x16 qk(qk_frag a, qk_frag b, f32x16 c) {
+        // Both operands E4M3 (format code 0), no block scales.
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+    }
+    __device__ static inline f32x16 pv(pv_frag a, pv_frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static inline uint32_t pack(float lo, float hi) { return pack2_bf16(lo, hi); }
+    __device__ static inline float sum2(uint32_t w, float l) { return Traits<__bf16>::sum2(w, l); }
+};
+
+// XOR swizzles of 16-byte chunks inside LDS rows (chunk c of row r lives at
+// chunk position c ^ swz(r)). The hardware serves 256 bytes (64 banks x 4
+// bytes) per pass.
+//  * K rows are read by 32 lanes at one chunk index and 32 different rows
+//    (the A operand of S^T = K Q^T): consecutive rows get different masks.
+//  * V rows are read by the transpose read: per half-wave 4 rows x 4 chunks.
+template <int NCH>   // chunks per row
+__device__ inline int k_swz(int r) { return (r / (16 / NCH)) % NCH; }
+template <int NCH>
+__device__ inline int v_swz(int r) { return 4 * ((r / (16 / NCH)) % (NCH / 4)); }
+
+// Copying one K or V tile (NROWS rows of ROWB bytes) from HBM straight into
+// LDS. Each global_load_lds_dwordx4 moves 1 KiB: lane l lands at byte 16 l
+// of it, i.e. at row i * RPI + l / NCH, chunk position l % NCH, and fetches
+// the global chunk (l % NCH) ^ swz(row) of that row. The per-lane byte offset
+// of that chunk inside a tile (row * row stride + chunk * 16) does not depend
+// on the tile, so it is computed once; each tile only adds a scalar base.
+template <int ROWB, int NROWS>
+struct TileDma {
+    static constexpr int NCH = ROWB / 16;
+    static constexpr int RPI = 1024 / ROWB;             // rows per instruction
+    static constexpr int NINSTR = NROWS * ROWB / 1024;
+    static constexpr int PER_WAVE = NINSTR / 4;
+    static constexpr int ROW_STEP = 4 * RPI;            // rows between a wave's instructions
+    static_assert(NINSTR % 4 == 0, "tile must split evenly over 4 waves");
+    // Instruction t of this wave covers rows r0 + ROW_STEP t. ROW_STEP = 256 /
+    // NCH, so both swizzles give the same mask for every t (they depend on
+    // r / (16 / NCH) modulo at most NCH, and ROW_STEP / (16 / NCH) = 16):
+    // one lane offset serves all of the wave's instructions.
+    uint32_t off;               // lane's byte offset inside the tile, instruction 0
+    int r0;                     // lane's tile row, instruction 0
+
+    __device__ void init(int wave, int lane, uint32_t gstride, bool kswz) {
+        r0 = wave * RPI + lane / NCH;
+        const int c = (lane % NCH) ^ (kswz ? k_swz<NCH>(r0) : v_swz<NCH>(r0));
+        off = (uint32_t)r0 * gstride + (uint32_t)c * 16;
+    }
+    // Rows [key0, key0 + NROWS) of the head starting at g. Rows past the end
+    // of the keys (only in the last tile) repeat the last key: finite values
+    // whose weights are 0 after masking.
+    __device__ void issue(const uint8_t* g, size_t gstride, int key0, int Skv, uint8_t* tile, int wave) const {
+        const uint8_t* gb = g + (size_t)key0 * gstride;
+        if (key0 + NROWS <= Skv) {
+            for (int t = 0; t < PER_WAVE; ++t)
+                __builtin_amdgcn_global_load_lds(GLOBAL_PTR(gb + (size_t)t * ROW_STEP * gstride + off),
+                                                 LDS_PTR(tile + (wave + 4 * t) * 1024), 16, 0, 0);
+        } else {
+            for (int t = 0; t < PER_WAVE; ++t) {
+                const int over = key0 + r0 + t * ROW_STEP - (Skv - 1);
+                const uint8_t* src = gb + (size_t)t * ROW_STEP * gstride + off -
+                                     (over > 0 ? (size_t)over * gstride : 0);
+                __builtin_amdgcn_global_load_lds(GLOBAL_PTR(src), LDS_PTR(tile + (wave + 4 * t) * 1024), 16, 0, 0);
+            }
+        }
+    }
+};
+
+
+}  // namespace attn

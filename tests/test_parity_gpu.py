@@ -63,9 +63,17 @@ SMALL = [
 ]
 
 
+@pytest.fixture(params=["32", "64"], ids=["rows32", "rows64"])
+def rows_per_wave(request, monkeypatch):
+    """Force the 32-row (two waves per SIMD) or the 64-row (one wave per SIMD)
+    matrix-core kernel; the library picks one by grid size otherwise."""
+    monkeypatch.setenv("ATTN_ROWS_PER_WAVE", request.param)
+    return request.param
+
+
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
-def test_parity_small(w):
-    print(f"case {w.name}", flush=True)
+def test_parity_small(w, rows_per_wave):
+    print(f"case {w.name} rows/wave {rows_per_wave}", flush=True)
     q, k, v, desc = workload.make_inputs(w)
     got = helpers.out_to_f64(helpers.gpu_run(w, q, k, v, desc))
     want = helpers.oracle_full(w, q, k, v, desc)
@@ -75,7 +83,7 @@ def test_parity_small(w):
     assert err <= TOL[w.dtype], err
 
 
-def test_scale_zero_and_negative():
+def test_scale_zero_and_negative(rows_per_wave):
     w = W("bf16", 1, 4, 2, 130, 130, 128, True)
     q, k, v, desc = workload.make_inputs(w)
     for scale in (0.0, -0.2):
@@ -120,7 +128,7 @@ def test_parity_full_size_sampled(name):
         assert torch.equal(o[:, 0].cpu(), v0)
 
 
-def test_gqa_equals_repeated_mha_bitwise():
+def test_gqa_equals_repeated_mha_bitwise(rows_per_wave):
     w = W("bf16", 2, 8, 2, 260, 260, 128, True)
     q, k, v, desc = workload.make_inputs(w)
     a = helpers.gpu_run(w, q, k, v, desc)
@@ -129,7 +137,7 @@ def test_gqa_equals_repeated_mha_bitwise():
     assert torch.equal(a, b)
 
 
-def test_deterministic_and_canaries():
+def test_deterministic_and_canaries(rows_per_wave):
     w = workload.WORKLOADS["bf16_gqa_b2_hq32_hkv8_s4096_d128_causal"]
     q, k, v, desc = workload.make_inputs(w, shapes=[(1, 700, 8, 128), (1, 700, 2, 128), (1, 700, 2, 128)])
     n, pad = q.numel(), 4096
@@ -143,7 +151,7 @@ def test_deterministic_and_canaries():
     assert not torch.isnan(out).any()
 
 
-def test_constant_v_gives_constant_output():
+def test_constant_v_gives_constant_output(rows_per_wave):
     w = W("bf16", 1, 4, 2, 200, 200, 128, True)
     q, k, _, desc = workload.make_inputs(w)
     row = torch.randn(128, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
