@@ -163,6 +163,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
         for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
     float m_run = -INFINITY;   // running max of scale*log2(e)*score (same on both halves)
     float l_part = 0.f;        // this lane's share of the running denominator
+    float neg_m = 0.f;         // exponent offset -m_run of the tile being weighted
 
     const float c_log2 = p.scale_log2;
     const bool c_nonneg = c_log2 >= 0.f;
@@ -235,14 +236,13 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
         }
     };
 
-    // Row max of one tile's scores and the lazy rescale of O and l; returns
-    // -m (the exponent offset). Scores of keys past the end or above the
-    // causal diagonal are first replaced by -inf (scale >= 0) or +inf
-    // (scale < 0), so that c * s = -inf for them; the test costs a few
-    // instructions per 32-key block and is skipped (wave-uniformly) wherever
-    // no key of the block is hidden from any row of the wave.
-    auto tile_max = [&](f32x16 (&s)[NKB], int j) -> float {
-        const float masked = c_nonneg ? -INFINITY : INFINITY;
+    // Masking of one tile's scores: keys past the end or above the causal
+    // diagonal become -inf (scale >= 0) or +inf (scale < 0), so that
+    // c * s = -inf for them. The test costs a few instructions per 32-key
+    // block and is skipped (wave-uniformly) wherever no key of the block is
+    // hidden from any row of the wave.
+    const float masked = c_nonneg ? -INFINITY : INFINITY;
+    auto mask_tile = [&](f32x16 (&s)[NKB], int j) {
         for (int kb = 0; kb < NKB; ++kb) {
             const int kbase_h = j * BN + kb * 32 + 4 * h;       // key of element i: kbase_h + koff(i)
             int lim = Skv - 1 - kbase_h;                         // last existing key offset
@@ -252,27 +252,28 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
                     s[kb][i] = (8 * (i >> 2) + (i & 3) > lim) ? masked : s[kb][i];
             }
         }
-        float mk[NKB];
-        if (c_nonneg) {
-            for (int kb = 0; kb < NKB; ++kb) {
-                float a = fmaxf(s[kb][0], fmaxf(s[kb][1], s[kb][2]));
-                float b = fmaxf(s[kb][3], fmaxf(s[kb][4], s[kb][5]));
-                a = fmaxf(a, fmaxf(s[kb][6], s[kb][7]));
-                b = fmaxf(b, fmaxf(s[kb][8], s[kb][9]));
-                a = fmaxf(a, fmaxf(s[kb][10], s[kb][11]));
-                b = fmaxf(b, fmaxf(s[kb][12], s[kb][13]));
-                a = fmaxf(a, fmaxf(s[kb][14], s[kb][15]));
-                mk[kb] = fmaxf(a, b);
-            }
-        } else {
-            for (int kb = 0; kb < NKB; ++kb) {
-                float a = s[kb][0];
-                for (int i = 1; i < 16; ++i) a = fminf(a, s[kb][i]);
-                mk[kb] = a;
-            }
+    };
+    // Partial row max (scale >= 0) of scores 16 g .. 16 g + 15 (block g / 1),
+    // split into four pieces so it can ride along the PV MFMA groups.
+    auto max_piece = [&](const f32x16 (&s)[NKB], int piece, float m) -> float {
+        constexpr int PER = NKB * 16 / 4;                        // scores per piece
+        const int base = piece * PER;
+        for (int e = 0; e < PER; e += 2) {
+            const int x = base + e;
+            m = fmaxf(m, fmaxf(s[x / 16][x % 16], s[x / 16][(x + 1) % 16]));
         }
-        float mraw = mk[0];
-        for (int kb = 1; kb < NKB; ++kb) mraw = c_nonneg ? fmaxf(mraw, mk[kb]) : fminf(mraw, mk[kb]);
+        return m;
+    };
+    auto min_all = [&](const f32x16 (&s)[NKB]) -> float {
+        float m = INFINITY;
+        for (int kb = 0; kb < NKB; ++kb)
+            for (int i = 0; i < 16; ++i) m = fminf(m, s[kb][i]);
+        return m;
+    };
+    // From this lane's raw max (min for scale < 0) of a tile: the row max in
+    // the log2 domain, the lazy rescale of O and l (only when the max grew by
+    // more than 8, i.e. a factor 2^8), and the new exponent offset -m.
+    auto finish_max = [&](float mraw) -> float {
         // c_log2 is never 0 (the host maps scale 0 to a tiny positive value),
         // so a fully masked row gives (+-inf) * c = -inf here.
         const float mt = xor32_max(mraw * c_log2);
@@ -287,42 +288,17 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
         return (m_run == -INFINITY) ? 0.f : -m_run;
     };
 
-    // Weights of one 32-key block: P = exp2(c s - m) packed to 16 bits, and
-    // the row-sum update over exactly those rounded weights.
-    auto block_weights = [&](const f32x16& sb, float neg_m, uint32_t (&pw)[8]) {
-        for (int i = 0; i < 8; ++i) {
-            const float x0 = fmaf(sb[2 * i], c_log2, neg_m);
-            const float x1 = fmaf(sb[2 * i + 1], c_log2, neg_m);
-            pw[i] = Tr::pack(__builtin_amdgcn_exp2f(x0), __builtin_amdgcn_exp2f(x1));
-            l_part = Tr::sum2(pw[i], l_part);
-        }
-    };
-
-    // O^T += V^T P^T for one 32-key block, V operands fetched one step ahead.
-    auto block_pv = [&](const uint8_t* vt, int kb, const uint32_t (&pw)[8]) {
-        for (int s2 = 0; s2 < 2; ++s2) {
-            const pv_frag pf = __builtin_bit_cast(pv_frag, (u32x4){pw[4 * s2], pw[4 * s2 + 1],
-                                                                   pw[4 * s2 + 2], pw[4 * s2 + 3]});
-            pv_frag vcur = load_v(vt, kb, s2, 0);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                pv_frag vnxt;
-                if (db + 1 < NDB) vnxt = load_v(vt, kb, s2, db + 1);
-                oacc[db] = Tr::pv(vcur, pf, oacc[db]);
-                if (db + 1 < NDB) vcur = vnxt;
-            }
-        }
-    };
-
-    // One pipelined iteration. Part 1: max / lazy rescale of tile j (small,
-    // branchy). Part 2, one straight-line block: scores of tile j+1 (when
-    // HAS_NEXT) into s_nxt, weights and PV of tile j from s_cur, so the
-    // matrix-core work of tile j+1 overlaps the exp work of tile j. Buffers:
-    // K(j+1) in kb_next, V(j) in vb_cur; meanwhile K(j+2) goes to kb_cur and
-    // V(j+1) to vb_next. Every wave runs exactly one barrier per iteration.
-    // Tiles above a wave's diagonal are computed like masked tiles (their
-    // weights are all 0); that only happens in workgroups holding several
-    // row blocks of one head.
+    // One pipelined iteration over tile j. With HAS_NEXT (tile j+1 exists):
+    //   A: scores of tile j+1 (MFMA) interleaved with the weights of tile j
+    //      (exp2(c s - m), packed, summed) — the offset -m of tile j is known;
+    //   A': masking of tile j+1's scores, only on boundary tiles;
+    //   B: PV of tile j (MFMA) interleaved with the row max of tile j+1;
+    //   C: cross-half max, lazy rescale of O (after PV of tile j), new -m.
+    // Buffers: K(j+1) in kb_next, V(j) in vb_cur; meanwhile K(j+2) goes to
+    // kb_cur and V(j+1) to vb_next. Every wave runs exactly one barrier per
+    // iteration. Tiles above a wave's own diagonal (in workgroups holding
+    // several row blocks of one head) are computed like masked tiles: all
+    // their weights are 0.
     auto iteration = [&](auto has_next_tag, int j, f32x16 (&s_cur)[NKB], f32x16 (&s_nxt)[NKB],
                          uint8_t* kb_cur, uint8_t* kb_next, uint8_t* vb_cur, uint8_t* vb_next) {
         constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
@@ -331,9 +307,6 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
             if (j + 2 < n_tiles) issue_k(j + 2, kb_cur);
             issue_v(j + 1, vb_next);
         }
-        const float neg_m = tile_max(s_cur, j);
-        // Weights of tile j, pair by pair (pair p covers scores 2p, 2p+1 of
-        // block p / 8), interleaved with the k-steps of tile j+1's scores.
         uint32_t pw[NKB][8];
         auto weight_pair = [&](int pp) {
             const int kb = pp / 8, i = pp % 8;
@@ -342,6 +315,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
             pw[kb][i] = Tr::pack(__builtin_amdgcn_exp2f(x0), __builtin_amdgcn_exp2f(x1));
             l_part = Tr::sum2(pw[kb][i], l_part);
         };
+        // ---- A ---------------------------------------------------------------
         if constexpr (HAS_NEXT) {
             constexpr int PAIRS = NKB * 8;
             constexpr int PER_STEP = PAIRS / KSTEPS;
@@ -360,10 +334,30 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
                     for (int kb = 0; kb < NKB; ++kb) cur[kb] = nxt[kb];
                 __builtin_amdgcn_sched_barrier(0);
             }
+            // ---- A' ------------------------------------------------------------
+            mask_tile(s_nxt, j + 1);
         } else {
             for (int pp = 0; pp < NKB * 8; ++pp) weight_pair(pp);
         }
-        for (int kb = 0; kb < NKB; ++kb) block_pv(vb_cur, kb, pw[kb]);
+        // ---- B -----------------------------------------------------------------
+        float mraw = masked;
+        const bool fused_max = HAS_NEXT && c_nonneg;
+#pragma unroll
+        for (int g = 0; g < NKB * 2; ++g) {
+            const int kb = g / 2, s2 = g % 2;
+            const pv_frag pf = __builtin_bit_cast(pv_frag, (u32x4){pw[kb][4 * s2], pw[kb][4 * s2 + 1],
+                                                                   pw[kb][4 * s2 + 2], pw[kb][4 * s2 + 3]});
+            pv_frag vf[NDB];
+            for (int db = 0; db < NDB; ++db) vf[db] = load_v(vb_cur, kb, s2, db);
+            for (int db = 0; db < NDB; ++db) oacc[db] = Tr::pv(vf[db], pf, oacc[db]);
+            if (fused_max) mraw = max_piece(s_nxt, g, mraw);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // ---- C -----------------------------------------------------------------
+        if constexpr (HAS_NEXT) {
+            if (!c_nonneg) mraw = min_all(s_nxt);
+            neg_m = finish_max(mraw);
+        }
         if constexpr (HAS_NEXT) finish_v(vb_next);
     };
 
@@ -374,6 +368,13 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
     finish_v(vbuf0);
     __syncthreads();
     qk_tile(kbuf0, s0);
+    mask_tile(s0, 0);
+    {
+        float mraw = c_nonneg ? max_piece(s0, 0, masked) : min_all(s0);
+        if (c_nonneg)
+            for (int g = 1; g < 4; ++g) mraw = max_piece(s0, g, mraw);
+        neg_m = finish_max(mraw);
+    }
     int j = 0;
     for (; j + 2 < n_tiles; j += 2) {
         iteration(std::true_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);

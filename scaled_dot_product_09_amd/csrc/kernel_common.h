@@ -71,13 +71,27 @@ __device__ inline WorkItem map_workgroup(const FwdParams& p, bool causal) {
     return w;
 }
 
+// The values of lanes l and l ^ 32 of a 64-wide wavefront, as (a, b) in some
+// order: v_permlane32_swap exchanges the upper half of one operand with the
+// lower half of the other, so each lane ends up holding both.
+__device__ inline void xor32_pair(float x, float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                    __builtin_bit_cast(unsigned, x), false, false);
+    a = __builtin_bit_cast(float, (unsigned)r[0]);
+    b = __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
 // Maximum of a value over lanes l and l ^ 32 of a 64-wide wavefront.
 __device__ inline float xor32_max(float x) {
-    return fmaxf(x, __shfl_xor(x, 32, 64));
+    float a, b;
+    xor32_pair(x, a, b);
+    return fmaxf(a, b);
 }
 
 __device__ inline float xor32_sum(float x) {
-    return x + __shfl_xor(x, 32, 64);
+    float a, b;
+    xor32_pair(x, a, b);
+    return a + b;
 }
 
 }  // namespace attn
