@@ -26,10 +26,10 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
     __shared__ __attribute__((aligned(16))) float lk[BK][D];
     __shared__ __attribute__((aligned(16))) float lv[BK][D];
 
-    const int tid = threadIdx.x;
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
     const int part = tid % TPR;
     const int rows_blocks = (p.Sq + RPW - 1) / RPW;
-    int bid = blockIdx.x;
+    int bid = (int)__builtin_amdgcn_workgroup_id_x();
     const int rb = bid % rows_blocks;  bid /= rows_blocks;
     const int hq = bid % p.Hq;
     const int b = bid / p.Hq;

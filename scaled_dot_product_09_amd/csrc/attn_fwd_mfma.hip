@@ -61,9 +61,15 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
     constexpr int NDB = D / 32;                       // 32-wide column blocks of O
     constexpr int KTILE = BN * KROWB, VTILE = BN * VROWB;
 
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * (KTILE + VTILE)];   // K0 K1 V0 V1
+    // Four separate LDS objects (not one array cut in four), so the compiler
+    // can prove that a copy landing in one buffer never aliases reads of
+    // another and does not make those reads wait for the copy.
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_k0[KTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_k1[KTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_v0[VTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_v1[VTILE];
 
-    const int tid = threadIdx.x;
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;              // which half of the wave
@@ -115,10 +121,10 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
     // tile j are formed), so K runs one tile ahead of V: iteration j reads
     // K(j+1) and V(j) and, meanwhile, loads K(j+2) into the K buffer K(j)
     // used and V(j+1) into the V buffer V(j-1) used.
-    uint8_t* const kbuf0 = lds;
-    uint8_t* const kbuf1 = lds + KTILE;
-    uint8_t* const vbuf0 = lds + 2 * KTILE;
-    uint8_t* const vbuf1 = lds + 2 * KTILE + VTILE;
+    uint8_t* const kbuf0 = lds_k0;
+    uint8_t* const kbuf1 = lds_k1;
+    uint8_t* const vbuf0 = lds_v0;
+    uint8_t* const vbuf1 = lds_v1;
     // FP8: V is widened to bf16 in registers (exact) and written to LDS by
     // the threads; 8 values (one 16-byte chunk) per thread and step.
     constexpr int V_ST = Tr::V_DMA ? 1 : (BN * D / 8) / 256;
@@ -299,21 +305,30 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
     // iteration. Tiles above a wave's own diagonal (in workgroups holding
     // several row blocks of one head) are computed like masked tiles: all
     // their weights are 0.
+    // The buffer pointers are __restrict__: once inlined, that marks every LDS
+    // access of the iteration with its buffer's scope, which is what lets
+    // the compiler see that copies into kb_cur / vb_next never alias reads of
+    // kb_next / vb_cur (otherwise it makes the reads wait for the copies).
     auto iteration = [&](auto has_next_tag, int j, f32x16 (&s_cur)[NKB], f32x16 (&s_nxt)[NKB],
-                         uint8_t* kb_cur, uint8_t* kb_next, uint8_t* vb_cur, uint8_t* vb_next) {
+                         uint8_t* __restrict__ kb_cur, uint8_t* __restrict__ kb_next,
+                         uint8_t* __restrict__ vb_cur, uint8_t* __restrict__ vb_next) {
         constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
-        __syncthreads();
+        dma_barrier();
         if constexpr (HAS_NEXT) {
             if (j + 2 < n_tiles) issue_k(j + 2, kb_cur);
             issue_v(j + 1, vb_next);
         }
         uint32_t pw[NKB][8];
+        pv_frag vf[2][NDB];     // V operands of two consecutive PV groups
         auto weight_pair = [&](int pp) {
             const int kb = pp / 8, i = pp % 8;
             const float x0 = fmaf(s_cur[kb][2 * i], c_log2, neg_m);
             const float x1 = fmaf(s_cur[kb][2 * i + 1], c_log2, neg_m);
             pw[kb][i] = Tr::pack(__builtin_amdgcn_exp2f(x0), __builtin_amdgcn_exp2f(x1));
             l_part = Tr::sum2(pw[kb][i], l_part);
+            // Keep the weights where they are computed (between the score
+            // MFMAs) instead of letting the compiler sink them to their use.
+            asm volatile("" : "+v"(pw[kb][i]), "+v"(l_part));
         };
         // ---- A ---------------------------------------------------------------
         if constexpr (HAS_NEXT) {
@@ -322,22 +337,29 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
             static_assert(PER_STEP * KSTEPS == PAIRS, "weight pairs must split evenly over k-steps");
             for (int kb = 0; kb < NKB; ++kb)
                 for (int i = 0; i < 16; ++i) s_nxt[kb][i] = 0.f;
-            qk_frag cur[NKB], nxt[NKB];
-            for (int kb = 0; kb < NKB; ++kb) cur[kb] = load_k(kb_next, kb, 0);
+            // K operands are fetched two k-steps ahead; the V operands of the
+            // first PV group are fetched during the last k-step.
+            qk_frag kf[3][NKB];
+            for (int kb = 0; kb < NKB; ++kb) kf[0][kb] = load_k(kb_next, kb, 0);
+            if (KSTEPS > 1)
+                for (int kb = 0; kb < NKB; ++kb) kf[1][kb] = load_k(kb_next, kb, 1);
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
-                if (ks + 1 < KSTEPS)
-                    for (int kb = 0; kb < NKB; ++kb) nxt[kb] = load_k(kb_next, kb, ks + 1);
-                for (int kb = 0; kb < NKB; ++kb) s_nxt[kb] = Tr::qk(cur[kb], qf[ks], s_nxt[kb]);
+                if (ks + 2 < KSTEPS)
+                    for (int kb = 0; kb < NKB; ++kb) kf[(ks + 2) % 3][kb] = load_k(kb_next, kb, ks + 2);
+                if (ks + 1 == KSTEPS)
+                    for (int db = 0; db < NDB; ++db) vf[0][db] = load_v(vb_cur, 0, 0, db);
+                for (int kb = 0; kb < NKB; ++kb) s_nxt[kb] = Tr::qk(kf[ks % 3][kb], qf[ks], s_nxt[kb]);
+#pragma unroll
                 for (int t = 0; t < PER_STEP; ++t) weight_pair(ks * PER_STEP + t);
-                if (ks + 1 < KSTEPS)
-                    for (int kb = 0; kb < NKB; ++kb) cur[kb] = nxt[kb];
                 __builtin_amdgcn_sched_barrier(0);
             }
             // ---- A' ------------------------------------------------------------
             mask_tile(s_nxt, j + 1);
         } else {
+#pragma unroll
             for (int pp = 0; pp < NKB * 8; ++pp) weight_pair(pp);
+            for (int db = 0; db < NDB; ++db) vf[0][db] = load_v(vb_cur, 0, 0, db);
         }
         // ---- B -----------------------------------------------------------------
         float mraw = masked;
@@ -347,9 +369,10 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
             const int kb = g / 2, s2 = g % 2;
             const pv_frag pf = __builtin_bit_cast(pv_frag, (u32x4){pw[kb][4 * s2], pw[kb][4 * s2 + 1],
                                                                    pw[kb][4 * s2 + 2], pw[kb][4 * s2 + 3]});
-            pv_frag vf[NDB];
-            for (int db = 0; db < NDB; ++db) vf[db] = load_v(vb_cur, kb, s2, db);
-            for (int db = 0; db < NDB; ++db) oacc[db] = Tr::pv(vf[db], pf, oacc[db]);
+            // V operands of the next group are fetched while this group's MFMAs run.
+            if (g + 1 < NKB * 2)
+                for (int db = 0; db < NDB; ++db) vf[(g + 1) & 1][db] = load_v(vb_cur, (g + 1) / 2, (g + 1) % 2, db);
+            for (int db = 0; db < NDB; ++db) oacc[db] = Tr::pv(vf[g & 1][db], pf, oacc[db]);
             if (fused_max) mraw = max_piece(s_nxt, g, mraw);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -366,7 +389,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
     issue_v(0, vbuf0);
     if (n_tiles > 1) issue_k(1, kbuf1);
     finish_v(vbuf0);
-    __syncthreads();
+    dma_barrier();
     qk_tile(kbuf0, s0);
     mask_tile(s0, 0);
     {

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256, 1) void fwd_rb2_kernel(FwdParams p) {
 
     __shared__ __attribute__((aligned(1024))) uint8_t lds[NKBUF * KTILE + NVBUF * VTILE];
 
-    const int tid = threadIdx.x;
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;              // which half of the wave
@@ -287,11 +287,11 @@ __global__ __launch_bounds__(256, 1) void fwd_rb2_kernel(FwdParams p) {
     issue_v(0);
     if (n_tiles > 1) issue_k(1);
     finish_v(0);
-    __syncthreads();
+    dma_barrier();
     qk_half(std::false_type{}, 0, kbuf(0), s0, s1, 0.f, pw1);
 
     for (int j = 0; j < n_tiles; ++j) {
-        __syncthreads();
+        dma_barrier();
         if (j + 2 < n_tiles) issue_k(j + 2);
         if (j + 1 < n_tiles) issue_v(j + 1);
         const uint8_t* kt = kbuf(j);

@@ -47,7 +47,7 @@ struct WorkItem {
 // XCD, row blocks go out in order of decreasing causal work (the last row
 // block first) so the short ones fill the tail of the launch.
 __device__ inline WorkItem map_workgroup(const FwdParams& p, bool causal) {
-    const int pid = blockIdx.x;
+    const int pid = (int)__builtin_amdgcn_workgroup_id_x();
     int rb_rank, unit;
     if (p.xcd_remap) {
         const int per = p.n_units >> 3;

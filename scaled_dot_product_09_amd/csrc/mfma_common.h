@@ -17,7 +17,10 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
-#define GLOBAL_PTR(p) ((const __attribute__((address_space(1))) void*)(p))
+
+// Word 3 of a CDNA buffer descriptor for raw (unformatted, unswizzled) byte
+// access: data format 32, every other field zero.
+constexpr int kBufferWord3 = 0x00020000;
 
 __device__ inline uint32_t pack2_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
@@ -25,6 +28,15 @@ __device__ inline uint32_t pack2_bf16(float lo, float hi) {
 
 __device__ inline uint32_t pack2_f16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
+}
+
+// Workgroup barrier after which every wave's HBM -> LDS buffer copies have
+// landed. Those copies complete on the vector memory counter, and the
+// workgroup fence of __syncthreads() does not wait for them, so each wave
+// first drains its own outstanding copies.
+__device__ inline void dma_barrier() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt and lgkmcnt left alone
+    __syncthreads();
 }
 
 // Per input type: the score product (QK), the weight product (PV) and the
@@ -133,18 +145,31 @@ struct TileDma {
     // Rows [key0, key0 + NROWS) of the head starting at g. Rows past the end
     // of the keys (only in the last tile) repeat the last key: finite values
     // whose weights are 0 after masking.
+    //
+    // The copy is a buffer load into LDS (MUBUF, not a FLAT global load):
+    // the tile's base address lives in a scalar buffer descriptor and each
+    // instruction's row offset in a scalar offset register, so the lanes only
+    // hold their fixed offset `off`, and, unlike the FLAT form, the
+    // compiler's LDS wait bookkeeping does not treat the copy as an LDS access
+    // of unknown order (which would force every later LDS operand read to wait
+    // for all outstanding reads). Every byte offset stays below the
+    // descriptor's size, rows [key0, Skv) of the head.
     __device__ void issue(const uint8_t* g, size_t gstride, int key0, int Skv, uint8_t* tile, int wave) const {
         const uint8_t* gb = g + (size_t)key0 * gstride;
+        const uint64_t span = (uint64_t)(Skv - key0) * gstride;
+        const int nrec = (int)(uint32_t)(span > 0xFFFFFFFFull ? 0xFFFFFFFFull : span);   // unsigned field
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)gb, 0, nrec, kBufferWord3);
+        const uint32_t step = (uint32_t)(ROW_STEP * gstride);
         if (key0 + NROWS <= Skv) {
             for (int t = 0; t < PER_WAVE; ++t)
-                __builtin_amdgcn_global_load_lds(GLOBAL_PTR(gb + (size_t)t * ROW_STEP * gstride + off),
-                                                 LDS_PTR(tile + (wave + 4 * t) * 1024), 16, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(tile + (wave + 4 * t) * 1024), 16,
+                                                         off, t * step, 0, 0);
         } else {
             for (int t = 0; t < PER_WAVE; ++t) {
                 const int over = key0 + r0 + t * ROW_STEP - (Skv - 1);
-                const uint8_t* src = gb + (size_t)t * ROW_STEP * gstride + off -
-                                     (over > 0 ? (size_t)over * gstride : 0);
-                __builtin_amdgcn_global_load_lds(GLOBAL_PTR(src), LDS_PTR(tile + (wave + 4 * t) * 1024), 16, 0, 0);
+                const uint32_t o = off + t * step - (over > 0 ? (uint32_t)over * (uint32_t)gstride : 0u);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(tile + (wave + 4 * t) * 1024), 16,
+                                                         o, 0, 0, 0);
             }
         }
     }
