@@ -8,6 +8,9 @@ FLOPs counted as half (4 B Hq Sq Skv D / 2), next to the MI355X dense bf16
 matrix-core peak, and next to the fp64 CPU oracle timed on a bounded sample of
 the same workload on this host's cores.
 
+Before timing: W warmup steps, then untimed steps for at least SETTLE_S seconds,
+so the GPU runs at its sustained clock (after idle it needs tens of ms of load).
+
 Prints ONE JSON line on stdout. ``--sweep-out FILE`` additionally writes one
 JSON line per named workload (sequence and batch sweeps included) to FILE.
 """
@@ -28,6 +31,7 @@ METRIC = "attention fwd TFLOP/s and % of MFMA peak at S=4096 causal GQA bf16"
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "f32": 157.3}
 PEAK_KIND = {"bf16": "mfma", "f16": "mfma", "e4m3": "mfma", "f32": "alu"}
 N_BUFFER_SETS = 4   # rotating input sets, so one call's inputs are not cache-warm from the last
+SETTLE_S = 0.25     # seconds of untimed steps after the warmup steps, before timing
 
 
 def kernel_source_hash():
@@ -90,7 +94,7 @@ def cpu_baseline(w, q, k, v, desc, budget_s):
                       f"Sq x Skv each, fp64 numpy, {elapsed:.1f} s; host has {os.cpu_count()} CPUs"}
 
 
-def time_workload(w, steps, warmup, rotate=True):
+def time_workload(w, steps, warmup, rotate=True, settle_s=SETTLE_S):
     import torch
     from scaled_dot_product_09_amd import attn, workload
     dev = torch.device("cuda:0")
@@ -112,6 +116,16 @@ def time_workload(w, steps, warmup, rotate=True):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+    # After idle the GPU needs some tens of milliseconds of load to reach its
+    # sustained clock (the first ~30 headline launches run up to 25 % slower):
+    # keep stepping, untimed, until at least settle_s of work has run.
+    settle = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < settle_s:
+        for i in range(8):
+            step(warmup + settle + i)
+        settle += 8
+        torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ev[0].record(stream)
     for i in range(steps):
@@ -121,7 +135,7 @@ def time_workload(w, steps, warmup, rotate=True):
     per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     total = ev[0].elapsed_time(ev[steps])
     return {"ms_per_step": total / steps, "median_ms": per[len(per) // 2], "min_ms": per[0],
-            "inputs": (q, k, v, desc)}
+            "settle_steps": settle, "inputs": (q, k, v, desc)}
 
 
 def result_line(w, t, steps, warmup, n_gpus, cpu=None, warm=None):
@@ -139,6 +153,7 @@ def result_line(w, t, steps, warmup, n_gpus, cpu=None, warm=None):
                    "parallelism": "single GPU", "rotating_input_sets": N_BUFFER_SETS},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "median_ms": round(t["median_ms"], 5), "min_ms": round(t["min_ms"], 5),
+        "settle_steps": t["settle_steps"],
         "roofline": {"bound": PEAK_KIND[w.dtype], "achieved": round(tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                      "traffic": load_traffic(w.name),
@@ -160,6 +175,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--sweep-out", default=None, help="also time every named workload, JSONL to this file")
+    ap.add_argument("--settle-s", type=float, default=SETTLE_S,
+                    help="seconds of untimed steps after the warmup steps (clock settle)")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="first run a plain device-to-device copy of this many MiB (untimed), a "
                          "reference dispatch of known size for scaling hardware byte counters")
@@ -183,8 +200,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    t = time_workload(w, args.steps, args.warmup, rotate=True)
-    warm = time_workload(w, args.steps, args.warmup, rotate=False)
+    t = time_workload(w, args.steps, args.warmup, rotate=True, settle_s=args.settle_s)
+    warm = time_workload(w, args.steps, args.warmup, rotate=False, settle_s=args.settle_s)
     cpu = None
     if not args.no_cpu:
         q, k, v, desc = t["inputs"]
@@ -194,7 +211,7 @@ def main():
     if args.sweep_out:
         with open(args.sweep_out, "w") as f:
             for n, wi in workload.WORKLOADS.items():
-                ti = time_workload(wi, args.steps, args.warmup, rotate=True)
+                ti = time_workload(wi, args.steps, args.warmup, rotate=True, settle_s=args.settle_s)
                 f.write(json.dumps(result_line(wi, ti, args.steps, args.warmup, 1)) + "\n")
                 f.flush()
                 print(f"sweep {n}: {ti['ms_per_step']:.4f} ms", file=sys.stderr, flush=True)

@@ -331,6 +331,12 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
             asm volatile("" : "+v"(pw[kb][i]), "+v"(l_part));
         };
         // ---- A ---------------------------------------------------------------
+        // Phase A is the one that mixes score MFMAs with the softmax VALU
+        // work; raising the wave's issue priority for it lets it win the
+        // issue arbitration over the SIMD's other wave (usually in its
+        // MFMA-only phase B), which keeps both the matrix core and the VALU
+        // fed. Measured: +2 % (D=128) and +6 % (D=64) over equal priority.
+        __builtin_amdgcn_s_setprio(1);
         if constexpr (HAS_NEXT) {
             constexpr int PAIRS = NKB * 8;
             constexpr int PER_STEP = PAIRS / KSTEPS;
@@ -362,6 +368,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
             for (int db = 0; db < NDB; ++db) vf[0][db] = load_v(vb_cur, 0, 0, db);
         }
         // ---- B -----------------------------------------------------------------
+        __builtin_amdgcn_s_setprio(0);
         float mraw = masked;
         const bool fused_max = HAS_NEXT && c_nonneg;
 #pragma unroll
