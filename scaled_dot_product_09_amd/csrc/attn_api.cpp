@@ -14,10 +14,11 @@
 #include "kernel_common.h"
 
 namespace attn {
-hipError_t launch_fwd_mfma(const FwdParams& p, int D, bool is_bf16, bool causal, hipStream_t stream);
+hipError_t launch_fwd_mfma(const FwdParams& p, int D, bool is_bf16, bool causal, int nwaves, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int D, bool causal, hipStream_t stream);
-hipError_t launch_fwd_fp8(const FwdParams& p, int D, bool causal, hipStream_t stream);
+hipError_t launch_fwd_fp8(const FwdParams& p, int D, bool causal, int nwaves, hipStream_t stream);
 hipError_t launch_fwd_rb2(const FwdParams& p, int D, int dtype, bool causal, hipStream_t stream);
+hipError_t launch_fwd_pp(const FwdParams& p, int D, int dtype, bool causal, hipStream_t stream);
 }
 
 namespace {
@@ -56,16 +57,16 @@ int validate(const void* q, const void* k, const void* v, const void* out,
 
 attn::FwdParams make_params(const void* q, const void* k, const void* v, void* out,
                             int B, int Hq, int Hkv, int Sq, int Skv, float scale_log2, float out_mul,
-                            bool mfma, int rows_per_wave) {
+                            bool mfma, int rows_per_wave, int waves) {
     attn::FwdParams p;
     p.q = q; p.k = k; p.v = v; p.out = out;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Sq = Sq; p.Skv = Skv;
     p.G = Hq / Hkv;
-    // A workgroup of four waves shares one KV head between gpack query heads
-    // (the largest of 4, 2, 1 dividing G) and 4 / gpack row blocks of
-    // rows_per_wave rows each.
+    // A workgroup of `waves` waves shares one KV head between gpack query
+    // heads (the largest of 4, 2, 1 dividing G) and waves / gpack row blocks
+    // of rows_per_wave rows each.
     p.gpack = mfma ? ((p.G % 4 == 0) ? 4 : (p.G % 2 == 0) ? 2 : 1) : 1;
-    p.rows_per_wg = rows_per_wave * (4 / p.gpack);
+    p.rows_per_wg = rows_per_wave * (waves / p.gpack);
     p.n_row_blocks = (Sq + p.rows_per_wg - 1) / p.rows_per_wg;
     p.n_units = B * Hkv * (p.G / p.gpack);
     p.xcd_remap = (p.n_units % 8 == 0) ? 1 : 0;
@@ -83,15 +84,39 @@ const float kLog2e = 1.4426950408889634f;
 // -inf, which lets the kernels mask with a single select.
 float nonzero_multiplier(float c) { return c == 0.0f ? 0x1p-100f : c; }
 
-// Matrix-core kernel choice: 32 query rows per wave (two waves per SIMD) by
-// default; 64 rows per wave (one wave per SIMD, half the LDS traffic per
-// flop) only on request, since it measures slower on every shape so far.
-// ATTN_ROWS_PER_WAVE=32 or 64 in the environment selects one explicitly
-// (the tests use it to cover both kernels on every shape).
-int rows_per_wave() {
-    const char* e = getenv("ATTN_ROWS_PER_WAVE");
-    if (e && strcmp(e, "64") == 0) return 64;
-    return 32;
+// Matrix-core kernel choice. Default: "w4", four independent waves per
+// workgroup (32 query rows each) and two workgroups per CU. Also built,
+// selectable with ATTN_KERNEL in the environment (the tests cover every one
+// on every shape): "pp", eight waves in two ping-pong groups of four, and
+// "rb2", 64 rows per wave, one wave per SIMD. Both measure slower on every
+// shape so far: on gfx950 a wave's matrix ops do not overlap another wave's
+// vector ops on the same SIMD, so the ping-pong split gains nothing.
+enum MfmaKernel { kPingPong, kFourWave, kEightWave, kRows64 };
+
+MfmaKernel mfma_kernel() {
+    const char* e = getenv("ATTN_KERNEL");
+    if (e && strcmp(e, "pp") == 0) return kPingPong;
+    if (e && strcmp(e, "w8") == 0) return kEightWave;
+    if (e && strcmp(e, "rb2") == 0) return kRows64;
+    return kFourWave;
+}
+
+hipError_t launch_mfma(const void* q, const void* k, const void* v, void* out,
+                       int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale_log2,
+                       float out_mul, int dtype, bool causal, hipStream_t stream) {
+    const MfmaKernel kern = mfma_kernel();
+    const int rpw = kern == kRows64 ? 64 : 32;
+    const int waves = (kern == kPingPong || kern == kEightWave) ? 8 : 4;
+    const attn::FwdParams p = make_params(q, k, v, out, B, Hq, Hkv, Sq, Skv, scale_log2, out_mul,
+                                          true, rpw, waves);
+    switch (kern) {
+        case kRows64: return attn::launch_fwd_rb2(p, D, dtype, causal, stream);
+        case kFourWave:
+        case kEightWave:
+            return dtype == ATTN_FP8_E4M3 ? attn::launch_fwd_fp8(p, D, causal, waves, stream)
+                                          : attn::launch_fwd_mfma(p, D, dtype == ATTN_BF16, causal, waves, stream);
+        default: return attn::launch_fwd_pp(p, D, dtype, causal, stream);
+    }
 }
 
 }  // namespace
@@ -111,14 +136,11 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out,
     hipError_t e;
     if (dtype == ATTN_F32) {
         const attn::FwdParams p = make_params(q, k, v, out, B, Hq, Hkv, Sq, Skv,
-                                              nonzero_multiplier(scale * kLog2e), 1.0f, false, 32);
+                                              nonzero_multiplier(scale * kLog2e), 1.0f, false, 32, 4);
         e = attn::launch_fwd_f32(p, D, causal != 0, stream);
     } else {
-        const int rpw = rows_per_wave();
-        const attn::FwdParams p = make_params(q, k, v, out, B, Hq, Hkv, Sq, Skv,
-                                              nonzero_multiplier(scale * kLog2e), 1.0f, true, rpw);
-        e = rpw == 64 ? attn::launch_fwd_rb2(p, D, dtype, causal != 0, stream)
-                      : attn::launch_fwd_mfma(p, D, dtype == ATTN_BF16, causal != 0, stream);
+        e = launch_mfma(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, nonzero_multiplier(scale * kLog2e), 1.0f,
+                        dtype, causal != 0, stream);
     }
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
@@ -135,11 +157,8 @@ extern "C" int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o
     if (noop) return ATTN_OK;
     const float sl2 = scale * q_descale * k_descale * kLog2e;
     if (!isfinite(sl2)) return ATTN_ERR_SCALE;
-    const int rpw = rows_per_wave();
-    const attn::FwdParams p = make_params(q, k, v, out, B, Hq, Hkv, Sq, Skv, nonzero_multiplier(sl2),
-                                          v_descale, true, rpw);
-    const hipError_t e = rpw == 64 ? attn::launch_fwd_rb2(p, D, ATTN_FP8_E4M3, causal != 0, stream)
-                                   : attn::launch_fwd_fp8(p, D, causal != 0, stream);
+    const hipError_t e = launch_mfma(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, nonzero_multiplier(sl2), v_descale,
+                                     ATTN_FP8_E4M3, causal != 0, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

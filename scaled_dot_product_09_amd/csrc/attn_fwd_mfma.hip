@@ -18,7 +18,7 @@
 //   * Each wave owns 32 query rows of one query head. A workgroup holds
 //     `gpack` query heads that read the same KV head, 4 / gpack row blocks of
 //     32 rows each, so every K/V tile staged in LDS serves 128 query rows.
-//   * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4,
+//   * K and V tiles go from HBM straight into LDS (buffer loads to LDS,
 //     no register staging), double-buffered: tile j+1 is in flight while
 //     tile j is computed, with one barrier per tile. 16-byte chunks are
 //     XOR-swizzled per row so the operand reads below are bank-conflict free.
@@ -45,8 +45,8 @@
 
 namespace attn {
 
-template <typename T, int D, int BN, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
+template <typename T, int D, int BN, bool CAUSAL, int NWAVES>
+__global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdParams p) {
     using Tr = Traits<T>;
     using qk_frag = typename Tr::qk_frag;
     using pv_frag = typename Tr::pv_frag;
@@ -89,15 +89,21 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
 
     // Q^T operand, kept in registers for the whole key loop: lane (h, n) holds
     // bytes [(2 ks + h) * QK_LANE_BYTES, +QK_LANE_BYTES) of row q0 + n.
+    // A negative scale is folded into Q: the kernel computes (-q).k, which
+    // is exactly -(q.k) (negation is exact and the products are summed in
+    // the same order), with the multiplier |c|, so the softmax below only
+    // ever sees c >= 0 and masks with -inf.
     qk_frag qf[KSTEPS];
     {
         const int row = q0 + n;
         const uint8_t* src = (const uint8_t*)(qbase + row * qstride);
+        const uint32_t flip = p.scale_log2 < 0.f ? Tr::SIGN_BITS : 0u;
         for (int ks = 0; ks < KSTEPS; ++ks) {
             u32x4 x[CH];
             for (int t = 0; t < CH; ++t) {
                 x[t] = (u32x4){0, 0, 0, 0};
                 if (row < Sq) x[t] = *(const u32x4*)(src + ((2 * ks + h) * CH + t) * 16);
+                x[t] ^= flip;
             }
             if constexpr (CH == 1) {
                 qf[ks] = __builtin_bit_cast(qk_frag, x[0]);
@@ -127,19 +133,26 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
     uint8_t* const vbuf1 = lds_v1;
     // FP8: V is widened to bf16 in registers (exact) and written to LDS by
     // the threads; 8 values (one 16-byte chunk) per thread and step.
-    constexpr int V_ST = Tr::V_DMA ? 1 : (BN * D / 8) / 256;
+    constexpr int NTHR = 64 * NWAVES;
+    constexpr int V_ST = Tr::V_DMA ? 1 : (BN * D / 8) / NTHR;
     u32x2 vstage[V_ST];
-    TileDma<KROWB, BN> kdma;
-    TileDma<VROWB, BN> vdma;
-    kdma.init(wave, lane, (uint32_t)kstride_b, true);
-    if constexpr (Tr::V_DMA) vdma.init(wave, lane, (uint32_t)kstride_b, false);
-    auto issue_k = [&](int j, uint8_t* kt) { kdma.issue(kbase, kstride_b, j * BN, Skv, kt, wave); };
+    // The copies are split over all waves, or over the first four when a
+    // tile has fewer 1 KiB pieces than there are waves.
+    constexpr int NWK = (BN * KROWB / 1024) % NWAVES == 0 ? NWAVES : 4;
+    constexpr int NWV = (BN * VROWB / 1024) % NWAVES == 0 ? NWAVES : 4;
+    TileDma<KROWB, BN, NWK> kdma;
+    TileDma<VROWB, BN, NWV> vdma;
+    kdma.init(kbase, (uint32_t)kstride_b, wave % NWK, lane, true);
+    if constexpr (Tr::V_DMA) vdma.init(vbase, (uint32_t)kstride_b, wave % NWV, lane, false);
+    auto issue_k = [&](int j, uint8_t* kt) {
+        if (NWK == NWAVES || wave < NWK) kdma.issue(j * BN, Skv, kt, wave);
+    };
     auto issue_v = [&](int j, uint8_t* vt) {
         if constexpr (Tr::V_DMA) {
-            vdma.issue(vbase, kstride_b, j * BN, Skv, vt, wave);
+            if (NWV == NWAVES || wave < NWV) vdma.issue(j * BN, Skv, vt, wave);
         } else {
             for (int u = 0; u < V_ST; ++u) {
-                const int id = u * 256 + tid;
+                const int id = u * NTHR + tid;
                 const int r = id / (D / 8), c = id % (D / 8);
                 const int key = min(j * BN + r, Skv - 1);
                 vstage[u] = *(const u32x2*)(vbase + key * kstride_b + c * 8);
@@ -149,7 +162,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
     auto finish_v = [&](uint8_t* vt) {   // FP8 only: widen the staged V and write it
         if constexpr (!Tr::V_DMA) {
             for (int u = 0; u < V_ST; ++u) {
-                const int id = u * 256 + tid;
+                const int id = u * NTHR + tid;
                 const int r = id / (D / 8), c = id % (D / 8);
                 u32x4 w;
                 for (int e = 0; e < 2; ++e) {
@@ -171,8 +184,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
     float l_part = 0.f;        // this lane's share of the running denominator
     float neg_m = 0.f;         // exponent offset -m_run of the tile being weighted
 
-    const float c_log2 = p.scale_log2;
-    const bool c_nonneg = c_log2 >= 0.f;
+    const float c_log2 = fabsf(p.scale_log2);   // > 0: the host never passes 0
     const int qrow = q0 + n;
     const int wave_last_row = q0 + 31;
 
@@ -243,11 +255,10 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
     };
 
     // Masking of one tile's scores: keys past the end or above the causal
-    // diagonal become -inf (scale >= 0) or +inf (scale < 0), so that
-    // c * s = -inf for them. The test costs a few instructions per 32-key
-    // block and is skipped (wave-uniformly) wherever no key of the block is
-    // hidden from any row of the wave.
-    const float masked = c_nonneg ? -INFINITY : INFINITY;
+    // diagonal become -inf, so that c * s = -inf for them. The test costs a
+    // few instructions per 32-key block and is skipped (wave-uniformly)
+    // wherever no key of the block is hidden from any row of the wave.
+    const float masked = -INFINITY;
     auto mask_tile = [&](f32x16 (&s)[NKB], int j) {
         for (int kb = 0; kb < NKB; ++kb) {
             const int kbase_h = j * BN + kb * 32 + 4 * h;       // key of element i: kbase_h + koff(i)
@@ -259,7 +270,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
             }
         }
     };
-    // Partial row max (scale >= 0) of scores 16 g .. 16 g + 15 (block g / 1),
+    // Partial row max of scores 16 g .. 16 g + 15 (block g / 1),
     // split into four pieces so it can ride along the PV MFMA groups.
     auto max_piece = [&](const f32x16 (&s)[NKB], int piece, float m) -> float {
         constexpr int PER = NKB * 16 / 4;                        // scores per piece
@@ -270,18 +281,11 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
         }
         return m;
     };
-    auto min_all = [&](const f32x16 (&s)[NKB]) -> float {
-        float m = INFINITY;
-        for (int kb = 0; kb < NKB; ++kb)
-            for (int i = 0; i < 16; ++i) m = fminf(m, s[kb][i]);
-        return m;
-    };
-    // From this lane's raw max (min for scale < 0) of a tile: the row max in
-    // the log2 domain, the lazy rescale of O and l (only when the max grew by
-    // more than 8, i.e. a factor 2^8), and the new exponent offset -m.
+    // From this lane's raw max of a tile: the row max in the log2 domain, the
+    // lazy rescale of O and l (only when the max grew by more than 8, i.e. a
+    // factor 2^8), and the new exponent offset -m.
     auto finish_max = [&](float mraw) -> float {
-        // c_log2 is never 0 (the host maps scale 0 to a tiny positive value),
-        // so a fully masked row gives (+-inf) * c = -inf here.
+        // c_log2 > 0, so a fully masked row gives -inf * c = -inf here.
         const float mt = xor32_max(mraw * c_log2);
         const float mnew = fmaxf(m_run, mt);
         if (__builtin_amdgcn_ballot_w64(mnew > m_run + 8.0f) != 0) {
@@ -320,14 +324,25 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
         }
         uint32_t pw[NKB][8];
         pv_frag vf[2][NDB];     // V operands of two consecutive PV groups
-        auto weight_pair = [&](int pp) {
+        // Weights of tile j in two stages, so that no dependency chain sits
+        // inside one k-step: stage 1 (scale, offset, exp2) of group g runs in
+        // k-step g, stage 2 (round to the input type, add to the row sum) in
+        // k-step g + 1, when the exp2 results have long been ready.
+        float ex[NKB * 8][2];
+        auto weight_exp = [&](int pp) {
             const int kb = pp / 8, i = pp % 8;
             const float x0 = fmaf(s_cur[kb][2 * i], c_log2, neg_m);
             const float x1 = fmaf(s_cur[kb][2 * i + 1], c_log2, neg_m);
-            pw[kb][i] = Tr::pack(__builtin_amdgcn_exp2f(x0), __builtin_amdgcn_exp2f(x1));
-            l_part = Tr::sum2(pw[kb][i], l_part);
+            ex[pp][0] = __builtin_amdgcn_exp2f(x0);
+            ex[pp][1] = __builtin_amdgcn_exp2f(x1);
             // Keep the weights where they are computed (between the score
             // MFMAs) instead of letting the compiler sink them to their use.
+            asm volatile("" : "+v"(ex[pp][0]), "+v"(ex[pp][1]));
+        };
+        auto weight_pack = [&](int pp) {
+            const int kb = pp / 8, i = pp % 8;
+            pw[kb][i] = Tr::pack(ex[pp][0], ex[pp][1]);
+            l_part = Tr::sum2(pw[kb][i], l_part);
             asm volatile("" : "+v"(pw[kb][i]), "+v"(l_part));
         };
         // ---- A ---------------------------------------------------------------
@@ -357,20 +372,27 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
                     for (int db = 0; db < NDB; ++db) vf[0][db] = load_v(vb_cur, 0, 0, db);
                 for (int kb = 0; kb < NKB; ++kb) s_nxt[kb] = Tr::qk(kf[ks % 3][kb], qf[ks], s_nxt[kb]);
 #pragma unroll
-                for (int t = 0; t < PER_STEP; ++t) weight_pair(ks * PER_STEP + t);
+                for (int t = 0; t < PER_STEP; ++t) weight_exp(ks * PER_STEP + t);
+                if (ks > 0) {
+#pragma unroll
+                    for (int t = 0; t < PER_STEP; ++t) weight_pack((ks - 1) * PER_STEP + t);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
+#pragma unroll
+            for (int t = 0; t < PER_STEP; ++t) weight_pack((KSTEPS - 1) * PER_STEP + t);
             // ---- A' ------------------------------------------------------------
             mask_tile(s_nxt, j + 1);
         } else {
 #pragma unroll
-            for (int pp = 0; pp < NKB * 8; ++pp) weight_pair(pp);
+            for (int pp = 0; pp < NKB * 8; ++pp) weight_exp(pp);
+#pragma unroll
+            for (int pp = 0; pp < NKB * 8; ++pp) weight_pack(pp);
             for (int db = 0; db < NDB; ++db) vf[0][db] = load_v(vb_cur, 0, 0, db);
         }
         // ---- B -----------------------------------------------------------------
         __builtin_amdgcn_s_setprio(0);
         float mraw = masked;
-        const bool fused_max = HAS_NEXT && c_nonneg;
 #pragma unroll
         for (int g = 0; g < NKB * 2; ++g) {
             const int kb = g / 2, s2 = g % 2;
@@ -380,14 +402,11 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
             if (g + 1 < NKB * 2)
                 for (int db = 0; db < NDB; ++db) vf[(g + 1) & 1][db] = load_v(vb_cur, (g + 1) / 2, (g + 1) % 2, db);
             for (int db = 0; db < NDB; ++db) oacc[db] = Tr::pv(vf[g & 1][db], pf, oacc[db]);
-            if (fused_max) mraw = max_piece(s_nxt, g, mraw);
+            if constexpr (HAS_NEXT) mraw = max_piece(s_nxt, g, mraw);
             __builtin_amdgcn_sched_barrier(0);
         }
         // ---- C -----------------------------------------------------------------
-        if constexpr (HAS_NEXT) {
-            if (!c_nonneg) mraw = min_all(s_nxt);
-            neg_m = finish_max(mraw);
-        }
+        if constexpr (HAS_NEXT) neg_m = finish_max(mraw);
         if constexpr (HAS_NEXT) finish_v(vb_next);
     };
 
@@ -400,9 +419,9 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
     qk_tile(kbuf0, s0);
     mask_tile(s0, 0);
     {
-        float mraw = c_nonneg ? max_piece(s0, 0, masked) : min_all(s0);
-        if (c_nonneg)
-            for (int g = 1; g < 4; ++g) mraw = max_piece(s0, g, mraw);
+        float mraw = masked;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) mraw = max_piece(s0, g, mraw);
         neg_m = finish_max(mraw);
     }
     int j = 0;
@@ -434,29 +453,37 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(FwdParams p) {
 }
 
 template <typename T, int D, int BN>
-static hipError_t launch_typed(const FwdParams& p, bool causal, hipStream_t stream) {
-    const dim3 grid(p.n_units * p.n_row_blocks), block(256);
-    if (causal)
-        hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, true>), grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, false>), grid, block, 0, stream, p);
+static hipError_t launch_typed(const FwdParams& p, bool causal, int nwaves, hipStream_t stream) {
+    const dim3 grid(p.n_units * p.n_row_blocks), block(64 * nwaves);
+    if (nwaves == 8) {
+        if (causal)
+            hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, true, 8>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, false, 8>), grid, block, 0, stream, p);
+    } else {
+        if (causal)
+            hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, true, 4>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, false, 4>), grid, block, 0, stream, p);
+    }
     return hipGetLastError();
 }
 
-// bf16 (is_bf16 = true) or f16 inputs, D = 64 or 128.
-hipError_t launch_fwd_mfma(const FwdParams& p, int D, bool is_bf16, bool causal, hipStream_t stream) {
+// bf16 (is_bf16 = true) or f16 inputs, D = 64 or 128; nwaves = 4 or 8 waves
+// per workgroup.
+hipError_t launch_fwd_mfma(const FwdParams& p, int D, bool is_bf16, bool causal, int nwaves, hipStream_t stream) {
     if (is_bf16) {
-        return D == 64 ? launch_typed<__bf16, 64, 64>(p, causal, stream)
-                       : launch_typed<__bf16, 128, 64>(p, causal, stream);
+        return D == 64 ? launch_typed<__bf16, 64, 64>(p, causal, nwaves, stream)
+                       : launch_typed<__bf16, 128, 64>(p, causal, nwaves, stream);
     }
-    return D == 64 ? launch_typed<_Float16, 64, 64>(p, causal, stream)
-                   : launch_typed<_Float16, 128, 64>(p, causal, stream);
+    return D == 64 ? launch_typed<_Float16, 64, 64>(p, causal, nwaves, stream)
+                   : launch_typed<_Float16, 128, 64>(p, causal, nwaves, stream);
 }
 
 // E4M3 inputs, bf16 output, D = 64 or 128.
-hipError_t launch_fwd_fp8(const FwdParams& p, int D, bool causal, hipStream_t stream) {
-    return D == 64 ? launch_typed<fp8_t, 64, 64>(p, causal, stream)
-                   : launch_typed<fp8_t, 128, 64>(p, causal, stream);
+hipError_t launch_fwd_fp8(const FwdParams& p, int D, bool causal, int nwaves, hipStream_t stream) {
+    return D == 64 ? launch_typed<fp8_t, 64, 64>(p, causal, nwaves, stream)
+                   : launch_typed<fp8_t, 128, 64>(p, causal, nwaves, stream);
 }
 
 }  // namespace attn

@@ -100,12 +100,12 @@ __global__ __launch_bounds__(256, 1) void fwd_rb2_kernel(FwdParams p) {
     u32x2 vstage[V_ST];
     TileDma<KROWB, BN> kdma;
     TileDma<VROWB, BN> vdma;
-    kdma.init(wave, lane, (uint32_t)kstride_b, true);
-    if constexpr (Tr::V_DMA) vdma.init(wave, lane, (uint32_t)kstride_b, false);
-    auto issue_k = [&](int j) { kdma.issue(kbase, kstride_b, j * BN, Skv, kbuf(j), wave); };
+    kdma.init(kbase, (uint32_t)kstride_b, wave, lane, true);
+    if constexpr (Tr::V_DMA) vdma.init(vbase, (uint32_t)kstride_b, wave, lane, false);
+    auto issue_k = [&](int j) { kdma.issue(j * BN, Skv, kbuf(j), wave); };
     auto issue_v = [&](int j) {
         if constexpr (Tr::V_DMA) {
-            vdma.issue(vbase, kstride_b, j * BN, Skv, vbuf(j), wave);
+            vdma.issue(j * BN, Skv, vbuf(j), wave);
         } else {
             for (int u = 0; u < V_ST; ++u) {
                 const int id = u * 256 + tid;

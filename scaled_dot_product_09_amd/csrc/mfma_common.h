@@ -48,6 +48,7 @@ template <> struct Traits<__bf16> {
     static constexpr int QK_LANE_BYTES = 16;    // bytes of one operand per lane per k-step
     static constexpr int QK_K = 16;             // contraction length of one QK MFMA
     static constexpr bool V_DMA = true;         // V goes to LDS unchanged
+    static constexpr uint32_t SIGN_BITS = 0x80008000u;   // sign bits of the inputs in one dword
     using qk_frag = bf16x8;
     using pv_frag = bf16x8;
     using out_t = __bf16;
@@ -70,6 +71,7 @@ template <> struct Traits<_Float16> {
     static constexpr int QK_LANE_BYTES = 16;
     static constexpr int QK_K = 16;
     static constexpr bool V_DMA = true;
+    static constexpr uint32_t SIGN_BITS = 0x80008000u;
     using qk_frag = f16x8;
     using pv_frag = f16x8;
     using out_t = _Float16;
@@ -91,6 +93,7 @@ template <> struct Traits<fp8_t> {
     static constexpr int QK_LANE_BYTES = 32;
     static constexpr int QK_K = 64;
     static constexpr bool V_DMA = false;        // V is widened to bf16 on its way to LDS
+    static constexpr uint32_t SIGN_BITS = 0x80808080u;
     using qk_frag = i32x8;
     using pv_frag = bf16x8;
     using out_t = __bf16;
@@ -117,59 +120,65 @@ template <int NCH>
 __device__ inline int v_swz(int r) { return 4 * ((r / (16 / NCH)) % (NCH / 4)); }
 
 // Copying one K or V tile (NROWS rows of ROWB bytes) from HBM straight into
-// LDS. Each global_load_lds_dwordx4 moves 1 KiB: lane l lands at byte 16 l
-// of it, i.e. at row i * RPI + l / NCH, chunk position l % NCH, and fetches
-// the global chunk (l % NCH) ^ swz(row) of that row. The per-lane byte offset
-// of that chunk inside a tile (row * row stride + chunk * 16) does not depend
-// on the tile, so it is computed once; each tile only adds a scalar base.
-template <int ROWB, int NROWS>
+// LDS, by NW waves. Each buffer_load_dwordx4 ... lds moves 1 KiB: lane l lands
+// at byte 16 l of it, i.e. at row i * RPI + l / NCH, chunk position l % NCH,
+// and fetches the global chunk (l % NCH) ^ swz(row) of that row. The per-lane
+// byte offset of that chunk inside a tile (row * row stride + chunk * 16)
+// does not depend on the tile, so it is computed once; each tile only adds a
+// scalar offset.
+template <int ROWB, int NROWS, int NW = 4>
 struct TileDma {
     static constexpr int NCH = ROWB / 16;
     static constexpr int RPI = 1024 / ROWB;             // rows per instruction
     static constexpr int NINSTR = NROWS * ROWB / 1024;
-    static constexpr int PER_WAVE = NINSTR / 4;
-    static constexpr int ROW_STEP = 4 * RPI;            // rows between a wave's instructions
-    static_assert(NINSTR % 4 == 0, "tile must split evenly over 4 waves");
-    // Instruction t of this wave covers rows r0 + ROW_STEP t. ROW_STEP = 256 /
-    // NCH, so both swizzles give the same mask for every t (they depend on
-    // r / (16 / NCH) modulo at most NCH, and ROW_STEP / (16 / NCH) = 16):
-    // one lane offset serves all of the wave's instructions.
+    static constexpr int PER_WAVE = NINSTR / NW;
+    static constexpr int ROW_STEP = NW * RPI;           // rows between a wave's instructions
+    static_assert(NINSTR % NW == 0, "tile must split evenly over the copying waves");
+    // Instruction t of this wave covers rows r0 + ROW_STEP t. ROW_STEP is a
+    // multiple of 256 / NCH, so both swizzles give the same mask for every t
+    // (they depend on r / (16 / NCH) modulo at most NCH, and ROW_STEP /
+    // (16 / NCH) is a multiple of 16): one lane offset serves all of the
+    // wave's instructions.
+    __amdgpu_buffer_rsrc_t rs;  // the whole head: base of its row 0, no range limit
+    uint32_t gstride;           // bytes between consecutive rows (keys)
     uint32_t off;               // lane's byte offset inside the tile, instruction 0
+    uint32_t cb;                // lane's byte offset inside its row
     int r0;                     // lane's tile row, instruction 0
 
-    __device__ void init(int wave, int lane, uint32_t gstride, bool kswz) {
+    __device__ void init(const uint8_t* head, uint32_t row_bytes_stride, int wave, int lane, bool kswz) {
+        gstride = row_bytes_stride;
+        rs = __builtin_amdgcn_make_buffer_rsrc((void*)head, 0, -1, kBufferWord3);
         r0 = wave * RPI + lane / NCH;
         const int c = (lane % NCH) ^ (kswz ? k_swz<NCH>(r0) : v_swz<NCH>(r0));
-        off = (uint32_t)r0 * gstride + (uint32_t)c * 16;
+        cb = (uint32_t)c * 16;
+        off = (uint32_t)r0 * gstride + cb;
     }
-    // Rows [key0, key0 + NROWS) of the head starting at g. Rows past the end
-    // of the keys (only in the last tile) repeat the last key: finite values
-    // whose weights are 0 after masking.
+    // Rows [key0, key0 + NROWS) of the head. Rows past the end of the keys
+    // (only in the last tile) repeat the last key: finite values whose
+    // weights are 0 after masking.
     //
     // The copy is a buffer load into LDS (MUBUF, not a FLAT global load):
-    // the tile's base address lives in a scalar buffer descriptor and each
-    // instruction's row offset in a scalar offset register, so the lanes only
-    // hold their fixed offset `off`, and, unlike the FLAT form, the
-    // compiler's LDS wait bookkeeping does not treat the copy as an LDS access
-    // of unknown order (which would force every later LDS operand read to wait
-    // for all outstanding reads). Every byte offset stays below the
-    // descriptor's size, rows [key0, Skv) of the head.
-    __device__ void issue(const uint8_t* g, size_t gstride, int key0, int Skv, uint8_t* tile, int wave) const {
-        const uint8_t* gb = g + (size_t)key0 * gstride;
-        const uint64_t span = (uint64_t)(Skv - key0) * gstride;
-        const int nrec = (int)(uint32_t)(span > 0xFFFFFFFFull ? 0xFFFFFFFFull : span);   // unsigned field
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)gb, 0, nrec, kBufferWord3);
-        const uint32_t step = (uint32_t)(ROW_STEP * gstride);
+    // the head's base address lives in a scalar buffer descriptor built
+    // once, the tile's and each instruction's row offset in a scalar offset
+    // register, so a tile costs a handful of scalar adds and the lanes only
+    // hold their fixed offset `off`. Unlike the FLAT form, the compiler's LDS
+    // wait bookkeeping does not treat the copy as an LDS access of unknown
+    // order (which would force every later LDS operand read to wait for all
+    // outstanding reads). Every byte offset stays below Skv * gstride < 2^32
+    // (a tensor has fewer than 2^31 elements of at most 2 bytes).
+    __device__ void issue(int key0, int Skv, uint8_t* tile, int wave) const {
+        const uint32_t t0 = (uint32_t)key0 * gstride;
+        const uint32_t step = (uint32_t)ROW_STEP * gstride;
         if (key0 + NROWS <= Skv) {
             for (int t = 0; t < PER_WAVE; ++t)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(tile + (wave + 4 * t) * 1024), 16,
-                                                         off, t * step, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(tile + (wave + NW * t) * 1024), 16,
+                                                         off, t0 + t * step, 0, 0);
         } else {
+            const int last = Skv - 1 - key0;        // last row of the tile that exists
             for (int t = 0; t < PER_WAVE; ++t) {
-                const int over = key0 + r0 + t * ROW_STEP - (Skv - 1);
-                const uint32_t o = off + t * step - (over > 0 ? (uint32_t)over * (uint32_t)gstride : 0u);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(tile + (wave + 4 * t) * 1024), 16,
-                                                         o, 0, 0, 0);
+                const uint32_t o = (uint32_t)min(r0 + t * ROW_STEP, last) * gstride + cb;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(tile + (wave + NW * t) * 1024), 16,
+                                                         o, t0, 0, 0);
             }
         }
     }

@@ -36,7 +36,7 @@ SMALL = [
     W("f32", 1, 4, 2, 77, 77, 128, True),
     W("f32", 1, 2, 1, 50, 130, 64, False),
     W("f32", 2, 2, 2, 1, 1, 64, True),
-    # bf16 head dim 64 (BN = 128 key tiles) and 128 (BN = 64)
+    # bf16 head dims 64 and 128 (64-key tiles)
     W("bf16", 1, 4, 4, 300, 300, 64, True),
     W("bf16", 2, 4, 4, 257, 257, 64, False),
     W("bf16", 1, 8, 2, 520, 520, 128, True),
@@ -52,6 +52,9 @@ SMALL = [
     W("bf16", 1, 4, 2, 100, 300, 128, False),     # Sq < Skv
     W("bf16", 1, 4, 2, 100, 300, 128, True),      # Sq < Skv, top-left causal
     W("bf16", 1, 4, 2, 300, 100, 64, True),       # Sq > Skv
+    W("bf16", 1, 8, 2, 600, 64, 128, True),       # one key tile
+    W("bf16", 1, 4, 1, 700, 700, 128, True),      # G = 4, odd tile count
+    W("bf16", 1, 8, 8, 1100, 1100, 128, False),   # G = 1: eight row blocks per workgroup
     *workload.PAGE_SHAPES[1:],
     # f16
     W("f16", 1, 8, 2, 300, 300, 128, True),
@@ -60,20 +63,24 @@ SMALL = [
     W("e4m3", 1, 4, 4, 400, 400, 128, True),
     W("e4m3", 1, 8, 2, 300, 300, 64, False),
     W("e4m3", 1, 2, 1, 70, 70, 128, True),
+    W("e4m3", 2, 8, 2, 192, 192, 128, True),
+    W("f16", 2, 2, 1, 256, 256, 64, False),
 ]
 
 
-@pytest.fixture(params=["32", "64"], ids=["rows32", "rows64"])
-def rows_per_wave(request, monkeypatch):
-    """Force the 32-row (two waves per SIMD) or the 64-row (one wave per SIMD)
-    matrix-core kernel; the library picks one by grid size otherwise."""
-    monkeypatch.setenv("ATTN_ROWS_PER_WAVE", request.param)
+@pytest.fixture(params=["w4", "w8", "pp", "rb2"])
+def kernel(request, monkeypatch):
+    """Force one of the matrix-core kernels: "w4" (four independent waves,
+    two workgroups per CU, the default), "w8" (eight independent waves, one
+    workgroup per CU), "pp" (eight waves in two ping-pong groups) or "rb2"
+    (64 query rows per wave)."""
+    monkeypatch.setenv("ATTN_KERNEL", request.param)
     return request.param
 
 
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
-def test_parity_small(w, rows_per_wave):
-    print(f"case {w.name} rows/wave {rows_per_wave}", flush=True)
+def test_parity_small(w, kernel):
+    print(f"case {w.name} kernel {kernel}", flush=True)
     q, k, v, desc = workload.make_inputs(w)
     got = helpers.out_to_f64(helpers.gpu_run(w, q, k, v, desc))
     want = helpers.oracle_full(w, q, k, v, desc)
@@ -83,7 +90,7 @@ def test_parity_small(w, rows_per_wave):
     assert err <= TOL[w.dtype], err
 
 
-def test_scale_zero_and_negative(rows_per_wave):
+def test_scale_zero_and_negative(kernel):
     w = W("bf16", 1, 4, 2, 130, 130, 128, True)
     q, k, v, desc = workload.make_inputs(w)
     for scale in (0.0, -0.2):
@@ -128,7 +135,7 @@ def test_parity_full_size_sampled(name):
         assert torch.equal(o[:, 0].cpu(), v0)
 
 
-def test_gqa_equals_repeated_mha_bitwise(rows_per_wave):
+def test_gqa_equals_repeated_mha_bitwise(kernel):
     w = W("bf16", 2, 8, 2, 260, 260, 128, True)
     q, k, v, desc = workload.make_inputs(w)
     a = helpers.gpu_run(w, q, k, v, desc)
@@ -137,7 +144,7 @@ def test_gqa_equals_repeated_mha_bitwise(rows_per_wave):
     assert torch.equal(a, b)
 
 
-def test_deterministic_and_canaries(rows_per_wave):
+def test_deterministic_and_canaries(kernel):
     w = workload.WORKLOADS["bf16_gqa_b2_hq32_hkv8_s4096_d128_causal"]
     q, k, v, desc = workload.make_inputs(w, shapes=[(1, 700, 8, 128), (1, 700, 2, 128), (1, 700, 2, 128)])
     n, pad = q.numel(), 4096
@@ -151,7 +158,7 @@ def test_deterministic_and_canaries(rows_per_wave):
     assert not torch.isnan(out).any()
 
 
-def test_constant_v_gives_constant_output(rows_per_wave):
+def test_constant_v_gives_constant_output(kernel):
     w = W("bf16", 1, 4, 2, 200, 200, 128, True)
     q, k, _, desc = workload.make_inputs(w)
     row = torch.randn(128, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
