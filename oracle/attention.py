@@ -12,8 +12,15 @@ Layout follows [Attention codelab §3]: Q is (B, T, N, H) and K, V are
 Readings taken where the pages are silent (each is pinned by a test):
 
 * Causal alignment when Sq != Skv: the pages only ever use Sq == Skv. The
-  reading here is the literal lower triangle of the Sq x Skv score matrix
-  (key j visible to query i iff j <= i), called top-left alignment.
+  reading for ``causal=True`` (also ``"top_left"``, 1) is the literal lower
+  triangle of the Sq x Skv score matrix (key j visible to query i iff
+  j <= i), called top-left alignment.
+* ``causal="bottom_right"`` (also 2) is the key-value-cache reading of the
+  grouped / multi-query inference use the pages motivate [Attention codelab
+  §9]: the Sq queries are the last Sq positions of a sequence of Skv tokens,
+  so query i sits at position Skv - Sq + i and sees keys j <= Skv - Sq + i.
+  It needs Sq <= Skv (every query then sees at least key 0). With Sq == Skv
+  both readings coincide.
 * Grouping of query heads onto KV heads [Attention codelab §9]: contiguous
   groups, query head h reads KV head h // (Hq // Hkv). This equals repeating
   each KV head Hq // Hkv times in a row along the head axis.
@@ -40,6 +47,24 @@ def kv_head_of(hq, Hq, Hkv):
     return hq // (Hq // Hkv)
 
 
+def _query_shift(causal, Sq, Skv):
+    """None without a mask, else the position of query row 0.
+
+    ``False``/0: no mask. ``True``/1/``"top_left"``: query i at position i.
+    ``"bottom_right"``/2: query i at position Skv - Sq + i (requires
+    Sq <= Skv).
+    """
+    if causal is False or causal == 0 or causal is None:
+        return None
+    if causal is True or causal == 1 or causal == "top_left":
+        return 0
+    if causal == 2 or causal == "bottom_right":
+        if Sq > Skv:
+            raise ValueError(f"bottom-right causal alignment needs Sq <= Skv (got {Sq} > {Skv})")
+        return Skv - Sq
+    raise ValueError(f"unknown causal mode {causal!r}")
+
+
 def _check_shapes(q, k, v):
     if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
         raise ValueError("q, k, v must be 4-D (B, S, H, D)")
@@ -55,11 +80,11 @@ def _check_shapes(q, k, v):
 
 
 def _scores(qh, kh, scale, causal, row0):
-    """Score step + causal mask for query rows row0 .. row0+len(qh)-1.
+    """Score step + causal mask for queries at positions row0 .. row0+len(qh)-1.
 
     Score = scale * Q K^T ([Attention codelab §1] steps 1-2, §4). With
-    ``causal`` the entries with key index j > query index i are set to -inf,
-    the lower-triangular mask of [Attention codelab §7].
+    ``causal`` the entries with key index j > query position i are set to
+    -inf, the lower-triangular mask of [Attention codelab §7].
     """
     s = scale * (qh @ kh.T)
     if causal:
@@ -85,9 +110,10 @@ def attention_weights(q, k, *, scale, causal, b=0, hq=0):
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     B, Sq, Hq, D = q.shape
-    Hkv = k.shape[2]
+    Skv, Hkv = k.shape[1], k.shape[2]
     g = kv_head_of(hq, Hq, Hkv)
-    return _softmax_rows(_scores(q[b, :, hq, :], k[b, :, g, :], scale, causal, 0))
+    shift = _query_shift(causal, Sq, Skv)
+    return _softmax_rows(_scores(q[b, :, hq, :], k[b, :, g, :], scale, shift is not None, shift or 0))
 
 
 def sdpa(q, k, v, *, scale, causal, row_chunk=1024):
@@ -111,6 +137,7 @@ def sdpa(q, k, v, *, scale, causal, row_chunk=1024):
         return out
     if Skv == 0:
         raise ValueError("Skv must be >= 1 when Sq > 0")
+    shift = _query_shift(causal, Sq, Skv)
     for b in range(B):
         for hq in range(Hq):
             g = kv_head_of(hq, Hq, Hkv)
@@ -118,7 +145,7 @@ def sdpa(q, k, v, *, scale, causal, row_chunk=1024):
             vh = v[b, :, g, :]
             for r0 in range(0, Sq, row_chunk):
                 qh = q[b, r0:r0 + row_chunk, hq, :]
-                p = _softmax_rows(_scores(qh, kh, scale, causal, r0))
+                p = _softmax_rows(_scores(qh, kh, scale, shift is not None, (shift or 0) + r0))
                 out[b, r0:r0 + qh.shape[0], hq, :] = p @ vh
     return out
 
@@ -127,13 +154,14 @@ def sdpa_one_row(qvec, kh, vh, *, i, scale, causal):
     """Output vector of one query vector at position ``i`` against one head.
 
     ``qvec`` is (D,), ``kh`` and ``vh`` are that head's (Skv, D) keys and
-    values; the causal mask uses the query position ``i``. Same definition
-    as :func:`sdpa`, for one row.
+    values; with a true ``causal`` the mask hides keys j > i, where ``i`` is
+    the query's position (for bottom-right alignment the caller passes
+    Skv - Sq + row). Same definition as :func:`sdpa`, for one row.
     """
     qh = np.asarray(qvec, dtype=np.float64).reshape(1, -1)
     kh = np.asarray(kh, dtype=np.float64)
     vh = np.asarray(vh, dtype=np.float64)
-    p = _softmax_rows(_scores(qh, kh, scale, causal, i))
+    p = _softmax_rows(_scores(qh, kh, scale, bool(causal), i))
     return (p @ vh)[0]
 
 
@@ -148,10 +176,12 @@ def sdpa_rows(q, k, v, rows, *, scale, causal):
     k = np.asarray(k)
     v = np.asarray(v)
     B, Sq, Hq, D, Skv, Hkv = _check_shapes(q, k, v)
+    shift = _query_shift(causal, Sq, Skv)
     res = np.empty((len(rows), D), dtype=np.float64)
     for n, (b, i, hq) in enumerate(rows):
         g = kv_head_of(hq, Hq, Hkv)
-        res[n] = sdpa_one_row(q[b, i, hq, :], k[b, :, g, :], v[b, :, g, :], i=i, scale=scale, causal=causal)
+        res[n] = sdpa_one_row(q[b, i, hq, :], k[b, :, g, :], v[b, :, g, :], i=(shift or 0) + i, scale=scale,
+                              causal=shift is not None)
     return res
 
 
@@ -161,6 +191,7 @@ def brute_sdpa(q, k, v, *, scale, causal):
     No numpy arithmetic at all: every score is a Python dot product, the
     softmax is exp(s - max) / sum, and each output element is a weighted sum,
     written directly from [Attention codelab §1]. Used to pin :func:`sdpa`.
+    ``causal`` takes the same values as in :func:`sdpa`.
     """
     B = len(q)
     Sq = len(q[0]) if B else 0
@@ -169,6 +200,7 @@ def brute_sdpa(q, k, v, *, scale, causal):
     Skv = len(k[0])
     Hkv = len(k[0][0])
     G = Hq // Hkv
+    shift = _query_shift(causal, Sq, Skv)
     out = [[[[0.0] * D for _ in range(Hq)] for _ in range(Sq)] for _ in range(B)]
     for b in range(B):
         for i in range(Sq):
@@ -176,7 +208,7 @@ def brute_sdpa(q, k, v, *, scale, causal):
                 g = h // G
                 s = []
                 for j in range(Skv):
-                    if causal and j > i:
+                    if shift is not None and j > shift + i:
                         continue
                     dot = 0.0
                     for d in range(D):

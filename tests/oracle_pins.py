@@ -10,7 +10,8 @@ show that each mistake is caught.
 Source: the codelab "Accelerate attention on GPU with cuDNN and
 TransformerEngine" — §1 (formula, weights summing to 1, output shaped like
 Q), §7 (causal mask: first position sees only itself, last sees all), §9
-(MHA / GQA / MQA broadcast, output shape unchanged).
+(MHA / GQA / MQA broadcast, output shape unchanged; the key-value-cache
+inference use that the bottom-right causal alignment serves).
 """
 
 import json
@@ -167,7 +168,9 @@ def pin_brute_force(fn):
     for (B, Sq, Skv, Hq, Hkv, D) in [(1, 3, 3, 1, 1, 2), (2, 5, 7, 4, 2, 3), (1, 9, 4, 4, 1, 8),
                                      (2, 6, 6, 2, 2, 5)]:
         q, k, v = _rand(B + Sq, B, Sq, Hq, D), _rand(Skv + 1, B, Skv, Hkv, D), _rand(D + 7, B, Skv, Hkv, D)
-        for causal in (False, True):
+        for causal in (False, True, "bottom_right"):
+            if causal == "bottom_right" and Sq > Skv:
+                continue
             got = fn(q, k, v, scale=0.37, causal=causal)
             want = np.array(oracle.brute_sdpa(q.tolist(), k.tolist(), v.tolist(), scale=0.37, causal=causal))
             np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
@@ -185,20 +188,54 @@ def pin_torch_cpu_library(fn):
         tv = torch.from_numpy(np.repeat(v, Hq // Hkv, axis=2)).permute(0, 2, 1, 3).contiguous()
         ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal)
         np.testing.assert_allclose(got, ref.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-10)
+    # Bottom-right alignment against torch's lower-right causal bias, Sq < Skv.
+    from torch.nn.attention.bias import causal_lower_right
+    Sq = 7
+    q = _rand(41, B, Sq, Hq, D)
+    got = fn(q, k, v, scale=1 / math.sqrt(D), causal="bottom_right")
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=causal_lower_right(Sq, S))
+    np.testing.assert_allclose(got, ref.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-10)
 
 
 def pin_rows_match_full(fn=None):
     """Sampled single rows (used at full problem sizes) equal the full result."""
     q, k, v = _rand(38, 2, 40, 4, 8), _rand(39, 2, 40, 2, 8), _rand(40, 2, 40, 2, 8)
-    for causal in (False, True):
-        full = oracle.sdpa(q, k, v, scale=0.5, causal=causal, row_chunk=7)
-        rows = [(0, 0, 0), (1, 39, 3), (1, 17, 2), (0, 25, 1)]
-        got = oracle.sdpa_rows(q, k, v, rows, scale=0.5, causal=causal)
-        for n, (b, i, h) in enumerate(rows):
-            np.testing.assert_allclose(got[n], full[b, i, h], rtol=0, atol=1e-13)
+    for causal in (False, True, "bottom_right"):
+        for qq in (q, q[:, 11:]):
+            full = oracle.sdpa(qq, k, v, scale=0.5, causal=causal, row_chunk=7)
+            rows = [(0, 0, 0), (1, qq.shape[1] - 1, 3), (1, 17, 2), (0, 25, 1)]
+            got = oracle.sdpa_rows(qq, k, v, rows, scale=0.5, causal=causal)
+            for n, (b, i, h) in enumerate(rows):
+                np.testing.assert_allclose(got[n], full[b, i, h], rtol=0, atol=1e-13)
+
+
+def pin_bottom_right_is_cache_suffix(fn):
+    """§9 key-value-cache reading: the Sq new queries at the end of a
+    sequence of Skv tokens, attending with bottom-right alignment, give
+    exactly the last Sq rows of causal self-attention over the whole
+    sequence (§7 mask), whatever Sq is."""
+    B, S, Hq, Hkv, D = 2, 29, 4, 2, 8
+    qf, k, v = _rand(42, B, S, Hq, D), _rand(43, B, S, Hkv, D), _rand(44, B, S, Hkv, D)
+    full = fn(qf, k, v, scale=0.45, causal=True)
+    for Sq in (1, 2, 5, 16, 29):
+        got = fn(qf[:, S - Sq:], k, v, scale=0.45, causal="bottom_right")
+        np.testing.assert_allclose(got, full[:, S - Sq:], rtol=0, atol=1e-12)
+
+
+def pin_bottom_right_limits(fn):
+    """Bottom-right alignment at its two ends: one query sees every key (the
+    same as no mask), and Sq == Skv is the ordinary §7 mask."""
+    q1, k, v = _rand(45, 1, 1, 2, 8), _rand(46, 1, 13, 1, 8), _rand(47, 1, 13, 1, 8)
+    np.testing.assert_allclose(fn(q1, k, v, scale=0.7, causal="bottom_right"),
+                               fn(q1, k, v, scale=0.7, causal=False), rtol=0, atol=1e-13)
+    q = _rand(48, 1, 13, 2, 8)
+    np.testing.assert_allclose(fn(q, k, v, scale=0.7, causal="bottom_right"),
+                               fn(q, k, v, scale=0.7, causal=True), rtol=0, atol=1e-13)
 
 
 ALL_PINS = [pin_golden, pin_weights_sum_to_one, pin_output_shape, pin_causal_first_row,
             pin_causal_last_row, pin_constant_v, pin_gqa_is_repeated_mha, pin_scale_zero_prefix_mean,
             pin_single_key, pin_two_keys_sigmoid, pin_shift_and_affine, pin_key_permutation,
-            pin_brute_force, pin_torch_cpu_library, pin_rows_match_full]
+            pin_brute_force, pin_torch_cpu_library, pin_rows_match_full, pin_bottom_right_is_cache_suffix,
+            pin_bottom_right_limits]

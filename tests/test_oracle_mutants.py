@@ -63,6 +63,19 @@ def _kv_head_modulo(hq, Hq, Hkv):
     return hq % Hkv
 
 
+_orig_shift = sdpa_mod._query_shift
+
+
+def _shift_bottom_right_as_top_left(causal, Sq, Skv):
+    r = _orig_shift(causal, Sq, Skv)
+    return 0 if r is not None else None
+
+
+def _shift_bottom_right_off_by_one(causal, Sq, Skv):
+    r = _orig_shift(causal, Sq, Skv)
+    return r + 1 if (r is not None and causal in (2, "bottom_right")) else r
+
+
 _orig_scores = sdpa_mod._scores
 
 MUTANTS = {
@@ -75,6 +88,8 @@ MUTANTS = {
     "softmax_not_normalised": ("_softmax_rows", _softmax_unnormalised),
     "softmax_without_exp": ("_softmax_rows", _softmax_no_exp),
     "kv_head_modulo": ("kv_head_of", _kv_head_modulo),
+    "bottom_right_as_top_left": ("_query_shift", _shift_bottom_right_as_top_left),
+    "bottom_right_off_by_one": ("_query_shift", _shift_bottom_right_off_by_one),
 }
 
 PINS = [p for p in oracle_pins.ALL_PINS if p is not oracle_pins.pin_brute_force]
