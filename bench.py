@@ -30,6 +30,7 @@ METRIC = "attention fwd TFLOP/s and % of MFMA peak at S=4096 causal GQA bf16"
 # MI355X published dense peaks (TFLOP/s) by arithmetic type of the products.
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "f32": 157.3}
 PEAK_KIND = {"bf16": "mfma", "f16": "mfma", "e4m3": "mfma", "f32": "alu"}
+PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E
 N_BUFFER_SETS = 4   # rotating input sets, so one call's inputs are not cache-warm from the last
 SETTLE_S = 0.25     # seconds of untimed steps after the warmup steps, before timing
 
@@ -108,10 +109,19 @@ def time_workload(w, steps, warmup, rotate=True, settle_s=SETTLE_S):
     fp8 = w.dtype == "e4m3"
     stream = torch.cuda.current_stream(dev)
 
+    ws = None
+    if w.n_split is not None:
+        n_split = w.n_split
+        if n_split == "auto":
+            n_split = attn.attn_split_suggest(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D, attn.CAUSAL_CODE[w.causal])
+        ws = torch.empty(max(attn.attn_split_workspace(w.B, w.Hq, w.Sq, w.D, n_split), 16), dtype=torch.uint8,
+                         device=dev)
+
     def step(i):
         qd, kd, vd, od = sets[i % nsets]
         attn.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=od,
-                 descales=desc if fp8 else None, stream=stream.cuda_stream)
+                 descales=desc if fp8 else None, stream=stream.cuda_stream,
+                 n_split=n_split if ws is not None else None, workspace=ws)
 
     for i in range(warmup):
         step(i)
@@ -135,7 +145,7 @@ def time_workload(w, steps, warmup, rotate=True, settle_s=SETTLE_S):
     per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     total = ev[0].elapsed_time(ev[steps])
     return {"ms_per_step": total / steps, "median_ms": per[len(per) // 2], "min_ms": per[0],
-            "settle_steps": settle, "inputs": (q, k, v, desc)}
+            "settle_steps": settle, "inputs": (q, k, v, desc), "n_split": n_split if ws is not None else 1}
 
 
 def result_line(w, t, steps, warmup, n_gpus, cpu=None, warm=None):
@@ -144,6 +154,18 @@ def result_line(w, t, steps, warmup, n_gpus, cpu=None, warm=None):
     ms = t["ms_per_step"]
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
+    nbytes = io_bytes(w)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    # Below the ridge point (peak flop/s over peak HBM bytes/s) the kernel is
+    # bound by HBM, not by the matrix cores.
+    hbm_bound = flops / nbytes < peak * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+    else:
+        roof = {"bound": PEAK_KIND[w.dtype], "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(tflops / peak, 4)}
+    roof.update({"traffic": load_traffic(w.name), "algorithmic_bytes": nbytes})
     line = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": n_gpus,
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
@@ -154,11 +176,12 @@ def result_line(w, t, steps, warmup, n_gpus, cpu=None, warm=None):
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "median_ms": round(t["median_ms"], 5), "min_ms": round(t["min_ms"], 5),
         "settle_steps": t["settle_steps"],
-        "roofline": {"bound": PEAK_KIND[w.dtype], "achieved": round(tflops, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
-                     "traffic": load_traffic(w.name),
-                     "algorithmic_bytes": io_bytes(w)},
+        "hbm_gbps": round(gbps, 1),
+        "roofline": roof,
     }
+    if t.get("n_split", 1) != 1:
+        line["config"]["n_split"] = t["n_split"]
+        line["config"]["entry_point"] = "attn_fwd_split"
     if warm is not None:
         line["warm_single_set_ms"] = round(warm["ms_per_step"], 5)
     if cpu is not None:

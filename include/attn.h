@@ -10,9 +10,14 @@
  * codelab "Accelerate attention on GPU with cuDNN and TransformerEngine",
  * §1 "How attention works", computed in the four steps listed there (score,
  * scale + softmax over keys, weighted sum of V, output shaped like Q).
- *   - causal != 0 applies the lower-triangular mask of §7 "Add a causal
+ *   - causal = 1 applies the lower-triangular mask of §7 "Add a causal
  *     mask": key j is visible to query i iff j <= i (top-left alignment when
  *     Sq != Skv; every row sees key 0, so no row is ever fully masked).
+ *   - causal = 2 is the same mask aligned to the bottom-right corner, the
+ *     key-value-cache form of the inference use §9 motivates GQA / MQA with:
+ *     the Sq queries are the last Sq of Skv tokens, so key j is visible to
+ *     query i iff j <= i + Skv - Sq. It needs Sq <= Skv. With Sq == Skv it
+ *     is the causal = 1 mask.
  *   - Hkv < Hq is the MHA / GQA / MQA broadcast of §9 "Compare MHA, GQA and
  *     MQA": contiguous groups of Hq / Hkv query heads share one K/V head.
  *   - The kernel is fused in the sense of §5-§6 of the codelab: one launch,
@@ -28,11 +33,13 @@
  * second product in the input type (bf16 / f16; bf16 on the FP8 path); the
  * output is rounded to nearest even once at the end.
  *
- * Ownership and synchronisation. The caller allocates and owns every buffer.
- * The library allocates nothing, keeps no pointer after it returns and never
- * synchronises: a call validates its arguments on the host, enqueues one
- * kernel on `stream` and returns. ATTN_OK means "enqueued". Calls are
- * stateless and may be made from several host threads at once.
+ * Ownership and synchronisation. The caller allocates and owns every buffer,
+ * including the workspace of attn_fwd_split. The library allocates nothing,
+ * keeps no pointer after it returns and never synchronises: a call validates
+ * its arguments on the host, enqueues its kernel(s) on `stream` and returns.
+ * ATTN_OK means "enqueued". Calls are stateless and may be made from several
+ * host threads at once (two calls sharing one workspace must be ordered, as
+ * for any buffer).
  *
  * Errors. Every entry point returns 0 or a negative attn_status. Arguments are
  * validated before any HIP call, so a rejected call launches nothing and
@@ -72,8 +79,16 @@ enum attn_status {
     ATTN_ERR_ALIGN = -6,      /* a pointer is not 16-byte aligned               */
     ATTN_ERR_ALIAS = -7,      /* out overlaps q, k or v                         */
     ATTN_ERR_SCALE = -8,      /* scale or a descale is NaN or infinite          */
-    ATTN_ERR_HIP = -9         /* the kernel launch failed (hipGetLastError)     */
+    ATTN_ERR_HIP = -9,        /* the kernel launch failed (hipGetLastError)     */
+    ATTN_ERR_CAUSAL = -10,    /* causal is not 0, 1 or 2, or causal = 2 with
+                                 Sq > Skv                                       */
+    ATTN_ERR_SPLIT = -11,     /* n_split outside 1 .. ATTN_MAX_SPLIT            */
+    ATTN_ERR_WORKSPACE = -12  /* workspace NULL, misaligned, too small, or
+                                 overlapping an input or the output             */
 };
+
+/* Largest number of key ranges attn_fwd_split accepts. */
+#define ATTN_MAX_SPLIT 256
 
 /*
  * attn_fwd — out = softmax(scale * q k^T [+ causal mask]) v.
@@ -87,7 +102,8 @@ enum attn_status {
  *            B * Sq == 0)
  *   D        head dimension, 64 or 128
  *   scale    any finite float; the codelab uses 1 / sqrt(D) (§4)
- *   causal   0 = full attention, nonzero = lower-triangular mask (§7)
+ *   causal   0 = full attention, 1 = lower-triangular mask (§7), 2 = the same
+ *            mask aligned bottom-right (Sq <= Skv; see above)
  *   dtype    ATTN_F32, ATTN_BF16 or ATTN_F16
  *   stream   HIP stream the kernel is enqueued on (0 = null stream)
  *
@@ -114,6 +130,42 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* out,
                  float scale, int causal,
                  float q_descale, float k_descale, float v_descale,
                  hipStream_t stream);
+
+/*
+ * attn_fwd_split — attn_fwd with the keys of every query row cut into
+ * n_split contiguous ranges that separate workgroups process, followed by a
+ * combine kernel (split-key or "flash-decoding" form). For grids too small
+ * to fill the GPU: few query rows against many keys, as in key-value-cache
+ * inference (§9). The result is the same softmax over all keys (each
+ * range's partial sums are rescaled to a common maximum before the one
+ * division), up to float rounding.
+ *
+ *   n_split    number of key ranges, 1 .. ATTN_MAX_SPLIT (attn_split_suggest
+ *              gives a value for the shape); 1 is exactly attn_fwd and needs
+ *              no workspace
+ *   workspace  device buffer of at least attn_split_workspace(...) bytes,
+ *              16-byte aligned, not overlapping q, k, v or out; its contents
+ *              on entry do not matter and are undefined after the call
+ *   workspace_bytes  its size
+ *   dtype      ATTN_BF16 or ATTN_F16
+ *
+ * Other arguments and errors as attn_fwd. Two kernels are enqueued on
+ * `stream` (the ranges, then the combine).
+ */
+int attn_fwd_split(const void* q, const void* k, const void* v, void* out,
+                   int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                   float scale, int causal, int dtype, int n_split,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* attn_split_workspace — bytes of workspace attn_fwd_split needs:
+ * n_split * B * Sq * Hq * (D + 2) * 4 (float32 partial outputs, maxima and
+ * weight sums); 0 for n_split <= 1 or an empty problem. */
+size_t attn_split_workspace(int B, int Hq, int Sq, int D, int n_split);
+
+/* attn_split_suggest — a key-range count for attn_fwd_split that fills the
+ * GPU for this shape (1 when attn_fwd alone already does). Arguments as
+ * attn_fwd; returns 1 for shapes attn_fwd would reject. */
+int attn_split_suggest(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal);
 
 /* attn_strerror — a static, human-readable description of a status code. */
 const char* attn_strerror(int status);

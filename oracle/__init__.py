@@ -15,7 +15,10 @@ where n is the codelab step:
 * §3 "Create Q, K, V test arrays": the (B, T, N, H) / (B, S, K, H) layout.
 * §4 "Implement attention from scratch": the unfused reference computation.
 * §7 "Add a causal mask": each position attends only to itself and earlier
-  positions (a lower-triangular mask).
+  positions (a lower-triangular mask); with fewer queries than keys it is
+  applied top-left (query i at position i) or, for the key-value-cache form
+  of the inference use §9 motivates, bottom-right (query i at position
+  Skv - Sq + i).
 * §9 "Compare MHA, GQA and MQA": K/V heads are broadcast over query heads when
   there are fewer of them; GQA with 2 KV heads each serving 4 query heads.
 * §10 "TransformerEngine and FP8": E4M3 (4 exponent, 3 mantissa bits) for the
@@ -27,7 +30,7 @@ Every function is pinned by tests in ``tests/test_oracle.py`` and
 values). No function here is "parity unpinned".
 """
 
-from .attention import attention_weights, sdpa, sdpa_rows, sdpa_one_row, brute_sdpa, kv_head_of
+from .attention import attention_weights, sdpa, sdpa_rows, sdpa_one_row, brute_sdpa, kv_head_of, query_shift
 from .codecs import (
     bf16_bits_to_f64,
     f16_bits_to_f64,
@@ -44,6 +47,7 @@ __all__ = [
     "sdpa_one_row",
     "brute_sdpa",
     "kv_head_of",
+    "query_shift",
     "bf16_bits_to_f64",
     "f16_bits_to_f64",
     "e4m3_bits_to_f64",

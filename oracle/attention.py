@@ -32,7 +32,7 @@ import math
 
 import numpy as np
 
-__all__ = ["kv_head_of", "attention_weights", "sdpa", "sdpa_rows", "sdpa_one_row", "brute_sdpa"]
+__all__ = ["kv_head_of", "query_shift", "attention_weights", "sdpa", "sdpa_rows", "sdpa_one_row", "brute_sdpa"]
 
 
 def kv_head_of(hq, Hq, Hkv):
@@ -63,6 +63,13 @@ def _query_shift(causal, Sq, Skv):
             raise ValueError(f"bottom-right causal alignment needs Sq <= Skv (got {Sq} > {Skv})")
         return Skv - Sq
     raise ValueError(f"unknown causal mode {causal!r}")
+
+
+def query_shift(causal, Sq, Skv):
+    """Public form of the causal reading: None (no mask) or the position of
+    query row 0, for callers that evaluate single rows with
+    :func:`sdpa_one_row`."""
+    return _query_shift(causal, Sq, Skv)
 
 
 def _check_shapes(q, k, v):

@@ -8,6 +8,7 @@ no fallback: if the library is missing or a call is rejected, an exception is
 raised.
 
 The names follow include/attn.h: ``attn_fwd``, ``attn_fwd_fp8``,
+``attn_fwd_split``, ``attn_split_workspace``, ``attn_split_suggest``,
 ``attn_strerror``; :func:`fwd` is the tensor-level convenience wrapper.
 """
 
@@ -25,8 +26,12 @@ DTYPE_CODE = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16, torch.float16:
               torch.float8_e4m3fn: ATTN_FP8_E4M3}
 STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_GROUP",
           -4: "ATTN_ERR_HEAD_DIM", -5: "ATTN_ERR_DTYPE", -6: "ATTN_ERR_ALIGN", -7: "ATTN_ERR_ALIAS",
-          -8: "ATTN_ERR_SCALE", -9: "ATTN_ERR_HIP"}
-EXPORTS = ("attn_fwd", "attn_fwd_fp8", "attn_strerror")
+          -8: "ATTN_ERR_SCALE", -9: "ATTN_ERR_HIP", -10: "ATTN_ERR_CAUSAL", -11: "ATTN_ERR_SPLIT",
+          -12: "ATTN_ERR_WORKSPACE"}
+EXPORTS = ("attn_fwd", "attn_fwd_fp8", "attn_fwd_split", "attn_split_workspace", "attn_split_suggest",
+           "attn_strerror")
+# causal argument: 0 none, 1 lower triangle (top-left), 2 bottom-right (Sq <= Skv)
+CAUSAL_CODE = {False: 0, True: 1, "top_left": 1, "bottom_right": 2, 0: 0, 1: 1, 2: 2}
 
 _lib = None
 
@@ -49,6 +54,12 @@ def lib():
         L.attn_fwd.restype = i
         L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, f, f, f, vp]
         L.attn_fwd_fp8.restype = i
+        L.attn_fwd_split.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, ctypes.c_size_t, vp]
+        L.attn_fwd_split.restype = i
+        L.attn_split_workspace.argtypes = [i, i, i, i, i]
+        L.attn_split_workspace.restype = ctypes.c_size_t
+        L.attn_split_suggest.argtypes = [i, i, i, i, i, i, i]
+        L.attn_split_suggest.restype = i
         L.attn_strerror.argtypes = [i]
         L.attn_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -70,20 +81,41 @@ def attn_fwd_fp8(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, scale, causal, q_descale,
                               float(q_descale), float(k_descale), float(v_descale), stream)
 
 
+def attn_fwd_split(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype, n_split, workspace,
+                   workspace_bytes, stream):
+    """Raw C call of the split-key entry point, returns the status code."""
+    return lib().attn_fwd_split(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, float(scale), int(causal), int(dtype),
+                                int(n_split), workspace, int(workspace_bytes), stream)
+
+
+def attn_split_workspace(B, Hq, Sq, D, n_split):
+    return int(lib().attn_split_workspace(B, Hq, Sq, D, n_split))
+
+
+def attn_split_suggest(B, Hq, Hkv, Sq, Skv, D, causal):
+    return int(lib().attn_split_suggest(B, Hq, Hkv, Sq, Skv, D, int(causal)))
+
+
 def _check(st):
     if st != 0:
         raise AttnError(st, attn_strerror(st))
 
 
-def fwd(q, k, v, *, causal=False, scale=None, out=None, descales=None, stream=None):
+def fwd(q, k, v, *, causal=False, scale=None, out=None, descales=None, stream=None, n_split=None,
+        workspace=None):
     """out = softmax(scale * q k^T [+ causal mask]) v on torch device tensors.
 
     q: (B, Sq, Hq, D), k and v: (B, Skv, Hkv, D), contiguous, same dtype
-    (float32, bfloat16, float16 or float8_e4m3fn) on one GPU. ``scale``
+    (float32, bfloat16, float16 or float8_e4m3fn) on one GPU. ``causal``:
+    False, True (lower triangle, top-left aligned) or "bottom_right" (the
+    queries are the last Sq of Skv positions; needs Sq <= Skv). ``scale``
     defaults to 1 / sqrt(D). E4M3 inputs need ``descales`` = (q, k, v)
-    dequantisation factors and produce a bfloat16 output. The kernel is
-    enqueued on ``stream`` (default: torch's current stream); nothing is
-    synchronised.
+    dequantisation factors and produce a bfloat16 output. ``n_split`` (an
+    int, or "auto" for the library's suggestion) selects the split-key path
+    for bfloat16 / float16, with ``workspace`` a uint8 device tensor of at
+    least attn_split_workspace(...) bytes (allocated here if None). The
+    kernels are enqueued on ``stream`` (default: torch's current stream);
+    nothing is synchronised.
     """
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or t.dim() != 4:
@@ -98,6 +130,9 @@ def fwd(q, k, v, *, causal=False, scale=None, out=None, descales=None, stream=No
         raise ValueError(f"shape mismatch q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
     B, Sq, Hq, D = q.shape
     Skv, Hkv = k.shape[1], k.shape[2]
+    if causal not in CAUSAL_CODE:
+        raise ValueError(f"causal must be one of {sorted(map(str, CAUSAL_CODE))}")
+    causal = CAUSAL_CODE[causal]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     code = DTYPE_CODE[q.dtype]
@@ -108,7 +143,19 @@ def fwd(q, k, v, *, causal=False, scale=None, out=None, descales=None, stream=No
         raise ValueError("out must be a contiguous tensor with q's shape, on q's device, of the output dtype")
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    if code == ATTN_FP8_E4M3:
+    if n_split is not None:
+        if code not in (ATTN_BF16, ATTN_F16):
+            raise ValueError("the split-key path takes bfloat16 or float16 inputs")
+        if n_split == "auto":
+            n_split = attn_split_suggest(B, Hq, Hkv, Sq, Skv, D, causal)
+        need = attn_split_workspace(B, Hq, Sq, D, n_split)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        elif workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != q.device:
+            raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
+        st = attn_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, Sq, Skv, D,
+                            scale, causal, code, n_split, workspace.data_ptr(), workspace.numel(), stream)
+    elif code == ATTN_FP8_E4M3:
         if descales is None:
             raise ValueError("E4M3 inputs need descales=(q_descale, k_descale, v_descale)")
         st = attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, Sq, Skv, D,

@@ -19,6 +19,7 @@ hipError_t launch_fwd_f32(const FwdParams& p, int D, bool causal, hipStream_t st
 hipError_t launch_fwd_fp8(const FwdParams& p, int D, bool causal, int nwaves, hipStream_t stream);
 hipError_t launch_fwd_rb2(const FwdParams& p, int D, int dtype, bool causal, hipStream_t stream);
 hipError_t launch_fwd_pp(const FwdParams& p, int D, int dtype, bool causal, hipStream_t stream);
+hipError_t launch_combine(const FwdParams& p, int D, bool is_bf16, hipStream_t stream);
 }
 
 namespace {
@@ -34,7 +35,7 @@ bool ranges_overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 // Shared validation of both entry points. Returns ATTN_OK or an error code;
 // sets *noop when the call has nothing to compute.
 int validate(const void* q, const void* k, const void* v, const void* out,
-             int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
+             int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale, int causal,
              int in_bytes, int out_bytes, bool* noop) {
     *noop = false;
     if (!q || !k || !v || !out) return ATTN_ERR_NULL;
@@ -42,8 +43,10 @@ int validate(const void* q, const void* k, const void* v, const void* out,
     if (Hq % Hkv != 0) return ATTN_ERR_GROUP;
     if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
     if (!isfinite(scale)) return ATTN_ERR_SCALE;
+    if (causal < 0 || causal > 2) return ATTN_ERR_CAUSAL;
     if ((int64_t)B * Sq == 0) { *noop = true; return ATTN_OK; }
     if (Skv < 1) return ATTN_ERR_SHAPE;
+    if (causal == 2 && Sq > Skv) return ATTN_ERR_CAUSAL;
     const int64_t nq = (int64_t)B * Sq * Hq * D;
     const int64_t nk = (int64_t)B * Skv * Hkv * D;
     if (nq >= kMaxElems || nk >= kMaxElems) return ATTN_ERR_SHAPE;
@@ -57,8 +60,13 @@ int validate(const void* q, const void* k, const void* v, const void* out,
 
 attn::FwdParams make_params(const void* q, const void* k, const void* v, void* out,
                             int B, int Hq, int Hkv, int Sq, int Skv, float scale_log2, float out_mul,
-                            bool mfma, int rows_per_wave, int waves) {
+                            int causal, bool mfma, int rows_per_wave, int waves) {
     attn::FwdParams p;
+    // Bottom-right alignment shifts every query to position Skv - Sq + i.
+    p.causal_off = causal == 2 ? Skv - Sq : 0;
+    p.n_split = 1;
+    p.part_o = nullptr;
+    p.part_ml = nullptr;
     p.q = q; p.k = k; p.v = v; p.out = out;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Sq = Sq; p.Skv = Skv;
     p.G = Hq / Hkv;
@@ -103,20 +111,30 @@ MfmaKernel mfma_kernel() {
 
 hipError_t launch_mfma(const void* q, const void* k, const void* v, void* out,
                        int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale_log2,
-                       float out_mul, int dtype, bool causal, hipStream_t stream) {
+                       float out_mul, int dtype, int causal, hipStream_t stream) {
     const MfmaKernel kern = mfma_kernel();
     const int rpw = kern == kRows64 ? 64 : 32;
     const int waves = (kern == kPingPong || kern == kEightWave) ? 8 : 4;
     const attn::FwdParams p = make_params(q, k, v, out, B, Hq, Hkv, Sq, Skv, scale_log2, out_mul,
-                                          true, rpw, waves);
+                                          causal, true, rpw, waves);
+    const bool masked = causal != 0;
     switch (kern) {
-        case kRows64: return attn::launch_fwd_rb2(p, D, dtype, causal, stream);
+        case kRows64: return attn::launch_fwd_rb2(p, D, dtype, masked, stream);
         case kFourWave:
         case kEightWave:
-            return dtype == ATTN_FP8_E4M3 ? attn::launch_fwd_fp8(p, D, causal, waves, stream)
-                                          : attn::launch_fwd_mfma(p, D, dtype == ATTN_BF16, causal, waves, stream);
-        default: return attn::launch_fwd_pp(p, D, dtype, causal, stream);
+            return dtype == ATTN_FP8_E4M3 ? attn::launch_fwd_fp8(p, D, masked, waves, stream)
+                                          : attn::launch_fwd_mfma(p, D, dtype == ATTN_BF16, masked, waves, stream);
+        default: return attn::launch_fwd_pp(p, D, dtype, masked, stream);
     }
+}
+
+// Workgroups of the four-wave kernel for a shape (the unit of the split
+// heuristic), and the key tiles a row block sees at most.
+int64_t base_grid(int B, int Hq, int Hkv, int Sq) {
+    const int G = Hq / Hkv;
+    const int gpack = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+    const int rows_per_wg = 32 * (4 / gpack);
+    return (int64_t)B * Hkv * (G / gpack) * ((Sq + rows_per_wg - 1) / rows_per_wg);
 }
 
 }  // namespace
@@ -131,16 +149,16 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out,
         default: return ATTN_ERR_DTYPE;   // includes ATTN_FP8_E4M3: use attn_fwd_fp8
     }
     bool noop;
-    const int st = validate(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, scale, eb, eb, &noop);
+    const int st = validate(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, scale, causal, eb, eb, &noop);
     if (st != ATTN_OK || noop) return st;
     hipError_t e;
     if (dtype == ATTN_F32) {
         const attn::FwdParams p = make_params(q, k, v, out, B, Hq, Hkv, Sq, Skv,
-                                              nonzero_multiplier(scale * kLog2e), 1.0f, false, 32, 4);
+                                              nonzero_multiplier(scale * kLog2e), 1.0f, causal, false, 32, 4);
         e = attn::launch_fwd_f32(p, D, causal != 0, stream);
     } else {
         e = launch_mfma(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, nonzero_multiplier(scale * kLog2e), 1.0f,
-                        dtype, causal != 0, stream);
+                        dtype, causal, stream);
     }
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
@@ -151,14 +169,61 @@ extern "C" int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o
                             float q_descale, float k_descale, float v_descale,
                             hipStream_t stream) {
     bool noop;
-    const int st = validate(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, scale, 1, 2, &noop);
+    const int st = validate(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, scale, causal, 1, 2, &noop);
     if (st != ATTN_OK) return st;
     if (!isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale)) return ATTN_ERR_SCALE;
     if (noop) return ATTN_OK;
     const float sl2 = scale * q_descale * k_descale * kLog2e;
     if (!isfinite(sl2)) return ATTN_ERR_SCALE;
     const hipError_t e = launch_mfma(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, nonzero_multiplier(sl2), v_descale,
-                                     ATTN_FP8_E4M3, causal != 0, stream);
+                                     ATTN_FP8_E4M3, causal, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+extern "C" size_t attn_split_workspace(int B, int Hq, int Sq, int D, int n_split) {
+    if (n_split <= 1 || B <= 0 || Hq <= 0 || Sq <= 0 || D <= 0) return 0;
+    return (size_t)n_split * B * Sq * Hq * (size_t)(D + 2) * sizeof(float);
+}
+
+extern "C" int attn_split_suggest(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Skv <= 0 || Hq % Hkv != 0 || (D != 64 && D != 128))
+        return 1;
+    // Aim at 1024 workgroups (four per CU, two resident at a time), with at
+    // least four 64-key tiles per range.
+    const int64_t base = base_grid(B, Hq, Hkv, Sq);
+    const int64_t tiles = (Skv + 63) / 64;
+    int64_t n = (1024 + base - 1) / base;
+    n = n < tiles / 4 ? n : tiles / 4;
+    if (causal == 1) n = n < (Sq + 63) / 64 / 4 ? n : (Sq + 63) / 64 / 4;   // keys beyond the rows are never read
+    if (n < 1) n = 1;
+    return (int)(n > ATTN_MAX_SPLIT ? ATTN_MAX_SPLIT : n);
+}
+
+extern "C" int attn_fwd_split(const void* q, const void* k, const void* v, void* out,
+                              int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                              float scale, int causal, int dtype, int n_split,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_DTYPE;
+    bool noop;
+    const int st = validate(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, scale, causal, 2, 2, &noop);
+    if (st != ATTN_OK) return st;
+    if (n_split < 1 || n_split > ATTN_MAX_SPLIT) return ATTN_ERR_SPLIT;
+    if (noop) return ATTN_OK;
+    if (n_split == 1) return attn_fwd(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype, stream);
+    const size_t need = attn_split_workspace(B, Hq, Sq, D, n_split);
+    if (!workspace || ((uintptr_t)workspace & 15) || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    const int64_t nq = (int64_t)B * Sq * Hq * D, nk = (int64_t)B * Skv * Hkv * D;
+    if (ranges_overlap(workspace, (int64_t)need, q, nq * 2) || ranges_overlap(workspace, (int64_t)need, k, nk * 2) ||
+        ranges_overlap(workspace, (int64_t)need, v, nk * 2) || ranges_overlap(workspace, (int64_t)need, out, nq * 2))
+        return ATTN_ERR_WORKSPACE;
+    // The split path always runs the four-wave kernel.
+    attn::FwdParams p = make_params(q, k, v, out, B, Hq, Hkv, Sq, Skv, nonzero_multiplier(scale * kLog2e), 1.0f,
+                                    causal, true, 32, 4);
+    p.n_split = n_split;
+    p.part_o = (float*)workspace;
+    p.part_ml = (float*)workspace + (size_t)n_split * B * Sq * Hq * D;
+    hipError_t e = attn::launch_fwd_mfma(p, D, dtype == ATTN_BF16, causal != 0, 4, stream);
+    if (e == hipSuccess) e = attn::launch_combine(p, D, dtype == ATTN_BF16, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -174,6 +239,9 @@ extern "C" const char* attn_strerror(int status) {
         case ATTN_ERR_ALIAS: return "out overlaps an input";
         case ATTN_ERR_SCALE: return "scale or a descale is not finite";
         case ATTN_ERR_HIP: return "HIP kernel launch failed";
+        case ATTN_ERR_CAUSAL: return "causal must be 0, 1 or 2 (2, bottom-right alignment, needs Sq <= Skv)";
+        case ATTN_ERR_SPLIT: return "n_split must be between 1 and ATTN_MAX_SPLIT";
+        case ATTN_ERR_WORKSPACE: return "workspace is NULL, not 16-byte aligned, smaller than attn_split_workspace(), or overlaps an input or the output";
         default: return "unknown status";
     }
 }

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
     float m_run = -INFINITY, l_run = 0.f;
 
     int kend = Skv;
-    if (CAUSAL) kend = min(Skv, min(rb * RPW + RPW, Sq));   // keys 0 .. last row
+    if (CAUSAL) kend = min(Skv, min(rb * RPW + RPW, Sq) + p.causal_off);   // keys 0 .. last visible
     for (int k0 = 0; k0 < kend; k0 += BK) {
         __syncthreads();
         for (int e = tid; e < BK * D / 4; e += 256) {
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
             for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
             float x = acc * p.scale_log2;
             const int key = k0 + j;
-            if (key >= Skv || (CAUSAL && key > row)) x = -INFINITY;
+            if (key >= Skv || (CAUSAL && key > row + p.causal_off)) x = -INFINITY;
             s[j] = x;
             mt = fmaxf(mt, x);
         }

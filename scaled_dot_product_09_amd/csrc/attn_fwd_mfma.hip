@@ -78,13 +78,14 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
     const WorkItem wi = map_workgroup(p, CAUSAL);
     const int hq = wi.hq0 + (wave % p.gpack);
     const int q0 = wi.row_base + (wave / p.gpack) * 32;
-    const int Sq = p.Sq, Skv = p.Skv;
+    const int Sq = p.Sq;
+    int Skv = p.Skv;                                   // keys of this workgroup's range, from its start
     const size_t qstride = (size_t)p.Hq * D;          // elements between query rows
     const size_t kstride = (size_t)p.Hkv * D;
 
     const T* qbase = (const T*)p.q + ((size_t)wi.b * Sq * p.Hq + hq) * D;
-    const uint8_t* kbase = (const uint8_t*)((const T*)p.k + ((size_t)wi.b * Skv * p.Hkv + wi.hkv) * D);
-    const uint8_t* vbase = (const uint8_t*)((const T*)p.v + ((size_t)wi.b * Skv * p.Hkv + wi.hkv) * D);
+    const uint8_t* kbase = (const uint8_t*)((const T*)p.k + ((size_t)wi.b * p.Skv * p.Hkv + wi.hkv) * D);
+    const uint8_t* vbase = (const uint8_t*)((const T*)p.v + ((size_t)wi.b * p.Skv * p.Hkv + wi.hkv) * D);
     const size_t kstride_b = kstride * Tr::IN_BYTES;
 
     // Q^T operand, kept in registers for the whole key loop: lane (h, n) holds
@@ -116,10 +117,38 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
 
     int n_tiles = (Skv + BN - 1) / BN;
     if (CAUSAL) {
-        const int last_row = min(wi.row_base + p.rows_per_wg, Sq) - 1;
+        const int last_row = min(wi.row_base + p.rows_per_wg, Sq) - 1 + p.causal_off;
         n_tiles = min(n_tiles, last_row / BN + 1);
     }
     n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
+
+    // Split keys (n_split > 1): this workgroup takes tiles [tb, te) of the
+    // n_tiles it would otherwise loop over, and writes an unnormalised partial
+    // result for a separate combine step. The key range is made to start at
+    // 0: the K/V bases move to key tb * BN, and the key count and the causal
+    // offset move with them.
+    int coff = p.causal_off;
+    const size_t qrow_idx = ((size_t)wi.split * p.B + wi.b) * Sq;   // partial-buffer row base
+    if (p.n_split > 1) {
+        const int tb = wi.split * n_tiles / p.n_split;
+        const int te = (wi.split + 1) * n_tiles / p.n_split;
+        n_tiles = te - tb;
+        kbase += (size_t)tb * BN * kstride_b;
+        vbase += (size_t)tb * BN * kstride_b;
+        Skv -= tb * BN;
+        coff -= tb * BN;
+        if (n_tiles == 0) {   // no keys in range: weight sum 0, max -inf, output 0
+            const int row = q0 + n;
+            if (row < Sq) {
+                const size_t r = (qrow_idx + row) * p.Hq + hq;
+                for (int db = 0; db < NDB; ++db)
+                    for (int jj = 0; jj < 4; ++jj)
+                        *(f32x4*)(p.part_o + r * D + db * 32 + 8 * jj + 4 * h) = (f32x4){0.f, 0.f, 0.f, 0.f};
+                if (h == 0) *(f32x2*)(p.part_ml + r * 2) = (f32x2){-INFINITY, 0.f};
+            }
+            return;
+        }
+    }
 
     // ---- tile staging ------------------------------------------------------
     // LDS: two K tiles and two V tiles. The loop below is software-pipelined
@@ -186,7 +215,6 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
 
     const float c_log2 = fabsf(p.scale_log2);   // > 0: the host never passes 0
     const int qrow = q0 + n;
-    const int wave_last_row = q0 + 31;
 
     // Per-lane constants of the V transpose read (see load_v).
     const int L16 = lane & 15;                 // lane inside its 16-lane group
@@ -263,7 +291,7 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
         for (int kb = 0; kb < NKB; ++kb) {
             const int kbase_h = j * BN + kb * 32 + 4 * h;       // key of element i: kbase_h + koff(i)
             int lim = Skv - 1 - kbase_h;                         // last existing key offset
-            if (CAUSAL) lim = min(lim, qrow - kbase_h);          // last visible key offset
+            if (CAUSAL) lim = min(lim, qrow + coff - kbase_h);   // last visible key offset
             if (__builtin_amdgcn_ballot_w64(lim < 27) != 0) {   // 27 = largest koff(i)
                 for (int i = 0; i < 16; ++i)
                     s[kb][i] = (8 * (i >> 2) + (i & 3) > lim) ? masked : s[kb][i];
@@ -438,6 +466,18 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
 
     // ---- epilogue: O = O^T / l, round once, store [b][row][hq][d] ----------
     const float l = xor32_sum(l_part);
+    if (p.n_split > 1) {
+        // Partial result of this key range: O and l relative to 2^m_run.
+        if (qrow < Sq) {
+            const size_t r = (qrow_idx + qrow) * p.Hq + hq;
+            for (int db = 0; db < NDB; ++db)
+                for (int jj = 0; jj < 4; ++jj)
+                    *(f32x4*)(p.part_o + r * D + db * 32 + 8 * jj + 4 * h) =
+                        (f32x4){oacc[db][4 * jj], oacc[db][4 * jj + 1], oacc[db][4 * jj + 2], oacc[db][4 * jj + 3]};
+            if (h == 0) *(f32x2*)(p.part_ml + r * 2) = (f32x2){m_run, l};
+        }
+        return;
+    }
     const float inv = p.out_mul / l;
     if (qrow < Sq) {
         out_t* orow = (out_t*)p.out + ((size_t)wi.b * Sq + qrow) * qstride + (size_t)hq * D;
@@ -454,7 +494,7 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
 
 template <typename T, int D, int BN>
 static hipError_t launch_typed(const FwdParams& p, bool causal, int nwaves, hipStream_t stream) {
-    const dim3 grid(p.n_units * p.n_row_blocks), block(64 * nwaves);
+    const dim3 grid(p.n_units * p.n_row_blocks * p.n_split), block(64 * nwaves);
     if (nwaves == 8) {
         if (causal)
             hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, true, 8>), grid, block, 0, stream, p);

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256, 1) void fwd_rb2_kernel(FwdParams p) {
 
     int n_tiles = (Skv + BN - 1) / BN;
     if (CAUSAL) {
-        const int last_row = min(wi.row_base + p.rows_per_wg, Sq) - 1;
+        const int last_row = min(wi.row_base + p.rows_per_wg, Sq) - 1 + p.causal_off;
         n_tiles = min(n_tiles, last_row / BN + 1);
     }
     n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256, 1) void fwd_rb2_kernel(FwdParams p) {
         for (int kb = 0; kb < NKB; ++kb) {
             const int kbase_h = j * BN + kb * 32 + 4 * h;
             int lim = Skv - 1 - kbase_h;
-            if (CAUSAL) lim = min(lim, qrow - kbase_h);
+            if (CAUSAL) lim = min(lim, qrow + p.causal_off - kbase_h);
             if (__builtin_amdgcn_ballot_w64(lim < 27) != 0) {
                 for (int i = 0; i < 16; ++i)
                     s[kb][i] = (8 * (i >> 2) + (i & 3) > lim) ? masked : s[kb][i];

@@ -131,7 +131,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
 
     int n_tiles = (Skv + BN - 1) / BN;
     if (CAUSAL) {
-        const int last_row = min(wi.row_base + p.rows_per_wg, Sq) - 1;
+        const int last_row = min(wi.row_base + p.rows_per_wg, Sq) - 1 + p.causal_off;
         n_tiles = min(n_tiles, last_row / BN + 1);
     }
     n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
         for (int kb = 0; kb < NKB; ++kb) {
             const int kbase_h = t * BN + kb * 32 + 4 * h;       // key of element i: kbase_h + koff(i)
             int lim = Skv - 1 - kbase_h;                         // last existing key offset
-            if (CAUSAL) lim = min(lim, qrow - kbase_h);          // last visible key offset
+            if (CAUSAL) lim = min(lim, qrow + p.causal_off - kbase_h);          // last visible key offset
             if (__builtin_amdgcn_ballot_w64(lim < 27) != 0) {   // 27 = largest koff(i)
 #pragma unroll
                 for (int i = 0; i < 16; ++i)

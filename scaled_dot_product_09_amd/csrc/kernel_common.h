@@ -33,32 +33,40 @@ struct FwdParams {
     int xcd_remap;      // 1 when n_units % 8 == 0 (see map_workgroup)
     float scale_log2;   // softmax scale * log2(e) (FP8: times q and k descales)
     float out_mul;      // factor applied to the normalised output (FP8: v descale)
+    int causal_off;     // causal: key j is visible to query row i iff j <= i + causal_off
+    int n_split;        // key ranges per (unit, row block); 1 = no split
+    float* part_o;      // n_split > 1: unnormalised partial outputs [n_split][B][Sq][Hq][D]
+    float* part_ml;     // n_split > 1: (running max, weight sum) pairs [n_split][B][Sq][Hq][2]
 };
 
 struct WorkItem {
     int b, hkv, hq0;    // batch, KV head, first query head of the workgroup
     int row_base;       // first query row of the workgroup
+    int split;          // which of the n_split key ranges
 };
 
-// Workgroup -> (unit, row block). The hardware hands workgroup i to XCD i % 8
-// (MI355X has 8 XCDs, each with its own L2). When the units split evenly over
-// the XCDs, XCD x gets a contiguous range of units, so every workgroup that
-// reads a given KV head runs on the same XCD and shares its L2. Within an
-// XCD, row blocks go out in order of decreasing causal work (the last row
-// block first) so the short ones fill the tail of the launch.
+// Workgroup -> (unit, row block, key range). The hardware hands workgroup i
+// to XCD i % 8 (MI355X has 8 XCDs, each with its own L2). When the units
+// split evenly over the XCDs, XCD x gets a contiguous range of units, so
+// every workgroup that reads a given KV head runs on the same XCD and shares
+// its L2. Within an XCD, row blocks go out in order of decreasing causal work
+// (the last row block first) so the short ones fill the tail of the launch;
+// the key ranges of one row block are neighbours.
 __device__ inline WorkItem map_workgroup(const FwdParams& p, bool causal) {
     const int pid = (int)__builtin_amdgcn_workgroup_id_x();
-    int rb_rank, unit;
+    int rank, unit;
     if (p.xcd_remap) {
         const int per = p.n_units >> 3;
         const int xcd = pid & 7;
         const int slot = pid >> 3;
-        rb_rank = slot / per;
-        unit = xcd * per + (slot - rb_rank * per);
+        rank = slot / per;
+        unit = xcd * per + (slot - rank * per);
     } else {
-        rb_rank = pid / p.n_units;
-        unit = pid - rb_rank * p.n_units;
+        rank = pid / p.n_units;
+        unit = pid - rank * p.n_units;
     }
+    const int rb_rank = rank / p.n_split;
+    const int split = rank - rb_rank * p.n_split;
     const int rb = causal ? (p.n_row_blocks - 1 - rb_rank) : rb_rank;
     const int groups = p.G / p.gpack;
     const int hgrp = unit % groups;
@@ -68,6 +76,7 @@ __device__ inline WorkItem map_workgroup(const FwdParams& p, bool causal) {
     w.b = t / p.Hkv;
     w.hq0 = w.hkv * p.G + hgrp * p.gpack;
     w.row_base = rb * p.rows_per_wg;
+    w.split = split;
     return w;
 }
 

@@ -44,9 +44,10 @@ class Workload:
     Sq: int
     Skv: int
     D: int
-    causal: bool
+    causal: object          # False, True (top-left lower triangle) or "bottom_right"
     seed: int
     note: str = field(default="", compare=False)
+    n_split: object = None  # None: attn_fwd; "auto" or an int: the split-key entry point
 
     @property
     def scale(self):
@@ -79,6 +80,13 @@ WORKLOADS = {w.name: w for w in [
     _mqa_batch(1), _mqa_batch(8), _mqa_batch(32),
     Workload("e4m3_mha_b4_h16_s4096_d128_causal", "e4m3", 4, 16, 16, 4096, 4096, 128, True, 9000,
              "FP8 E4M3 inputs, bf16 output; seed 9000 as the codelab's FP8 cell (§10)"),
+    # Key-value-cache (decode) form of the GQA / MQA inference use of §9: a few
+    # new queries at the end of a long cached sequence, bottom-right causal,
+    # keys split over workgroups. Seeds: Skv + B.
+    Workload("bf16_gqa_decode_b8_hq32_hkv8_sq1_skv16384", "bf16", 8, 32, 8, 1, 16384, 128, "bottom_right",
+             16384 + 8, "decode: one new token per sequence, 16384-token cache, GQA", n_split="auto"),
+    Workload("bf16_mqa_decode_b32_hq32_hkv1_sq4_skv8192", "bf16", 32, 32, 1, 4, 8192, 128, "bottom_right",
+             8192 + 32, "decode: four new tokens per sequence, 8192-token cache, MQA", n_split="auto"),
 ]}
 
 HEADLINE = "bf16_gqa_b2_hq32_hkv8_s4096_d128_causal"
@@ -128,7 +136,13 @@ def make_inputs(w, *, seed=None, shapes=None):
 
 def metric_flops(B, Hq, Sq, Skv, D, causal):
     """Attention forward FLOPs as the metric counts them: 4 B Hq Sq Skv D,
-    halved for a causal mask (QK^T and PV, 2 flops per multiply-add)."""
+    halved for a (top-left) causal mask (QK^T and PV, 2 flops per
+    multiply-add). For bottom-right alignment, whose queries see nearly every
+    key when Sq << Skv, the visible (query, key) pairs are counted exactly:
+    Sq (Skv - Sq) + Sq (Sq + 1) / 2 per head."""
+    if causal == "bottom_right":
+        pairs = Sq * (Skv - Sq) + Sq * (Sq + 1) / 2
+        return 4.0 * B * Hq * D * pairs
     f = 4.0 * B * Hq * Sq * Skv * D
     return f / 2 if causal else f
 

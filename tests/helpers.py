@@ -41,14 +41,14 @@ def out_to_f64(t):
     raise ValueError(t.dtype)
 
 
-def gpu_run(w, q, k, v, desc, *, scale=None, causal=None, out=None):
+def gpu_run(w, q, k, v, desc, *, scale=None, causal=None, out=None, n_split=None, workspace=None):
     """Run the HIP library on CPU input tensors; returns the output tensor on the GPU."""
     dev = torch.device("cuda:0")
     qd, kd, vd = (x.to(dev) for x in (q, k, v))
     scale = w.scale if scale is None else scale
     causal = w.causal if causal is None else causal
     o = attn.fwd(qd, kd, vd, causal=causal, scale=scale, out=out,
-                 descales=desc if w.dtype == "e4m3" else None)
+                 descales=desc if w.dtype == "e4m3" else None, n_split=n_split, workspace=workspace)
     torch.cuda.synchronize()
     return o
 
@@ -64,14 +64,15 @@ def oracle_rows(w, q, k, v, desc, rows, *, scale=None, causal=None):
     """Oracle output vectors for sampled (b, i, hq) rows, decoding only what they need."""
     scale = w.scale if scale is None else scale
     causal = w.causal if causal is None else causal
-    Hq, Hkv = q.shape[2], k.shape[2]
+    Sq, Hq, Skv, Hkv = q.shape[1], q.shape[2], k.shape[1], k.shape[2]
+    shift = oracle.query_shift(causal, Sq, Skv)
     res = []
     for (b, i, hq) in rows:
         g = oracle.kv_head_of(hq, Hq, Hkv)
         res.append(oracle.sdpa_one_row(to_f64(q[b, i, hq], w.dtype, desc[0]),
                                        to_f64(k[b, :, g], w.dtype, desc[1]),
                                        to_f64(v[b, :, g], w.dtype, desc[2]),
-                                       i=i, scale=scale, causal=causal))
+                                       i=(shift or 0) + i, scale=scale, causal=shift is not None))
     return np.stack(res)
 
 

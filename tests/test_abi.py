@@ -62,6 +62,7 @@ def call_fp8(q=Q, k=K, v=V, o=O, B=2, Hq=8, Hkv=2, Sq=64, Skv=64, D=128, scale=0
     (dict(o=Q), -7), (dict(o=K + 16), -7), (dict(o=V - 16), -7),
     (dict(scale=float("nan")), -8), (dict(scale=float("inf")), -8),
     (dict(B=1 << 20, Sq=1 << 20), -2),
+    (dict(causal=3), -10), (dict(causal=-1), -10), (dict(causal=2, Sq=65, Skv=64), -10),
 ])
 def test_rejected_before_launch(kw, status):
     assert call(**kw) == status
@@ -76,6 +77,42 @@ def test_fp8_rejected_before_launch(kw, status):
     assert call_fp8(**kw) == status
 
 
+W = 0x800000   # fake 16-byte aligned workspace, far from the tensors
+
+
+def call_split(q=Q, k=K, v=V, o=O, B=2, Hq=8, Hkv=2, Sq=64, Skv=64, D=128, scale=0.125, causal=1,
+               dtype=attn.ATTN_BF16, n_split=4, ws=W, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = attn.attn_split_workspace(B, Hq, Sq, D, n_split)
+    return attn.attn_fwd_split(q, k, v, o, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype, n_split, ws, ws_bytes,
+                               None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), -1), (dict(D=80), -4), (dict(Hq=3, Hkv=2), -3), (dict(o=Q), -7), (dict(causal=5), -10),
+    (dict(dtype=attn.ATTN_F32), -5), (dict(dtype=attn.ATTN_FP8_E4M3), -5),
+    (dict(n_split=0), -11), (dict(n_split=257), -11), (dict(n_split=-3), -11),
+    (dict(ws=0), -12), (dict(ws=W + 8), -12), (dict(ws_bytes=1000), -12),
+    (dict(ws=Q), -12), (dict(ws=O - 64), -12), (dict(ws=K + 1024), -12),
+])
+def test_split_rejected_before_launch(kw, status):
+    assert call_split(**kw) == status
+
+
+def test_split_workspace_size_and_suggestion():
+    # n_split * B * Sq * Hq * (D + 2) float32 values.
+    assert attn.attn_split_workspace(2, 8, 64, 128, 4) == 4 * 2 * 64 * 8 * 130 * 4
+    assert attn.attn_split_workspace(2, 8, 64, 128, 1) == 0
+    assert attn.attn_split_workspace(0, 8, 64, 128, 4) == 0
+    # Decode (one query, long cache) splits; a large causal prefill does not.
+    assert attn.attn_split_suggest(8, 32, 8, 1, 16384, 128, 0) > 1
+    assert attn.attn_split_suggest(2, 32, 8, 4096, 4096, 128, 1) == 1
+    assert attn.attn_split_suggest(1, 32, 8, 1, 64, 128, 2) == 1      # too few keys to split
+    for args in [(1, 32, 1, 1, 1 << 17, 128, 2), (64, 64, 8, 1, 4096, 64, 0)]:
+        assert 1 <= attn.attn_split_suggest(*args) <= 256
+    assert attn.attn_split_suggest(1, 3, 2, 1, 100, 128, 0) == 1     # invalid shape
+
+
 def test_empty_problem_is_a_noop():
     # B * Sq == 0 returns success without any HIP call, whatever the other sizes.
     assert call(B=0) == 0
@@ -83,6 +120,8 @@ def test_empty_problem_is_a_noop():
     assert call(Sq=0, Skv=0) == 0
     assert call(B=0, dtype=attn.ATTN_F32) == 0
     assert call_fp8(Sq=0) == 0
+    assert call_split(Sq=0, ws=0) == 0
+    assert call_split(n_split=1, B=0, ws=0) == 0
 
 
 def test_python_wrapper_rejects_host_tensors():

@@ -1,0 +1,139 @@
+"""GPU parity of the key-value-cache (decode) form: bottom-right causal
+alignment and the split-key entry point, against the fp64 oracle.
+
+Bottom-right alignment puts the Sq queries at positions Skv - Sq .. Skv - 1
+(the reading of the codelab's §7 mask for the §9 inference use; the oracle's
+pins tie it to full causal self-attention). The split-key path cuts every
+row's keys into n_split ranges and combines the partial softmax sums; its
+result must match the oracle exactly as the single-pass kernel does, for any
+n_split, including ranges that hold no visible key of a row.
+
+Bounds (max-abs against the oracle on the decoded inputs): 1e-5 fp32,
+2e-2 bf16 / f16, 6e-2 E4M3.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from scaled_dot_product_09_amd import attn, workload
+from scaled_dot_product_09_amd.workload import Workload
+from tests import helpers
+from tests.helpers import TOL
+
+pytestmark = pytest.mark.gpu
+
+
+def W(dtype, B, Hq, Hkv, Sq, Skv, D, causal, seed=11):
+    tag = {False: "", True: "_causal", "bottom_right": "_br"}[causal]
+    return Workload(f"{dtype}_b{B}_hq{Hq}_hkv{Hkv}_sq{Sq}_skv{Skv}_d{D}{tag}", dtype, B, Hq, Hkv, Sq, Skv, D,
+                    causal, seed)
+
+
+@pytest.fixture(params=["w4", "w8", "pp", "rb2"])
+def kernel(request, monkeypatch):
+    """Every matrix-core kernel applies the bottom-right mask."""
+    monkeypatch.setenv("ATTN_KERNEL", request.param)
+    return request.param
+
+
+BOTTOM_RIGHT = [
+    W("bf16", 2, 8, 2, 1, 1000, 128, "bottom_right"),
+    W("bf16", 1, 4, 4, 7, 300, 64, "bottom_right"),
+    W("bf16", 1, 8, 1, 64, 1024, 128, "bottom_right"),
+    W("bf16", 1, 4, 2, 130, 131, 128, "bottom_right"),
+    W("bf16", 2, 4, 2, 200, 200, 64, "bottom_right"),        # Sq == Skv: the ordinary mask
+    W("f16", 1, 8, 2, 33, 777, 128, "bottom_right"),
+    W("e4m3", 1, 8, 2, 5, 500, 128, "bottom_right"),
+    W("e4m3", 1, 4, 4, 70, 200, 64, "bottom_right"),
+]
+
+
+@pytest.mark.parametrize("w", BOTTOM_RIGHT, ids=lambda w: w.name)
+def test_bottom_right_parity(w, kernel):
+    print(f"case {w.name} kernel {kernel}", flush=True)
+    q, k, v, desc = workload.make_inputs(w)
+    got = helpers.out_to_f64(helpers.gpu_run(w, q, k, v, desc))
+    want = helpers.oracle_full(w, q, k, v, desc)
+    err = helpers.max_abs_err(got, want)
+    print(f"  max-abs {err:.3e}", flush=True)
+    assert err <= TOL[w.dtype], err
+
+
+def test_bottom_right_f32():
+    for w in (W("f32", 1, 4, 2, 3, 200, 64, "bottom_right"), W("f32", 1, 2, 1, 40, 77, 128, "bottom_right")):
+        q, k, v, desc = workload.make_inputs(w)
+        got = helpers.out_to_f64(helpers.gpu_run(w, q, k, v, desc))
+        assert helpers.max_abs_err(got, helpers.oracle_full(w, q, k, v, desc)) <= TOL["f32"]
+
+
+def test_bottom_right_is_suffix_of_causal():
+    """The last Sq rows of causal self-attention over Skv tokens equal the
+    bottom-right call with those Sq queries (same GPU kernel, same inputs)."""
+    w = W("bf16", 1, 8, 2, 512, 512, 128, True)
+    q, k, v, desc = workload.make_inputs(w)
+    full = helpers.gpu_run(w, q, k, v, desc)
+    for Sq in (1, 32, 100):
+        tail = helpers.gpu_run(w, q[:, 512 - Sq:].contiguous(), k, v, desc, causal="bottom_right")
+        # Different row positions inside the workgroup tile, same arithmetic per row.
+        assert torch.equal(tail, full[:, 512 - Sq:])
+
+
+SPLIT = [
+    (W("bf16", 2, 8, 2, 1, 1000, 128, "bottom_right"), (2, 3, 8, 16)),
+    (W("bf16", 1, 32, 8, 4, 2049, 128, "bottom_right"), (5, 32)),
+    (W("bf16", 1, 4, 4, 100, 700, 64, False), (2, 7)),
+    (W("bf16", 1, 8, 2, 300, 300, 128, True), (2, 4, 9)),       # top-left: upper rows see few keys
+    (W("bf16", 1, 4, 1, 64, 640, 128, "bottom_right"), (10, 40)),  # more ranges than some rows have tiles
+    (W("f16", 2, 8, 1, 3, 333, 64, "bottom_right"), (3, 6)),
+]
+
+
+@pytest.mark.parametrize("w,splits", SPLIT, ids=lambda x: x.name if isinstance(x, Workload) else str(x))
+def test_split_parity(w, splits):
+    q, k, v, desc = workload.make_inputs(w)
+    want = helpers.oracle_full(w, q, k, v, desc)
+    for n in splits:
+        print(f"case {w.name} n_split {n}", flush=True)
+        got = helpers.out_to_f64(helpers.gpu_run(w, q, k, v, desc, n_split=n))
+        err = helpers.max_abs_err(got, want)
+        print(f"  max-abs {err:.3e}", flush=True)
+        assert err <= TOL[w.dtype], (n, err)
+
+
+def test_split_ignores_workspace_contents_and_is_deterministic():
+    w = W("bf16", 2, 16, 4, 2, 1500, 128, "bottom_right")
+    q, k, v, desc = workload.make_inputs(w)
+    n = 6
+    need = attn.attn_split_workspace(w.B, w.Hq, w.Sq, w.D, n)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda:0")   # NaN float32 everywhere
+    a = helpers.gpu_run(w, q, k, v, desc, n_split=n, workspace=ws)
+    ws.fill_(0)
+    b = helpers.gpu_run(w, q, k, v, desc, n_split=n, workspace=ws)
+    assert torch.equal(a, b)
+    assert not torch.isnan(a).any()
+    err = helpers.max_abs_err(helpers.out_to_f64(a), helpers.oracle_full(w, q, k, v, desc))
+    assert err <= TOL["bf16"], err
+
+
+def test_split_one_equals_attn_fwd():
+    w = W("bf16", 1, 8, 2, 40, 900, 128, "bottom_right")
+    q, k, v, desc = workload.make_inputs(w)
+    a = helpers.gpu_run(w, q, k, v, desc)
+    b = helpers.gpu_run(w, q, k, v, desc, n_split=1)
+    assert torch.equal(a, b)
+
+
+def test_split_auto_on_decode_shape():
+    w = workload.WORKLOADS["bf16_gqa_decode_b8_hq32_hkv8_sq1_skv16384"]
+    n = attn.attn_split_suggest(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D, 2)
+    assert n > 1
+    q, k, v, desc = workload.make_inputs(w)
+    o = helpers.gpu_run(w, q, k, v, desc, n_split="auto")
+    rng = np.random.default_rng(5)
+    rows = sorted({(int(rng.integers(w.B)), 0, int(rng.integers(w.Hq))) for _ in range(24)})
+    idx = torch.tensor(rows)
+    got = helpers.out_to_f64(o[idx[:, 0], idx[:, 1], idx[:, 2]])
+    err = helpers.max_abs_err(got, helpers.oracle_rows(w, q, k, v, desc, rows))
+    print(f"  n_split {n}, {len(rows)} rows, max-abs {err:.3e}", flush=True)
+    assert err <= TOL["bf16"], err

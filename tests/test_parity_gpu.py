@@ -120,7 +120,7 @@ def test_parity_full_size_sampled(name):
     w = workload.WORKLOADS[name]
     print(f"case {name} (full size, sampled rows)", flush=True)
     q, k, v, desc = workload.make_inputs(w)
-    o = helpers.gpu_run(w, q, k, v, desc)
+    o = helpers.gpu_run(w, q, k, v, desc, n_split=w.n_split)
     rows = _sample_rows(w, np.random.default_rng(w.seed))
     idx = torch.tensor(rows)
     got_rows = helpers.out_to_f64(o[idx[:, 0], idx[:, 1], idx[:, 2]])
@@ -128,7 +128,7 @@ def test_parity_full_size_sampled(name):
     err = helpers.max_abs_err(got_rows, want)
     print(f"  {len(rows)} rows, max-abs {err:.3e}", flush=True)
     assert err <= TOL[w.dtype], err
-    if w.causal and w.dtype in ("bf16", "f16"):
+    if w.causal is True and w.dtype in ("bf16", "f16"):
         # Causal row 0 sees only key 0: weight exactly 1, so the output is V[0] bit for bit.
         g = np.arange(w.Hq) // (w.Hq // w.Hkv)
         v0 = v[:, 0][:, torch.from_numpy(g)]
