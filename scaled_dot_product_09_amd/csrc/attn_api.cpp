@@ -60,7 +60,7 @@ int validate(const void* q, const void* k, const void* v, const void* out,
 
 attn::FwdParams make_params(const void* q, const void* k, const void* v, void* out,
                             int B, int Hq, int Hkv, int Sq, int Skv, float scale_log2, float out_mul,
-                            int causal, bool mfma, int rows_per_wave, int waves) {
+                            int causal, bool mfma, int rows_per_wave, int waves, bool wide_heads = false) {
     attn::FwdParams p;
     // Bottom-right alignment shifts every query to position Skv - Sq + i.
     p.causal_off = causal == 2 ? Skv - Sq : 0;
@@ -71,10 +71,28 @@ attn::FwdParams make_params(const void* q, const void* k, const void* v, void* o
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Sq = Sq; p.Skv = Skv;
     p.G = Hq / Hkv;
     // A workgroup of `waves` waves shares one KV head between gpack query
-    // heads (the largest of 4, 2, 1 dividing G) and waves / gpack row blocks
-    // of rows_per_wave rows each.
+    // heads and covers rows_per_wave * waves / gpack rows of each. gpack is
+    // the largest of 4, 2, 1 dividing G. The four- and eight-wave kernels
+    // (wide_heads), whose MFMA columns may mix heads, double it while G
+    // allows and the heads' Sq rows still fit the workgroup's slots
+    // (gpack * Sq <= rows_per_wave * waves): with few query rows (decode
+    // with GQA / MQA) the slots then hold rows of many heads instead of
+    // empty rows of one.
     p.gpack = mfma ? ((p.G % 4 == 0) ? 4 : (p.G % 2 == 0) ? 2 : 1) : 1;
-    p.rows_per_wg = rows_per_wave * (waves / p.gpack);
+    if (mfma && wide_heads) {
+        const int slots = rows_per_wave * waves;
+        while (p.G % (2 * p.gpack) == 0 && 2 * p.gpack <= slots && (int64_t)2 * p.gpack * Sq <= slots)
+            p.gpack *= 2;
+    }
+    p.rows_per_wg = rows_per_wave * waves / p.gpack;
+    // Slot map of the four- and eight-wave kernels: runs of head_stride
+    // consecutive rows of one head, heads interleaved between runs. 32 (one
+    // head per wave, 32 rows) when there are that many rows; with fewer
+    // rows, the smallest power of two >= Sq, so the rows of all gpack heads
+    // sit in the first waves and the rest have no work.
+    int hs = 1;
+    while (hs < Sq && hs < 32) hs *= 2;
+    p.head_stride = hs < p.rows_per_wg ? hs : p.rows_per_wg;
     p.n_row_blocks = (Sq + p.rows_per_wg - 1) / p.rows_per_wg;
     p.n_units = B * Hkv * (p.G / p.gpack);
     p.xcd_remap = (p.n_units % 8 == 0) ? 1 : 0;
@@ -115,8 +133,9 @@ hipError_t launch_mfma(const void* q, const void* k, const void* v, void* out,
     const MfmaKernel kern = mfma_kernel();
     const int rpw = kern == kRows64 ? 64 : 32;
     const int waves = (kern == kPingPong || kern == kEightWave) ? 8 : 4;
+    const bool wide = kern == kFourWave || kern == kEightWave;
     const attn::FwdParams p = make_params(q, k, v, out, B, Hq, Hkv, Sq, Skv, scale_log2, out_mul,
-                                          causal, true, rpw, waves);
+                                          causal, true, rpw, waves, wide);
     const bool masked = causal != 0;
     switch (kern) {
         case kRows64: return attn::launch_fwd_rb2(p, D, dtype, masked, stream);
@@ -131,10 +150,9 @@ hipError_t launch_mfma(const void* q, const void* k, const void* v, void* out,
 // Workgroups of the four-wave kernel for a shape (the unit of the split
 // heuristic), and the key tiles a row block sees at most.
 int64_t base_grid(int B, int Hq, int Hkv, int Sq) {
-    const int G = Hq / Hkv;
-    const int gpack = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
-    const int rows_per_wg = 32 * (4 / gpack);
-    return (int64_t)B * Hkv * (G / gpack) * ((Sq + rows_per_wg - 1) / rows_per_wg);
+    const attn::FwdParams p = make_params(nullptr, nullptr, nullptr, nullptr, B, Hq, Hkv, Sq, 1, 1.0f, 1.0f,
+                                          0, true, 32, 4, true);
+    return (int64_t)p.n_units * p.n_row_blocks;
 }
 
 }  // namespace
@@ -188,11 +206,13 @@ extern "C" size_t attn_split_workspace(int B, int Hq, int Sq, int D, int n_split
 extern "C" int attn_split_suggest(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Skv <= 0 || Hq % Hkv != 0 || (D != 64 && D != 128))
         return 1;
-    // Aim at 1024 workgroups (four per CU, two resident at a time), with at
-    // least four 64-key tiles per range.
+    // Aim at 256 workgroups (one per CU), with at least four 64-key tiles per
+    // range. Measured on decode shapes (one to four queries, 4K to 64K keys,
+    // GQA and MQA): more ranges than that cost more in partial results and
+    // short ranges than they gain in parallelism.
     const int64_t base = base_grid(B, Hq, Hkv, Sq);
     const int64_t tiles = (Skv + 63) / 64;
-    int64_t n = (1024 + base - 1) / base;
+    int64_t n = (256 + base - 1) / base;
     n = n < tiles / 4 ? n : tiles / 4;
     if (causal == 1) n = n < (Sq + 63) / 64 / 4 ? n : (Sq + 63) / 64 / 4;   // keys beyond the rows are never read
     if (n < 1) n = 1;
@@ -218,7 +238,7 @@ extern "C" int attn_fwd_split(const void* q, const void* k, const void* v, void*
         return ATTN_ERR_WORKSPACE;
     // The split path always runs the four-wave kernel.
     attn::FwdParams p = make_params(q, k, v, out, B, Hq, Hkv, Sq, Skv, nonzero_multiplier(scale * kLog2e), 1.0f,
-                                    causal, true, 32, 4);
+                                    causal, true, 32, 4, true);
     p.n_split = n_split;
     p.part_o = (float*)workspace;
     p.part_ml = (float*)workspace + (size_t)n_split * B * Sq * Hq * D;

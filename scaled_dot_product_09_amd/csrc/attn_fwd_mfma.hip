@@ -76,8 +76,21 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
     const int n = lane & 31;              // query column inside the wave's 32 rows
 
     const WorkItem wi = map_workgroup(p, CAUSAL);
-    const int hq = wi.hq0 + (wave % p.gpack);
-    const int q0 = wi.row_base + (wave / p.gpack) * 32;
+    // The workgroup's 32 * NWAVES query slots cover gpack query heads (of one
+    // KV head) times rows_per_wg rows, in runs of HS = head_stride rows of
+    // one head: slot s is head hq0 + (s / HS) % gpack and row
+    // row_base + (s / (HS gpack)) HS + s % HS. Lane n of a wave owns slot
+    // 32 wave + n. With HS = 32 a wave holds 32 rows of one head; with
+    // fewer rows than that per head (decode with GQA / MQA) a wave's 32 MFMA
+    // columns hold rows of several heads instead of empty rows.
+    const int HS = p.head_stride;
+    const int slot = wave * 32 + n;
+    const int hq = wi.hq0 + (slot / HS) % p.gpack;
+    const int qrow = wi.row_base + (slot / (HS * p.gpack)) * HS + slot % HS;
+    // No slot of this wave holds a query row (its first slot has its
+    // smallest row): it only copies tiles and keeps the workgroup's barriers.
+    const bool wave_idle =
+        __builtin_amdgcn_readfirstlane(wi.row_base + (wave * 32 / (HS * p.gpack)) * HS) >= p.Sq;
     const int Sq = p.Sq;
     int Skv = p.Skv;                                   // keys of this workgroup's range, from its start
     const size_t qstride = (size_t)p.Hq * D;          // elements between query rows
@@ -89,14 +102,14 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
     const size_t kstride_b = kstride * Tr::IN_BYTES;
 
     // Q^T operand, kept in registers for the whole key loop: lane (h, n) holds
-    // bytes [(2 ks + h) * QK_LANE_BYTES, +QK_LANE_BYTES) of row q0 + n.
+    // bytes [(2 ks + h) * QK_LANE_BYTES, +QK_LANE_BYTES) of its slot's row.
     // A negative scale is folded into Q: the kernel computes (-q).k, which
     // is exactly -(q.k) (negation is exact and the products are summed in
     // the same order), with the multiplier |c|, so the softmax below only
     // ever sees c >= 0 and masks with -inf.
     qk_frag qf[KSTEPS];
     {
-        const int row = q0 + n;
+        const int row = qrow;
         const uint8_t* src = (const uint8_t*)(qbase + row * qstride);
         const uint32_t flip = p.scale_log2 < 0.f ? Tr::SIGN_BITS : 0u;
         for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -138,7 +151,7 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
         Skv -= tb * BN;
         coff -= tb * BN;
         if (n_tiles == 0) {   // no keys in range: weight sum 0, max -inf, output 0
-            const int row = q0 + n;
+            const int row = qrow;
             if (row < Sq) {
                 const size_t r = (qrow_idx + row) * p.Hq + hq;
                 for (int db = 0; db < NDB; ++db)
@@ -214,7 +227,6 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
     float neg_m = 0.f;         // exponent offset -m_run of the tile being weighted
 
     const float c_log2 = fabsf(p.scale_log2);   // > 0: the host never passes 0
-    const int qrow = q0 + n;
 
     // Per-lane constants of the V transpose read (see load_v).
     const int L16 = lane & 15;                 // lane inside its 16-lane group
@@ -444,24 +456,36 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
     if (n_tiles > 1) issue_k(1, kbuf1);
     finish_v(vbuf0);
     dma_barrier();
-    qk_tile(kbuf0, s0);
-    mask_tile(s0, 0);
-    {
+    if (!wave_idle) {
+        qk_tile(kbuf0, s0);
+        mask_tile(s0, 0);
         float mraw = masked;
 #pragma unroll
         for (int g = 0; g < 4; ++g) mraw = max_piece(s0, g, mraw);
         neg_m = finish_max(mraw);
     }
-    int j = 0;
-    for (; j + 2 < n_tiles; j += 2) {
-        iteration(std::true_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
-        iteration(std::true_type{}, j + 1, s1, s0, kbuf1, kbuf0, vbuf1, vbuf0);
-    }
-    if (j + 1 < n_tiles) {
-        iteration(std::true_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
-        iteration(std::false_type{}, j + 1, s1, s0, kbuf1, kbuf0, vbuf1, vbuf0);
+    if (wave_idle) {
+        // Same copies and barriers as an iteration, no compute.
+        for (int j = 0; j < n_tiles; ++j) {
+            dma_barrier();
+            if (j + 1 < n_tiles) {
+                if (j + 2 < n_tiles) issue_k(j + 2, (j & 1) ? kbuf1 : kbuf0);
+                issue_v(j + 1, (j & 1) ? vbuf0 : vbuf1);
+                finish_v((j & 1) ? vbuf0 : vbuf1);
+            }
+        }
     } else {
-        iteration(std::false_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
+        int j = 0;
+        for (; j + 2 < n_tiles; j += 2) {
+            iteration(std::true_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
+            iteration(std::true_type{}, j + 1, s1, s0, kbuf1, kbuf0, vbuf1, vbuf0);
+        }
+        if (j + 1 < n_tiles) {
+            iteration(std::true_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
+            iteration(std::false_type{}, j + 1, s1, s0, kbuf1, kbuf0, vbuf1, vbuf0);
+        } else {
+            iteration(std::false_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
+        }
     }
 
     // ---- epilogue: O = O^T / l, round once, store [b][row][hq][d] ----------

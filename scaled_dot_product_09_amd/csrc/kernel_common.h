@@ -27,6 +27,7 @@ struct FwdParams {
     int B, Hq, Hkv, Sq, Skv;
     int G;              // query heads per KV head, Hq / Hkv
     int gpack;          // query heads of one KV head handled by one workgroup
+    int head_stride;    // consecutive query slots of one head (see the slot map of the kernels)
     int rows_per_wg;    // query rows per head handled by one workgroup
     int n_row_blocks;   // ceil(Sq / rows_per_wg)
     int n_units;        // B * Hkv * (G / gpack): (batch, KV head, head group) units
