@@ -103,8 +103,9 @@ def time_workload(w, steps, warmup, rotate=True, settle_s=SETTLE_S):
     nsets = N_BUFFER_SETS if rotate else 1
     sets = []
     for i in range(nsets):
-        qd, kd, vd = (x.to(dev) for x in (q, k, v))
-        od = torch.empty(q.shape, dtype=torch.bfloat16 if w.dtype == "e4m3" else q.dtype, device=dev)
+        qd, kd, vd = (workload.to_layout(x.to(dev), w.layout) for x in (q, k, v))
+        od = workload.to_layout(torch.empty(q.shape, dtype=torch.bfloat16 if w.dtype == "e4m3" else q.dtype,
+                                            device=dev), w.layout)
         sets.append((qd, kd, vd, od))
     fp8 = w.dtype == "e4m3"
     stream = torch.cuda.current_stream(dev)
@@ -172,7 +173,7 @@ def result_line(w, t, steps, warmup, n_gpus, cpu=None, warm=None):
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq, "Skv": w.Skv,
                    "D": w.D, "causal": w.causal, "input_dtype": w.dtype, "output_dtype": w.out_dtype,
-                   "parallelism": "single GPU", "rotating_input_sets": N_BUFFER_SETS},
+                   "parallelism": "single GPU", "rotating_input_sets": N_BUFFER_SETS, "layout": w.layout},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "median_ms": round(t["median_ms"], 5), "min_ms": round(t["min_ms"], 5),
         "settle_steps": t["settle_steps"],

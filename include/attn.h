@@ -52,6 +52,8 @@
 #define ATTN_MI355X_ATTN_H
 
 #include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -73,7 +75,7 @@ enum attn_status {
     ATTN_ERR_SHAPE = -2,      /* B < 0, Sq < 0, Hq/Hkv/D <= 0, or Skv < 1 with
                                  B*Sq > 0, or a tensor exceeds 2^31 elements     */
     ATTN_ERR_GROUP = -3,      /* Hq is not a multiple of Hkv                    */
-    ATTN_ERR_HEAD_DIM = -4,   /* D is not 64 or 128                             */
+    ATTN_ERR_HEAD_DIM = -4,   /* D is not 32, 64 or 128 (E4M3: not 64 or 128)  */
     ATTN_ERR_DTYPE = -5,      /* unknown dtype, or ATTN_FP8_E4M3 given to
                                  attn_fwd (FP8 needs attn_fwd_fp8's descales)   */
     ATTN_ERR_ALIGN = -6,      /* a pointer is not 16-byte aligned               */
@@ -83,8 +85,10 @@ enum attn_status {
     ATTN_ERR_CAUSAL = -10,    /* causal is not 0, 1 or 2, or causal = 2 with
                                  Sq > Skv                                       */
     ATTN_ERR_SPLIT = -11,     /* n_split outside 1 .. ATTN_MAX_SPLIT            */
-    ATTN_ERR_WORKSPACE = -12  /* workspace NULL, misaligned, too small, or
+    ATTN_ERR_WORKSPACE = -12, /* workspace NULL, misaligned, too small, or
                                  overlapping an input or the output             */
+    ATTN_ERR_STRIDE = -13     /* a stride is negative or above 2^40, or out's
+                                 strides map two elements to one address        */
 };
 
 /* Largest number of key ranges attn_fwd_split accepts. */
@@ -100,7 +104,7 @@ enum attn_status {
  *   Hq, Hkv  query heads and K/V heads (> 0, Hq % Hkv == 0)
  *   Sq, Skv  query and key/value sequence lengths (Sq >= 0; Skv >= 1 unless
  *            B * Sq == 0)
- *   D        head dimension, 64 or 128
+ *   D        head dimension: 32, 64 or 128 (attn_fwd_fp8: 64 or 128)
  *   scale    any finite float; the codelab uses 1 / sqrt(D) (§4)
  *   causal   0 = full attention, 1 = lower-triangular mask (§7), 2 = the same
  *            mask aligned bottom-right (Sq <= Skv; see above)
@@ -166,6 +170,31 @@ size_t attn_split_workspace(int B, int Hq, int Sq, int D, int n_split);
  * GPU for this shape (1 when attn_fwd alone already does). Arguments as
  * attn_fwd; returns 1 for shapes attn_fwd would reject. */
 int attn_split_suggest(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal);
+
+/*
+ * attn_fwd_strided — attn_fwd on tensors with arbitrary batch, sequence and
+ * head strides (the head dimension D must be contiguous): e.g. (B, H, S, D)
+ * tensors seen as (B, S, H, D), slices of a packed QKV buffer, or K and V
+ * shared by every batch (batch stride 0). The layout sensitivity of fused
+ * kernels is noted in §3 of the codelab.
+ *
+ *   q_strides, k_strides, v_strides, out_strides
+ *            host pointers to 3 element strides each: batch, sequence, head
+ *            (element (b, i, h, d) of q is q[b*s0 + i*s1 + h*s2 + d]); each
+ *            stride in [0, 2^40], times the element size a multiple of 16
+ *            bytes; out's strides must give every output element its own
+ *            address, and out's span must not overlap any input's span
+ *   dtype    ATTN_F32, ATTN_BF16 or ATTN_F16
+ *
+ * Other arguments and errors as attn_fwd; additionally ATTN_ERR_STRIDE, and
+ * ATTN_ERR_SHAPE when (Skv - 1) * key stride + D elements of one head span
+ * 2^32 bytes or more.
+ */
+int attn_fwd_strided(const void* q, const void* k, const void* v, void* out,
+                     int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                     const int64_t* q_strides, const int64_t* k_strides,
+                     const int64_t* v_strides, const int64_t* out_strides,
+                     float scale, int causal, int dtype, hipStream_t stream);
 
 /* attn_strerror — a static, human-readable description of a status code. */
 const char* attn_strerror(int status);

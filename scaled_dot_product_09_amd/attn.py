@@ -9,7 +9,8 @@ raised.
 
 The names follow include/attn.h: ``attn_fwd``, ``attn_fwd_fp8``,
 ``attn_fwd_split``, ``attn_split_workspace``, ``attn_split_suggest``,
-``attn_strerror``; :func:`fwd` is the tensor-level convenience wrapper.
+``attn_fwd_strided``, ``attn_strerror``; :func:`fwd` is the tensor-level
+convenience wrapper.
 """
 
 import ctypes
@@ -27,9 +28,9 @@ DTYPE_CODE = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16, torch.float16:
 STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_GROUP",
           -4: "ATTN_ERR_HEAD_DIM", -5: "ATTN_ERR_DTYPE", -6: "ATTN_ERR_ALIGN", -7: "ATTN_ERR_ALIAS",
           -8: "ATTN_ERR_SCALE", -9: "ATTN_ERR_HIP", -10: "ATTN_ERR_CAUSAL", -11: "ATTN_ERR_SPLIT",
-          -12: "ATTN_ERR_WORKSPACE"}
+          -12: "ATTN_ERR_WORKSPACE", -13: "ATTN_ERR_STRIDE"}
 EXPORTS = ("attn_fwd", "attn_fwd_fp8", "attn_fwd_split", "attn_split_workspace", "attn_split_suggest",
-           "attn_strerror")
+           "attn_fwd_strided", "attn_strerror")
 # causal argument: 0 none, 1 lower triangle (top-left), 2 bottom-right (Sq <= Skv)
 CAUSAL_CODE = {False: 0, True: 1, "top_left": 1, "bottom_right": 2, 0: 0, 1: 1, 2: 2}
 
@@ -60,6 +61,8 @@ def lib():
         L.attn_split_workspace.restype = ctypes.c_size_t
         L.attn_split_suggest.argtypes = [i, i, i, i, i, i, i]
         L.attn_split_suggest.restype = i
+        L.attn_fwd_strided.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, vp, vp, f, i, i, vp]
+        L.attn_fwd_strided.restype = i
         L.attn_strerror.argtypes = [i]
         L.attn_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -96,6 +99,14 @@ def attn_split_suggest(B, Hq, Hkv, Sq, Skv, D, causal):
     return int(lib().attn_split_suggest(B, Hq, Hkv, Sq, Skv, D, int(causal)))
 
 
+def attn_fwd_strided(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, q_strides, k_strides, v_strides, out_strides,
+                     scale, causal, dtype, stream):
+    """Raw C call of the strided entry point (strides: 3 ints each), returns the status code."""
+    arr = [(ctypes.c_int64 * 3)(*map(int, st)) for st in (q_strides, k_strides, v_strides, out_strides)]
+    return lib().attn_fwd_strided(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, *[ctypes.addressof(a) for a in arr],
+                                  float(scale), int(causal), int(dtype), stream)
+
+
 def _check(st):
     if st != 0:
         raise AttnError(st, attn_strerror(st))
@@ -105,8 +116,11 @@ def fwd(q, k, v, *, causal=False, scale=None, out=None, descales=None, stream=No
         workspace=None):
     """out = softmax(scale * q k^T [+ causal mask]) v on torch device tensors.
 
-    q: (B, Sq, Hq, D), k and v: (B, Skv, Hkv, D), contiguous, same dtype
-    (float32, bfloat16, float16 or float8_e4m3fn) on one GPU. ``causal``:
+    q: (B, Sq, Hq, D), k and v: (B, Skv, Hkv, D), same dtype (float32,
+    bfloat16, float16 or float8_e4m3fn) on one GPU. Non-contiguous views
+    (last axis contiguous; e.g. transposed (B, H, S, D) storage or slices of a
+    packed buffer) go through attn_fwd_strided (float32 / bfloat16 / float16;
+    ``out`` may be such a view too). ``causal``:
     False, True (lower triangle, top-left aligned) or "bottom_right" (the
     queries are the last Sq of Skv positions; needs Sq <= Skv). ``scale``
     defaults to 1 / sqrt(D). E4M3 inputs need ``descales`` = (q, k, v)
@@ -122,8 +136,9 @@ def fwd(q, k, v, *, causal=False, scale=None, out=None, descales=None, stream=No
             raise ValueError(f"{name} must be a 4-D torch tensor (B, S, H, D)")
         if not t.is_cuda:
             raise ValueError(f"{name} must be on the GPU")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
+        if t.stride(3) != 1:
+            raise ValueError(f"{name}'s last (head-dimension) axis must be contiguous")
+    dense = q.is_contiguous() and k.is_contiguous() and v.is_contiguous()
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in DTYPE_CODE:
         raise ValueError(f"unsupported or mixed dtypes {q.dtype}, {k.dtype}, {v.dtype}")
     if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
@@ -139,8 +154,19 @@ def fwd(q, k, v, *, causal=False, scale=None, out=None, descales=None, stream=No
     out_dtype = torch.bfloat16 if code == ATTN_FP8_E4M3 else q.dtype
     if out is None:
         out = torch.empty((B, Sq, Hq, D), dtype=out_dtype, device=q.device)
-    elif out.shape != q.shape or out.dtype != out_dtype or not out.is_contiguous() or out.device != q.device:
-        raise ValueError("out must be a contiguous tensor with q's shape, on q's device, of the output dtype")
+    elif out.shape != q.shape or out.dtype != out_dtype or out.device != q.device or out.stride(3) != 1:
+        raise ValueError("out must have q's shape, q's device, the output dtype and a contiguous last axis")
+    dense = dense and out.is_contiguous()
+    if not dense:
+        if code == ATTN_FP8_E4M3 or n_split is not None:
+            raise ValueError("strided layouts are supported for float32 / bfloat16 / float16 without n_split")
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = attn_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, Sq, Skv, D,
+                              q.stride()[:3], k.stride()[:3], v.stride()[:3], out.stride()[:3],
+                              scale, causal, code, stream)
+        _check(st)
+        return out
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     if n_split is not None:

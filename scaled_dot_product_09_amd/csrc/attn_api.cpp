@@ -41,7 +41,8 @@ int validate(const void* q, const void* k, const void* v, const void* out,
     if (!q || !k || !v || !out) return ATTN_ERR_NULL;
     if (B < 0 || Sq < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Skv < 0) return ATTN_ERR_SHAPE;
     if (Hq % Hkv != 0) return ATTN_ERR_GROUP;
-    if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+    if (D != 32 && D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+    if (D == 32 && in_bytes == 1) return ATTN_ERR_HEAD_DIM;   // one FP8 score MFMA spans 64 of D
     if (!isfinite(scale)) return ATTN_ERR_SCALE;
     if (causal < 0 || causal > 2) return ATTN_ERR_CAUSAL;
     if ((int64_t)B * Sq == 0) { *noop = true; return ATTN_OK; }
@@ -101,6 +102,20 @@ attn::FwdParams make_params(const void* q, const void* k, const void* v, void* o
     return p;
 }
 
+// Dense (B, S, H, D) element strides of the batch, sequence and head axes.
+void dense_strides(int64_t* st, int S, int H, int D) {
+    st[0] = (int64_t)S * H * D;
+    st[1] = (int64_t)H * D;
+    st[2] = D;
+}
+
+void set_dense_strides(attn::FwdParams& p, int D) {
+    dense_strides(p.sq, p.Sq, p.Hq, D);
+    dense_strides(p.sk, p.Skv, p.Hkv, D);
+    dense_strides(p.sv, p.Skv, p.Hkv, D);
+    dense_strides(p.so, p.Sq, p.Hq, D);
+}
+
 const float kLog2e = 1.4426950408889634f;
 
 // The kernels never see a zero score multiplier: scale 0 (every visible key
@@ -127,15 +142,27 @@ MfmaKernel mfma_kernel() {
     return kFourWave;
 }
 
+// strides: NULL (dense) or q, k, v, out element strides (batch, seq, head).
 hipError_t launch_mfma(const void* q, const void* k, const void* v, void* out,
                        int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale_log2,
-                       float out_mul, int dtype, int causal, hipStream_t stream) {
-    const MfmaKernel kern = mfma_kernel();
+                       float out_mul, int dtype, int causal, const int64_t* strides, hipStream_t stream) {
+    // Head dimension 32 and strided layouts exist only in the four- and
+    // eight-wave kernel.
+    const bool four_or_eight = D == 32 || strides;
+    const MfmaKernel kern = (four_or_eight && (mfma_kernel() == kPingPong || mfma_kernel() == kRows64))
+                                ? kFourWave : mfma_kernel();
     const int rpw = kern == kRows64 ? 64 : 32;
     const int waves = (kern == kPingPong || kern == kEightWave) ? 8 : 4;
     const bool wide = kern == kFourWave || kern == kEightWave;
-    const attn::FwdParams p = make_params(q, k, v, out, B, Hq, Hkv, Sq, Skv, scale_log2, out_mul,
-                                          causal, true, rpw, waves, wide);
+    attn::FwdParams p = make_params(q, k, v, out, B, Hq, Hkv, Sq, Skv, scale_log2, out_mul,
+                                    causal, true, rpw, waves, wide);
+    if (strides) {
+        for (int i = 0; i < 3; ++i) {
+            p.sq[i] = strides[i]; p.sk[i] = strides[3 + i]; p.sv[i] = strides[6 + i]; p.so[i] = strides[9 + i];
+        }
+    } else {
+        set_dense_strides(p, D);
+    }
     const bool masked = causal != 0;
     switch (kern) {
         case kRows64: return attn::launch_fwd_rb2(p, D, dtype, masked, stream);
@@ -171,12 +198,13 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out,
     if (st != ATTN_OK || noop) return st;
     hipError_t e;
     if (dtype == ATTN_F32) {
-        const attn::FwdParams p = make_params(q, k, v, out, B, Hq, Hkv, Sq, Skv,
-                                              nonzero_multiplier(scale * kLog2e), 1.0f, causal, false, 32, 4);
+        attn::FwdParams p = make_params(q, k, v, out, B, Hq, Hkv, Sq, Skv,
+                                        nonzero_multiplier(scale * kLog2e), 1.0f, causal, false, 32, 4);
+        set_dense_strides(p, D);
         e = attn::launch_fwd_f32(p, D, causal != 0, stream);
     } else {
         e = launch_mfma(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, nonzero_multiplier(scale * kLog2e), 1.0f,
-                        dtype, causal, stream);
+                        dtype, causal, nullptr, stream);
     }
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
@@ -194,7 +222,7 @@ extern "C" int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o
     const float sl2 = scale * q_descale * k_descale * kLog2e;
     if (!isfinite(sl2)) return ATTN_ERR_SCALE;
     const hipError_t e = launch_mfma(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, nonzero_multiplier(sl2), v_descale,
-                                     ATTN_FP8_E4M3, causal, stream);
+                                     ATTN_FP8_E4M3, causal, nullptr, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -204,7 +232,7 @@ extern "C" size_t attn_split_workspace(int B, int Hq, int Sq, int D, int n_split
 }
 
 extern "C" int attn_split_suggest(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal) {
-    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Skv <= 0 || Hq % Hkv != 0 || (D != 64 && D != 128))
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Skv <= 0 || Hq % Hkv != 0 || (D != 32 && D != 64 && D != 128))
         return 1;
     // Aim at 256 workgroups (one per CU), with at least four 64-key tiles per
     // range. Measured on decode shapes (one to four queries, 4K to 64K keys,
@@ -239,11 +267,96 @@ extern "C" int attn_fwd_split(const void* q, const void* k, const void* v, void*
     // The split path always runs the four-wave kernel.
     attn::FwdParams p = make_params(q, k, v, out, B, Hq, Hkv, Sq, Skv, nonzero_multiplier(scale * kLog2e), 1.0f,
                                     causal, true, 32, 4, true);
+    set_dense_strides(p, D);
     p.n_split = n_split;
     p.part_o = (float*)workspace;
     p.part_ml = (float*)workspace + (size_t)n_split * B * Sq * Hq * D;
     hipError_t e = attn::launch_fwd_mfma(p, D, dtype == ATTN_BF16, causal != 0, 4, stream);
     if (e == hipSuccess) e = attn::launch_combine(p, D, dtype == ATTN_BF16, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+namespace {
+
+// Largest element offset a (B, S, H, D) view with non-negative strides reaches, plus 1.
+int64_t extent(const int64_t* st, int B, int S, int H, int D) {
+    return (int64_t)(B - 1) * st[0] + (int64_t)(S - 1) * st[1] + (int64_t)(H - 1) * st[2] + D;
+}
+
+// No two (b, i, h, d) of a view share an element: sorted by stride, every
+// axis of size > 1 steps over the whole extent of the faster ones.
+bool injective(const int64_t* st, int B, int S, int H, int D) {
+    int64_t s[4] = {1, st[0], st[1], st[2]};
+    int64_t n[4] = {D, B, S, H};
+    for (int a = 1; a < 4; ++a)
+        for (int b = a; b > 0 && s[b] < s[b - 1]; --b) {
+            int64_t t = s[b]; s[b] = s[b - 1]; s[b - 1] = t;
+            t = n[b]; n[b] = n[b - 1]; n[b - 1] = t;
+        }
+    int64_t span = 1;   // elements covered by the faster axes, as a stride unit
+    for (int a = 0; a < 4; ++a) {
+        if (n[a] == 1) continue;
+        if (s[a] < span) return false;
+        span = s[a] * n[a];
+    }
+    return true;
+}
+
+}  // namespace
+
+extern "C" int attn_fwd_strided(const void* q, const void* k, const void* v, void* out,
+                                int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                                const int64_t* q_strides, const int64_t* k_strides,
+                                const int64_t* v_strides, const int64_t* out_strides,
+                                float scale, int causal, int dtype, hipStream_t stream) {
+    int eb;
+    switch (dtype) {
+        case ATTN_F32: eb = 4; break;
+        case ATTN_BF16: case ATTN_F16: eb = 2; break;
+        default: return ATTN_ERR_DTYPE;
+    }
+    if (!q || !k || !v || !out || !q_strides || !k_strides || !v_strides || !out_strides) return ATTN_ERR_NULL;
+    if (B < 0 || Sq < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Skv < 0) return ATTN_ERR_SHAPE;
+    if (Hq % Hkv != 0) return ATTN_ERR_GROUP;
+    if (D != 32 && D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+    if (!isfinite(scale)) return ATTN_ERR_SCALE;
+    if (causal < 0 || causal > 2) return ATTN_ERR_CAUSAL;
+    if ((int64_t)B * Sq == 0) return ATTN_OK;
+    if (Skv < 1) return ATTN_ERR_SHAPE;
+    if (causal == 2 && Sq > Skv) return ATTN_ERR_CAUSAL;
+    const int64_t* all[4] = {q_strides, k_strides, v_strides, out_strides};
+    for (const int64_t* st : all)
+        for (int i = 0; i < 3; ++i) {
+            if (st[i] < 0 || st[i] > ((int64_t)1 << 40)) return ATTN_ERR_STRIDE;
+            if ((st[i] * eb) % 16 != 0) return ATTN_ERR_ALIGN;
+        }
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15) return ATTN_ERR_ALIGN;
+    if (!injective(out_strides, B, Sq, Hq, D)) return ATTN_ERR_STRIDE;
+    // A key tile's byte offsets inside one head must fit in 32 bits.
+    if (((int64_t)(Skv - 1) * k_strides[1] + D) * eb >= ((int64_t)1 << 32) ||
+        ((int64_t)(Skv - 1) * v_strides[1] + D) * eb >= ((int64_t)1 << 32))
+        return ATTN_ERR_SHAPE;
+    const int64_t eq = extent(q_strides, B, Sq, Hq, D) * eb, ek = extent(k_strides, B, Skv, Hkv, D) * eb;
+    const int64_t ev = extent(v_strides, B, Skv, Hkv, D) * eb, eo = extent(out_strides, B, Sq, Hq, D) * eb;
+    if (ranges_overlap(out, eo, q, eq) || ranges_overlap(out, eo, k, ek) || ranges_overlap(out, eo, v, ev))
+        return ATTN_ERR_ALIAS;
+    int64_t strides[12];
+    for (int i = 0; i < 3; ++i) {
+        strides[i] = q_strides[i]; strides[3 + i] = k_strides[i];
+        strides[6 + i] = v_strides[i]; strides[9 + i] = out_strides[i];
+    }
+    hipError_t e;
+    if (dtype == ATTN_F32) {
+        attn::FwdParams p = make_params(q, k, v, out, B, Hq, Hkv, Sq, Skv,
+                                        nonzero_multiplier(scale * kLog2e), 1.0f, causal, false, 32, 4);
+        for (int i = 0; i < 3; ++i) {
+            p.sq[i] = strides[i]; p.sk[i] = strides[3 + i]; p.sv[i] = strides[6 + i]; p.so[i] = strides[9 + i];
+        }
+        e = attn::launch_fwd_f32(p, D, causal != 0, stream);
+    } else {
+        e = launch_mfma(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, nonzero_multiplier(scale * kLog2e), 1.0f,
+                        dtype, causal, strides, stream);
+    }
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -253,7 +366,7 @@ extern "C" const char* attn_strerror(int status) {
         case ATTN_ERR_NULL: return "a pointer argument is NULL";
         case ATTN_ERR_SHAPE: return "invalid shape (B, Sq >= 0; Hq, Hkv, D > 0; Skv >= 1 unless B*Sq == 0; < 2^31 elements per tensor)";
         case ATTN_ERR_GROUP: return "Hq is not a multiple of Hkv";
-        case ATTN_ERR_HEAD_DIM: return "head dimension D must be 64 or 128";
+        case ATTN_ERR_HEAD_DIM: return "head dimension D must be 32, 64 or 128 (64 or 128 for E4M3 inputs)";
         case ATTN_ERR_DTYPE: return "unsupported dtype (attn_fwd takes F32, BF16, F16; E4M3 goes through attn_fwd_fp8)";
         case ATTN_ERR_ALIGN: return "q, k, v and out must be 16-byte aligned";
         case ATTN_ERR_ALIAS: return "out overlaps an input";
@@ -261,6 +374,7 @@ extern "C" const char* attn_strerror(int status) {
         case ATTN_ERR_HIP: return "HIP kernel launch failed";
         case ATTN_ERR_CAUSAL: return "causal must be 0, 1 or 2 (2, bottom-right alignment, needs Sq <= Skv)";
         case ATTN_ERR_SPLIT: return "n_split must be between 1 and ATTN_MAX_SPLIT";
+        case ATTN_ERR_STRIDE: return "a stride is negative or too large, or out's strides make two elements share memory";
         case ATTN_ERR_WORKSPACE: return "workspace is NULL, not 16-byte aligned, smaller than attn_split_workspace(), or overlaps an input or the output";
         default: return "unknown status";
     }

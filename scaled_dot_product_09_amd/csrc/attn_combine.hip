@@ -20,8 +20,8 @@ namespace attn {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
-                                                      void* __restrict__ out, int n_split, int rows,
-                                                      float out_mul) {
+                                                      const FwdParams p, int rows) {
+    const int n_split = p.n_split;
     using Tr = Traits<T>;
     constexpr int TPR = D / 4;
     const int t = (int)__builtin_amdgcn_workgroup_id_x() * 256 + (int)__builtin_amdgcn_workitem_id_x();
@@ -42,10 +42,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         acc[2] = fmaf(w, o[2], acc[2]);
         acc[3] = fmaf(w, o[3], acc[3]);
     }
-    const float inv = out_mul / L;
+    const float inv = p.out_mul / L;
     const uint32_t w0 = Tr::pack(acc[0] * inv, acc[1] * inv);
     const uint32_t w1 = Tr::pack(acc[2] * inv, acc[3] * inv);
-    *(u32x2*)((typename Tr::out_t*)out + (size_t)r * D + d0) = (u32x2){w0, w1};
+    // r = (b Sq + row) Hq + hq, the partials' (row, head) order.
+    const int hq = r % p.Hq, t2 = r / p.Hq, row = t2 % p.Sq, b = t2 / p.Sq;
+    typename Tr::out_t* o = (typename Tr::out_t*)p.out + b * p.so[0] + row * p.so[1] + hq * p.so[2] + d0;
+    *(u32x2*)o = (u32x2){w0, w1};
 }
 
 template <typename T, int D>
@@ -53,14 +56,18 @@ static hipError_t launch_combine_typed(const FwdParams& p, hipStream_t stream) {
     const int rows = p.B * p.Sq * p.Hq;
     const int threads = rows * (D / 4);
     hipLaunchKernelGGL((combine_kernel<T, D>), dim3((threads + 255) / 256), dim3(256), 0, stream,
-                       (const float*)p.part_o, (const float*)p.part_ml, p.out, p.n_split, rows, p.out_mul);
+                       (const float*)p.part_o, (const float*)p.part_ml, p, rows);
     return hipGetLastError();
 }
 
-// is_bf16: bfloat16 output, else float16; D = 64 or 128.
+// is_bf16: bfloat16 output, else float16; D = 32, 64 or 128.
 hipError_t launch_combine(const FwdParams& p, int D, bool is_bf16, hipStream_t stream) {
-    if (is_bf16) return D == 64 ? launch_combine_typed<__bf16, 64>(p, stream) : launch_combine_typed<__bf16, 128>(p, stream);
-    return D == 64 ? launch_combine_typed<_Float16, 64>(p, stream) : launch_combine_typed<_Float16, 128>(p, stream);
+    if (is_bf16) {
+        return D == 32 ? launch_combine_typed<__bf16, 32>(p, stream)
+             : D == 64 ? launch_combine_typed<__bf16, 64>(p, stream) : launch_combine_typed<__bf16, 128>(p, stream);
+    }
+    return D == 32 ? launch_combine_typed<_Float16, 32>(p, stream)
+         : D == 64 ? launch_combine_typed<_Float16, 64>(p, stream) : launch_combine_typed<_Float16, 128>(p, stream);
 }
 
 }  // namespace attn

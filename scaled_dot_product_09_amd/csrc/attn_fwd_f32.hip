@@ -36,11 +36,11 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
     const int hkv = hq / p.G;
     const int row = rb * RPW + tid / TPR;
     const int Sq = p.Sq, Skv = p.Skv;
-    const size_t qstride = (size_t)p.Hq * D, kstride = (size_t)p.Hkv * D;
+    const int64_t kstride = p.sk[1], vstride = p.sv[1];
 
-    const float* qrow = (const float*)p.q + ((size_t)b * Sq + row) * qstride + (size_t)hq * D + part * 32;
-    const float* kb = (const float*)p.k + ((size_t)b * Skv * p.Hkv + hkv) * D;
-    const float* vb = (const float*)p.v + ((size_t)b * Skv * p.Hkv + hkv) * D;
+    const float* qrow = (const float*)p.q + b * p.sq[0] + row * p.sq[1] + hq * p.sq[2] + part * 32;
+    const float* kb = (const float*)p.k + b * p.sk[0] + hkv * p.sk[2];
+    const float* vb = (const float*)p.v + b * p.sv[0] + hkv * p.sv[2];
 
     float qv[32], o[32];
     for (int d = 0; d < 32; ++d) { qv[d] = row < Sq ? qrow[d] : 0.f; o[d] = 0.f; }
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
             f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
             if (k0 + r < Skv) {
                 kx = *(const f32x4*)(kb + (k0 + r) * kstride + c);
-                vx = *(const f32x4*)(vb + (k0 + r) * kstride + c);
+                vx = *(const f32x4*)(vb + (k0 + r) * vstride + c);
             }
             *(f32x4*)&lk[r][c] = kx;
             *(f32x4*)&lv[r][c] = vx;
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
 
     if (row < Sq) {
         const float inv = p.out_mul / l_run;
-        float* orow = (float*)p.out + ((size_t)b * Sq + row) * qstride + (size_t)hq * D + part * 32;
+        float* orow = (float*)p.out + b * p.so[0] + row * p.so[1] + hq * p.so[2] + part * 32;
         for (int d = 0; d < 32; d += 4)
             *(f32x4*)(orow + d) = (f32x4){o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv};
     }
@@ -110,7 +110,10 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
 hipError_t launch_fwd_f32(const FwdParams& p, int D, bool causal, hipStream_t stream) {
     const int rpw = 256 / (D / 32);
     const dim3 grid((unsigned)p.B * p.Hq * ((p.Sq + rpw - 1) / rpw)), block(256);
-    if (D == 64) {
+    if (D == 32) {
+        if (causal) hipLaunchKernelGGL((fwd_f32_kernel<32, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((fwd_f32_kernel<32, false>), grid, block, 0, stream, p);
+    } else if (D == 64) {
         if (causal) hipLaunchKernelGGL((fwd_f32_kernel<64, true>), grid, block, 0, stream, p);
         else hipLaunchKernelGGL((fwd_f32_kernel<64, false>), grid, block, 0, stream, p);
     } else {

@@ -93,13 +93,12 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
         __builtin_amdgcn_readfirstlane(wi.row_base + (wave * 32 / (HS * p.gpack)) * HS) >= p.Sq;
     const int Sq = p.Sq;
     int Skv = p.Skv;                                   // keys of this workgroup's range, from its start
-    const size_t qstride = (size_t)p.Hq * D;          // elements between query rows
-    const size_t kstride = (size_t)p.Hkv * D;
 
-    const T* qbase = (const T*)p.q + ((size_t)wi.b * Sq * p.Hq + hq) * D;
-    const uint8_t* kbase = (const uint8_t*)((const T*)p.k + ((size_t)wi.b * p.Skv * p.Hkv + wi.hkv) * D);
-    const uint8_t* vbase = (const uint8_t*)((const T*)p.v + ((size_t)wi.b * p.Skv * p.Hkv + wi.hkv) * D);
-    const size_t kstride_b = kstride * Tr::IN_BYTES;
+    const T* qbase = (const T*)p.q + wi.b * p.sq[0] + hq * p.sq[2];
+    const uint8_t* kbase = (const uint8_t*)((const T*)p.k + wi.b * p.sk[0] + wi.hkv * p.sk[2]);
+    const uint8_t* vbase = (const uint8_t*)((const T*)p.v + wi.b * p.sv[0] + wi.hkv * p.sv[2]);
+    const size_t krow_b = (size_t)p.sk[1] * Tr::IN_BYTES;   // bytes between keys
+    const size_t vrow_b = (size_t)p.sv[1] * Tr::IN_BYTES;
 
     // Q^T operand, kept in registers for the whole key loop: lane (h, n) holds
     // bytes [(2 ks + h) * QK_LANE_BYTES, +QK_LANE_BYTES) of its slot's row.
@@ -110,7 +109,7 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
     qk_frag qf[KSTEPS];
     {
         const int row = qrow;
-        const uint8_t* src = (const uint8_t*)(qbase + row * qstride);
+        const uint8_t* src = (const uint8_t*)(qbase + row * p.sq[1]);
         const uint32_t flip = p.scale_log2 < 0.f ? Tr::SIGN_BITS : 0u;
         for (int ks = 0; ks < KSTEPS; ++ks) {
             u32x4 x[CH];
@@ -146,8 +145,8 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
         const int tb = wi.split * n_tiles / p.n_split;
         const int te = (wi.split + 1) * n_tiles / p.n_split;
         n_tiles = te - tb;
-        kbase += (size_t)tb * BN * kstride_b;
-        vbase += (size_t)tb * BN * kstride_b;
+        kbase += (size_t)tb * BN * krow_b;
+        vbase += (size_t)tb * BN * vrow_b;
         Skv -= tb * BN;
         coff -= tb * BN;
         if (n_tiles == 0) {   // no keys in range: weight sum 0, max -inf, output 0
@@ -184,8 +183,8 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
     constexpr int NWV = (BN * VROWB / 1024) % NWAVES == 0 ? NWAVES : 4;
     TileDma<KROWB, BN, NWK> kdma;
     TileDma<VROWB, BN, NWV> vdma;
-    kdma.init(kbase, (uint32_t)kstride_b, wave % NWK, lane, true);
-    if constexpr (Tr::V_DMA) vdma.init(vbase, (uint32_t)kstride_b, wave % NWV, lane, false);
+    kdma.init(kbase, (uint32_t)krow_b, wave % NWK, lane, true);
+    if constexpr (Tr::V_DMA) vdma.init(vbase, (uint32_t)vrow_b, wave % NWV, lane, false);
     auto issue_k = [&](int j, uint8_t* kt) {
         if (NWK == NWAVES || wave < NWK) kdma.issue(j * BN, Skv, kt, wave);
     };
@@ -197,7 +196,7 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
                 const int id = u * NTHR + tid;
                 const int r = id / (D / 8), c = id % (D / 8);
                 const int key = min(j * BN + r, Skv - 1);
-                vstage[u] = *(const u32x2*)(vbase + key * kstride_b + c * 8);
+                vstage[u] = *(const u32x2*)(vbase + key * vrow_b + c * 8);
             }
         }
     };
@@ -504,7 +503,7 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
     }
     const float inv = p.out_mul / l;
     if (qrow < Sq) {
-        out_t* orow = (out_t*)p.out + ((size_t)wi.b * Sq + qrow) * qstride + (size_t)hq * D;
+        out_t* orow = (out_t*)p.out + wi.b * p.so[0] + qrow * p.so[1] + hq * p.so[2];
         for (int db = 0; db < NDB; ++db) {
             for (int jj = 0; jj < 4; ++jj) {
                 const int d0 = db * 32 + 8 * jj + 4 * h;
@@ -533,18 +532,20 @@ static hipError_t launch_typed(const FwdParams& p, bool causal, int nwaves, hipS
     return hipGetLastError();
 }
 
-// bf16 (is_bf16 = true) or f16 inputs, D = 64 or 128; nwaves = 4 or 8 waves
-// per workgroup.
+// bf16 (is_bf16 = true) or f16 inputs, D = 32, 64 or 128; nwaves = 4 or 8
+// waves per workgroup.
 hipError_t launch_fwd_mfma(const FwdParams& p, int D, bool is_bf16, bool causal, int nwaves, hipStream_t stream) {
     if (is_bf16) {
-        return D == 64 ? launch_typed<__bf16, 64, 64>(p, causal, nwaves, stream)
+        return D == 32 ? launch_typed<__bf16, 32, 64>(p, causal, nwaves, stream)
+             : D == 64 ? launch_typed<__bf16, 64, 64>(p, causal, nwaves, stream)
                        : launch_typed<__bf16, 128, 64>(p, causal, nwaves, stream);
     }
-    return D == 64 ? launch_typed<_Float16, 64, 64>(p, causal, nwaves, stream)
+    return D == 32 ? launch_typed<_Float16, 32, 64>(p, causal, nwaves, stream)
+         : D == 64 ? launch_typed<_Float16, 64, 64>(p, causal, nwaves, stream)
                    : launch_typed<_Float16, 128, 64>(p, causal, nwaves, stream);
 }
 
-// E4M3 inputs, bf16 output, D = 64 or 128.
+// E4M3 inputs, bf16 output, D = 64 or 128 (one FP8 score MFMA spans 64 of D).
 hipError_t launch_fwd_fp8(const FwdParams& p, int D, bool causal, int nwaves, hipStream_t stream) {
     return D == 64 ? launch_typed<fp8_t, 64, 64>(p, causal, nwaves, stream)
                    : launch_typed<fp8_t, 128, 64>(p, causal, nwaves, stream);

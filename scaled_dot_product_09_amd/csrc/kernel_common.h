@@ -20,10 +20,13 @@ typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
 // Everything a forward kernel needs, passed by value as one kernel argument.
 struct FwdParams {
-    const void* q;      // [B][Sq][Hq][D]
-    const void* k;      // [B][Skv][Hkv][D]
-    const void* v;      // [B][Skv][Hkv][D]
-    void* out;          // [B][Sq][Hq][D]
+    const void* q;      // (B, Sq, Hq, D), element strides sq
+    const void* k;      // (B, Skv, Hkv, D), element strides sk
+    const void* v;      // (B, Skv, Hkv, D), element strides sv
+    void* out;          // (B, Sq, Hq, D), element strides so
+    // Element strides of the batch, sequence and head axes (D is contiguous);
+    // dense (B, S, H, D) tensors have {S H D, H D, D}.
+    int64_t sq[3], sk[3], sv[3], so[3];
     int B, Hq, Hkv, Sq, Skv;
     int G;              // query heads per KV head, Hq / Hkv
     int gpack;          // query heads of one KV head handled by one workgroup

@@ -25,7 +25,8 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "PAGE_SHAPES", "draw_normal", "make_inputs", "metric_flops", "io_bytes"]
+__all__ = ["Workload", "WORKLOADS", "PAGE_SHAPES", "draw_normal", "make_inputs", "metric_flops", "io_bytes",
+           "to_layout"]
 
 DTYPES = ("f32", "bf16", "f16", "e4m3")
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16,
@@ -48,6 +49,7 @@ class Workload:
     seed: int
     note: str = field(default="", compare=False)
     n_split: object = None  # None: attn_fwd; "auto" or an int: the split-key entry point
+    layout: str = "bshd"    # storage of q, k, v, out on the GPU: "bshd" (dense) or "bhsd" (transposed views)
 
     @property
     def scale(self):
@@ -87,6 +89,12 @@ WORKLOADS = {w.name: w for w in [
              16384 + 8, "decode: one new token per sequence, 16384-token cache, GQA", n_split="auto"),
     Workload("bf16_mqa_decode_b32_hq32_hkv1_sq4_skv8192", "bf16", 32, 32, 1, 4, 8192, 128, "bottom_right",
              8192 + 32, "decode: four new tokens per sequence, 8192-token cache, MQA", n_split="auto"),
+    # More head dimensions and layouts: head dim 32; the headline shape with
+    # q, k, v, out stored as (B, H, S, D) and handed over as strided views.
+    Workload("bf16_mha_b4_h32_s2048_d32_causal", "bf16", 4, 32, 32, 2048, 2048, 32, True, 32,
+             "head dim 32; seed 32"),
+    Workload("bf16_gqa_b2_hq32_hkv8_s4096_d128_causal_bhsd", "bf16", 2, 32, 8, 4096, 4096, 128, True, 42,
+             "headline shape, (B, H, S, D) storage, strided entry point", layout="bhsd"),
 ]}
 
 HEADLINE = "bf16_gqa_b2_hq32_hkv8_s4096_d128_causal"
@@ -132,6 +140,17 @@ def make_inputs(w, *, seed=None, shapes=None):
         return qs[0], ks[0], vs[0], (qs[1], ks[1], vs[1])
     t = [torch.from_numpy(a).to(TORCH_DTYPE[w.dtype]) for a in x]
     return t[0], t[1], t[2], (1.0, 1.0, 1.0)
+
+
+def to_layout(x, layout):
+    """A (B, S, H, D) tensor in the workload's storage: itself for "bshd"; for
+    "bhsd" a (B, S, H, D) view of dense (B, H, S, D) storage of the same
+    values (so the library sees a strided layout)."""
+    if layout == "bshd":
+        return x
+    if layout == "bhsd":
+        return x.transpose(1, 2).contiguous().transpose(1, 2)
+    raise ValueError(layout)
 
 
 def metric_flops(B, Hq, Sq, Skv, D, causal):

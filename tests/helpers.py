@@ -44,7 +44,10 @@ def out_to_f64(t):
 def gpu_run(w, q, k, v, desc, *, scale=None, causal=None, out=None, n_split=None, workspace=None):
     """Run the HIP library on CPU input tensors; returns the output tensor on the GPU."""
     dev = torch.device("cuda:0")
-    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    qd, kd, vd = (workload.to_layout(x.to(dev), w.layout) for x in (q, k, v))
+    if out is None and w.layout != "bshd":
+        out = workload.to_layout(torch.empty(q.shape, dtype=torch.bfloat16 if w.dtype == "e4m3" else q.dtype,
+                                             device=dev), w.layout)
     scale = w.scale if scale is None else scale
     causal = w.causal if causal is None else causal
     o = attn.fwd(qd, kd, vd, causal=causal, scale=scale, out=out,

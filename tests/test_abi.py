@@ -56,7 +56,7 @@ def call_fp8(q=Q, k=K, v=V, o=O, B=2, Hq=8, Hkv=2, Sq=64, Skv=64, D=128, scale=0
 @pytest.mark.parametrize("kw,status", [
     (dict(q=0), -1), (dict(k=0), -1), (dict(v=0), -1), (dict(o=0), -1),
     (dict(B=-1), -2), (dict(Sq=-1), -2), (dict(Hq=0), -2), (dict(Hkv=0), -2), (dict(D=0), -2),
-    (dict(Skv=0), -2), (dict(Hq=6, Hkv=4), -3), (dict(D=96), -4), (dict(D=32), -4),
+    (dict(Skv=0), -2), (dict(Hq=6, Hkv=4), -3), (dict(D=96), -4), (dict(D=16), -4), (dict(D=256), -4),
     (dict(dtype=attn.ATTN_FP8_E4M3), -5), (dict(dtype=7), -5), (dict(dtype=-1), -5),
     (dict(q=Q + 8), -6), (dict(o=O + 2), -6),
     (dict(o=Q), -7), (dict(o=K + 16), -7), (dict(o=V - 16), -7),
@@ -69,7 +69,7 @@ def test_rejected_before_launch(kw, status):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(q=0), -1), (dict(D=80), -4), (dict(Hq=3, Hkv=2), -3), (dict(o=Q), -7),
+    (dict(q=0), -1), (dict(D=80), -4), (dict(D=32), -4), (dict(Hq=3, Hkv=2), -3), (dict(o=Q), -7),
     (dict(dq=float("nan")), -8), (dict(dv=float("inf")), -8), (dict(scale=float("-inf")), -8),
     (dict(q=Q + 4), -6),
 ])
@@ -113,6 +113,36 @@ def test_split_workspace_size_and_suggestion():
     assert attn.attn_split_suggest(1, 3, 2, 1, 100, 128, 0) == 1     # invalid shape
 
 
+def call_strided(q=Q, k=K, v=V, o=O, B=2, Hq=8, Hkv=2, Sq=64, Skv=64, D=128, qs=None, ks=None, vs=None, os_=None,
+                 scale=0.125, causal=1, dtype=attn.ATTN_BF16):
+    dense = lambda S, H: (S * H * D, H * D, D)
+    qs = qs or dense(Sq, Hq)
+    ks = ks or dense(Skv, Hkv)
+    vs = vs or dense(Skv, Hkv)
+    os_ = os_ or dense(Sq, Hq)
+    return attn.attn_fwd_strided(q, k, v, o, B, Hq, Hkv, Sq, Skv, D, qs, ks, vs, os_, scale, causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), -1), (dict(D=80), -4), (dict(Hq=3, Hkv=2), -3), (dict(causal=4), -10),
+    (dict(dtype=attn.ATTN_FP8_E4M3), -5),
+    (dict(qs=(-8, 1024, 128)), -13), (dict(ks=(0, 1 << 41, 128)), -13),
+    (dict(qs=(8192, 1028, 128)), -6), (dict(vs=(1002, 256, 128)), -6),
+    (dict(os_=(8192, 1024, 0)), -13), (dict(os_=(8192, 64, 128)), -13),   # heads or rows collide
+    (dict(o=Q + 1024), -7), (dict(o=K), -7),
+    (dict(Skv=1 << 20, ks=(0, 1 << 14, 128)), -2),                        # one head spans >= 4 GiB
+])
+def test_strided_rejected_before_launch(kw, status):
+    assert call_strided(**kw) == status
+
+
+def test_strided_null_stride_pointer():
+    L = attn.lib()
+    st = (ctypes.c_int64 * 3)(8192, 1024, 128)
+    assert L.attn_fwd_strided(Q, K, V, O, 2, 8, 2, 64, 64, 128, None, ctypes.addressof(st), ctypes.addressof(st),
+                              ctypes.addressof(st), 0.125, 1, attn.ATTN_BF16, None) == -1
+
+
 def test_empty_problem_is_a_noop():
     # B * Sq == 0 returns success without any HIP call, whatever the other sizes.
     assert call(B=0) == 0
@@ -122,6 +152,7 @@ def test_empty_problem_is_a_noop():
     assert call_fp8(Sq=0) == 0
     assert call_split(Sq=0, ws=0) == 0
     assert call_split(n_split=1, B=0, ws=0) == 0
+    assert call_strided(Sq=0) == 0
 
 
 def test_python_wrapper_rejects_host_tensors():

@@ -86,6 +86,7 @@ SPLIT = [
     (W("bf16", 1, 8, 2, 300, 300, 128, True), (2, 4, 9)),       # top-left: upper rows see few keys
     (W("bf16", 1, 4, 1, 64, 640, 128, "bottom_right"), (10, 40)),  # more ranges than some rows have tiles
     (W("f16", 2, 8, 1, 3, 333, 64, "bottom_right"), (3, 6)),
+    (W("bf16", 2, 16, 4, 1, 2000, 32, "bottom_right"), (4, 11)),
 ]
 
 

@@ -55,6 +55,11 @@ SMALL = [
     W("bf16", 1, 8, 2, 600, 64, 128, True),       # one key tile
     W("bf16", 1, 4, 1, 700, 700, 128, True),      # G = 4, odd tile count
     W("bf16", 1, 8, 8, 1100, 1100, 128, False),   # G = 1: eight row blocks per workgroup
+    # head dim 32
+    W("bf16", 2, 8, 2, 333, 333, 32, True),
+    W("bf16", 1, 4, 4, 200, 260, 32, False),
+    W("f16", 1, 8, 1, 129, 129, 32, True),
+    W("f32", 1, 4, 2, 70, 90, 32, True),
     *workload.PAGE_SHAPES[1:],
     # f16
     W("f16", 1, 8, 2, 300, 300, 128, True),
