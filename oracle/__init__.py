@@ -22,15 +22,19 @@ where n is the codelab step:
 * §9 "Compare MHA, GQA and MQA": K/V heads are broadcast over query heads when
   there are fewer of them; GQA with 2 KV heads each serving 4 query heads.
 * §10 "TransformerEngine and FP8": E4M3 (4 exponent, 3 mantissa bits) for the
-  forward pass with per-tensor amax scaling.
+  forward pass with per-tensor amax scaling; E5M2 for the backward pass.
+* §1 also motivates the scale by the softmax's gradients: ``backward.py``
+  holds the row log-sum-exp and the chain-rule gradients dQ, dK, dV.
 
 Every function is pinned by tests in ``tests/test_oracle.py`` and
-``tests/test_codecs.py`` to facts that do not come from the oracle itself
+``tests/test_codecs.py`` (``tests/test_oracle_backward.py`` for the
+backward) to facts that do not come from the oracle itself
 (closed forms, invariants, brute force, library routines, hand-derived golden
 values). No function here is "parity unpinned".
 """
 
 from .attention import attention_weights, sdpa, sdpa_rows, sdpa_one_row, brute_sdpa, kv_head_of, query_shift
+from .backward import sdpa_lse, sdpa_backward
 from .codecs import (
     bf16_bits_to_f64,
     f16_bits_to_f64,
@@ -48,6 +52,8 @@ __all__ = [
     "brute_sdpa",
     "kv_head_of",
     "query_shift",
+    "sdpa_lse",
+    "sdpa_backward",
     "bf16_bits_to_f64",
     "f16_bits_to_f64",
     "e4m3_bits_to_f64",
