@@ -1,6 +1,6 @@
 /*
  * attn.h — C ABI of libattn.so, a fused scaled dot-product attention forward
- * pass for AMD Instinct MI355X (gfx950).
+ * pass (and its backward pass, attn_bwd) for AMD Instinct MI355X (gfx950).
  *
  * Operation. For every batch b, query head h and query row i:
  *
@@ -79,14 +79,15 @@ enum attn_status {
     ATTN_ERR_DTYPE = -5,      /* unknown dtype, or ATTN_FP8_E4M3 given to
                                  attn_fwd (FP8 needs attn_fwd_fp8's descales)   */
     ATTN_ERR_ALIGN = -6,      /* a pointer is not 16-byte aligned               */
-    ATTN_ERR_ALIAS = -7,      /* out overlaps q, k or v                         */
+    ATTN_ERR_ALIAS = -7,      /* an output (out, lse, a gradient) overlaps an
+                                 input or another output                        */
     ATTN_ERR_SCALE = -8,      /* scale or a descale is NaN or infinite          */
     ATTN_ERR_HIP = -9,        /* the kernel launch failed (hipGetLastError)     */
     ATTN_ERR_CAUSAL = -10,    /* causal is not 0, 1 or 2, or causal = 2 with
                                  Sq > Skv                                       */
     ATTN_ERR_SPLIT = -11,     /* n_split outside 1 .. ATTN_MAX_SPLIT            */
     ATTN_ERR_WORKSPACE = -12, /* workspace NULL, misaligned, too small, or
-                                 overlapping an input or the output             */
+                                 overlapping an input or an output              */
     ATTN_ERR_STRIDE = -13     /* a stride is negative or above 2^40, or out's
                                  strides map two elements to one address        */
 };
@@ -116,6 +117,28 @@ enum attn_status {
 int attn_fwd(const void* q, const void* k, const void* v, void* out,
              int B, int Hq, int Hkv, int Sq, int Skv, int D,
              float scale, int causal, int dtype, hipStream_t stream);
+
+/*
+ * attn_fwd_lse — attn_fwd that also stores, for every row, the natural-log
+ * log-sum-exp of its visible scaled scores:
+ *
+ *     lse[b,h,i] = log( sum_j exp( scale * <q[b,i,h,:], k[b,j,g,:]> ) )
+ *
+ * over the keys j the mask leaves visible. It is the normaliser of the
+ * softmax (weights = exp(score - lse)), kept so that a backward pass can
+ * rebuild the weights without another pass over the keys; the codelab's §1
+ * motivates the scale by the softmax's gradients.
+ *
+ *   lse      device pointer to float32 [B][Hq][Sq], 4-byte aligned, not
+ *            overlapping q, k, v or out
+ *   dtype    ATTN_F32, ATTN_BF16 or ATTN_F16
+ *
+ * Other arguments and errors as attn_fwd (ATTN_ERR_NULL for a NULL lse).
+ * The output equals attn_fwd's bit for bit.
+ */
+int attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* lse,
+                 int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                 float scale, int causal, int dtype, hipStream_t stream);
 
 /*
  * attn_fwd_fp8 — the same operation on E4M3 inputs, bfloat16 output.
@@ -195,6 +218,56 @@ int attn_fwd_strided(const void* q, const void* k, const void* v, void* out,
                      const int64_t* q_strides, const int64_t* k_strides,
                      const int64_t* v_strides, const int64_t* out_strides,
                      float scale, int causal, int dtype, hipStream_t stream);
+
+/*
+ * attn_bwd — gradients of the forward pass: with L = sum(dout * out) for
+ * out = attn_fwd(q, k, v) (same scale, causal mask and head grouping),
+ *
+ *     dq = dL/dq,  dk = dL/dk,  dv = dL/dv.
+ *
+ * The codelab's §1 motivates the scale by the softmax's gradients, which
+ * vanish when the scores saturate it. Writing S = scale q k^T (masked
+ * entries -inf), P = softmax(S) = exp(S - lse), dP = dout v^T and
+ * Delta_i = rowsum(dout_i * out_i) (equal to rowsum(P_i * dP_i)):
+ *
+ *     dS = P * (dP - Delta),  dv = P^T dout,  dk = scale dS^T q,  dq = scale dS k,
+ *
+ * with dk and dv of a K/V head summed over the query heads that share it
+ * (§9). Products run on matrix cores in the input type with float32
+ * accumulation; P and dS enter them rounded to the input type; the
+ * gradients are rounded once at the end. The result is deterministic (no
+ * atomics).
+ *
+ *   q, k, v   the forward's inputs (device, layout above)
+ *   out       the forward's output, [B][Sq][Hq][D]
+ *   dout      gradient of the loss with respect to out, [B][Sq][Hq][D]
+ *   lse       the forward's row log-sum-exp from attn_fwd_lse, float32
+ *             [B][Hq][Sq], 4-byte aligned
+ *   dq        output, [B][Sq][Hq][D]
+ *   dk, dv    outputs, [B][Skv][Hkv][D] (written in full: keys no query
+ *             sees get 0)
+ *   dtype     ATTN_BF16 or ATTN_F16 (every tensor above but lse)
+ *   workspace device buffer of at least attn_bwd_workspace(B, Hq, Sq)
+ *             bytes, 16-byte aligned; holds Delta between the two kernels;
+ *             contents on entry do not matter
+ *   workspace_bytes  its size
+ *
+ * The outputs and the workspace must not overlap an input or each other
+ * (ATTN_ERR_ALIAS; ATTN_ERR_WORKSPACE for the workspace). Other arguments
+ * and errors as attn_fwd. B * (Sq + Skv) == 0 is a no-op; Sq == 0 with
+ * Skv > 0 writes zero dk and dv. Pointers to empty tensors may be NULL (q,
+ * out, dout, lse, dq when B * Sq == 0; k, v, dk, dv when B * Skv == 0).
+ * Two kernels are enqueued on `stream`.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv,
+             int B, int Hq, int Hkv, int Sq, int Skv, int D,
+             float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
+             hipStream_t stream);
+
+/* attn_bwd_workspace — bytes of workspace attn_bwd needs: B * Hq * Sq * 4
+ * (one float32 Delta per query row); 0 for an empty problem. */
+size_t attn_bwd_workspace(int B, int Hq, int Sq);
 
 /* attn_strerror — a static, human-readable description of a status code. */
 const char* attn_strerror(int status);

@@ -7,10 +7,11 @@ exceptions. torch provides device memory and streams, nothing else. There is
 no fallback: if the library is missing or a call is rejected, an exception is
 raised.
 
-The names follow include/attn.h: ``attn_fwd``, ``attn_fwd_fp8``,
+The names follow include/attn.h: ``attn_fwd``, ``attn_fwd_lse``, ``attn_fwd_fp8``,
 ``attn_fwd_split``, ``attn_split_workspace``, ``attn_split_suggest``,
-``attn_fwd_strided``, ``attn_strerror``; :func:`fwd` is the tensor-level
-convenience wrapper.
+``attn_fwd_strided``, ``attn_bwd``, ``attn_bwd_workspace``,
+``attn_strerror``; :func:`fwd`, :func:`fwd_lse` and :func:`bwd` are the
+tensor-level convenience wrappers.
 """
 
 import ctypes
@@ -29,8 +30,8 @@ STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR
           -4: "ATTN_ERR_HEAD_DIM", -5: "ATTN_ERR_DTYPE", -6: "ATTN_ERR_ALIGN", -7: "ATTN_ERR_ALIAS",
           -8: "ATTN_ERR_SCALE", -9: "ATTN_ERR_HIP", -10: "ATTN_ERR_CAUSAL", -11: "ATTN_ERR_SPLIT",
           -12: "ATTN_ERR_WORKSPACE", -13: "ATTN_ERR_STRIDE"}
-EXPORTS = ("attn_fwd", "attn_fwd_fp8", "attn_fwd_split", "attn_split_workspace", "attn_split_suggest",
-           "attn_fwd_strided", "attn_strerror")
+EXPORTS = ("attn_fwd", "attn_fwd_lse", "attn_fwd_fp8", "attn_fwd_split", "attn_split_workspace", "attn_split_suggest",
+           "attn_fwd_strided", "attn_bwd", "attn_bwd_workspace", "attn_strerror")
 # causal argument: 0 none, 1 lower triangle (top-left), 2 bottom-right (Sq <= Skv)
 CAUSAL_CODE = {False: 0, True: 1, "top_left": 1, "bottom_right": 2, 0: 0, 1: 1, 2: 2}
 
@@ -53,6 +54,8 @@ def lib():
         vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         L.attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
         L.attn_fwd.restype = i
+        L.attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+        L.attn_fwd_lse.restype = i
         L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, f, f, f, vp]
         L.attn_fwd_fp8.restype = i
         L.attn_fwd_split.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, ctypes.c_size_t, vp]
@@ -63,6 +66,10 @@ def lib():
         L.attn_split_suggest.restype = i
         L.attn_fwd_strided.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, vp, vp, f, i, i, vp]
         L.attn_fwd_strided.restype = i
+        L.attn_bwd.argtypes = [vp] * 9 + [i, i, i, i, i, i, f, i, i, vp, ctypes.c_size_t, vp]
+        L.attn_bwd.restype = i
+        L.attn_bwd_workspace.argtypes = [i, i, i]
+        L.attn_bwd_workspace.restype = ctypes.c_size_t
         L.attn_strerror.argtypes = [i]
         L.attn_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -76,6 +83,12 @@ def attn_strerror(status):
 def attn_fwd(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype, stream):
     """Raw C call: pointers as ints, returns the status code."""
     return lib().attn_fwd(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, float(scale), int(causal), int(dtype), stream)
+
+
+def attn_fwd_lse(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype, stream):
+    """Raw C call of the forward with the row log-sum-exp output, returns the status code."""
+    return lib().attn_fwd_lse(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, float(scale), int(causal), int(dtype),
+                              stream)
 
 
 def attn_fwd_fp8(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, scale, causal, q_descale, k_descale, v_descale, stream):
@@ -107,9 +120,66 @@ def attn_fwd_strided(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, q_strides, k_strides,
                                   float(scale), int(causal), int(dtype), stream)
 
 
+def attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype, workspace,
+             workspace_bytes, stream):
+    """Raw C call of the backward pass, returns the status code."""
+    return lib().attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, float(scale), int(causal),
+                          int(dtype), workspace, int(workspace_bytes), stream)
+
+
+def attn_bwd_workspace(B, Hq, Sq):
+    return int(lib().attn_bwd_workspace(B, Hq, Sq))
+
+
 def _check(st):
     if st != 0:
         raise AttnError(st, attn_strerror(st))
+
+
+def _check_qkv(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4:
+            raise ValueError(f"{name} must be a 4-D torch tensor (B, S, H, D)")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in DTYPE_CODE:
+        raise ValueError(f"unsupported or mixed dtypes {q.dtype}, {k.dtype}, {v.dtype}")
+    if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
+        raise ValueError(f"shape mismatch q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+
+
+def _causal_code(causal):
+    if causal not in CAUSAL_CODE:
+        raise ValueError(f"causal must be one of {sorted(map(str, CAUSAL_CODE))}")
+    return CAUSAL_CODE[causal]
+
+
+def fwd_lse(q, k, v, *, causal=False, scale=None, out=None, lse=None, stream=None):
+    """(out, lse): the forward of :func:`fwd` plus the float32 row log-sum-exp
+    lse[b, h, i] = log sum_j exp(scale q.k) over the visible keys, shape
+    (B, Hq, Sq). Contiguous float32 / bfloat16 / float16 tensors."""
+    _check_qkv(q, k, v)
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("fwd_lse takes contiguous (B, S, H, D) tensors")
+    if q.dtype == torch.float8_e4m3fn:
+        raise ValueError("fwd_lse takes float32, bfloat16 or float16")
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    causal = _causal_code(causal)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of q's shape, dtype and device")
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    elif lse.shape != (B, Hq, Sq) or lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (B, Hq, Sq) tensor on q's device")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(attn_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                        B, Hq, Hkv, Sq, Skv, D, scale, causal, DTYPE_CODE[q.dtype], stream))
+    return out, lse
 
 
 def fwd(q, k, v, *, causal=False, scale=None, out=None, descales=None, stream=None, n_split=None,
@@ -131,23 +201,14 @@ def fwd(q, k, v, *, causal=False, scale=None, out=None, descales=None, stream=No
     kernels are enqueued on ``stream`` (default: torch's current stream);
     nothing is synchronised.
     """
+    _check_qkv(q, k, v)
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if not isinstance(t, torch.Tensor) or t.dim() != 4:
-            raise ValueError(f"{name} must be a 4-D torch tensor (B, S, H, D)")
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be on the GPU")
         if t.stride(3) != 1:
             raise ValueError(f"{name}'s last (head-dimension) axis must be contiguous")
     dense = q.is_contiguous() and k.is_contiguous() and v.is_contiguous()
-    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in DTYPE_CODE:
-        raise ValueError(f"unsupported or mixed dtypes {q.dtype}, {k.dtype}, {v.dtype}")
-    if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
-        raise ValueError(f"shape mismatch q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
     B, Sq, Hq, D = q.shape
     Skv, Hkv = k.shape[1], k.shape[2]
-    if causal not in CAUSAL_CODE:
-        raise ValueError(f"causal must be one of {sorted(map(str, CAUSAL_CODE))}")
-    causal = CAUSAL_CODE[causal]
+    causal = _causal_code(causal)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     code = DTYPE_CODE[q.dtype]
@@ -191,3 +252,48 @@ def fwd(q, k, v, *, causal=False, scale=None, out=None, descales=None, stream=No
                       scale, causal, code, stream)
     _check(st)
     return out
+
+
+def bwd(q, k, v, out, dout, lse, *, causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None,
+        stream=None):
+    """(dq, dk, dv): gradients of sum(dout * out) for out = fwd(q, k, v).
+
+    ``out`` and ``lse`` come from :func:`fwd_lse` on the same inputs with the
+    same ``causal`` and ``scale``; ``dout`` has out's shape. Contiguous
+    bfloat16 / float16 tensors on one GPU; the gradients have the inputs'
+    shapes and dtype. ``workspace`` is a uint8 device tensor of at least
+    attn_bwd_workspace(B, Hq, Sq) bytes (allocated here if None).
+    """
+    _check_qkv(q, k, v)
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("the backward pass takes bfloat16 or float16 tensors")
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout), ("lse", lse)):
+        if not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be contiguous and on q's device")
+    if out.shape != q.shape or dout.shape != q.shape or out.dtype != q.dtype or dout.dtype != q.dtype:
+        raise ValueError("out and dout must have q's shape and dtype")
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    if lse.shape != (B, Hq, Sq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a float32 (B, Hq, Sq) tensor")
+    causal = _causal_code(causal)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    grads = []
+    for name, g, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if g is None:
+            g = torch.empty_like(ref)
+        elif g.shape != ref.shape or g.dtype != ref.dtype or g.device != ref.device or not g.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor of its input's shape, dtype and device")
+        grads.append(g)
+    need = attn_bwd_workspace(B, Hq, Sq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    elif workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != q.device:
+        raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    dq, dk, dv = grads
+    _check(attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Sq, Skv, D, scale, causal,
+                    DTYPE_CODE[q.dtype], workspace.data_ptr(), workspace.numel(), stream))
+    return dq, dk, dv

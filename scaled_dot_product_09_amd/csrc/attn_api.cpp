@@ -20,6 +20,7 @@ hipError_t launch_fwd_fp8(const FwdParams& p, int D, bool causal, int nwaves, hi
 hipError_t launch_fwd_rb2(const FwdParams& p, int D, int dtype, bool causal, hipStream_t stream);
 hipError_t launch_fwd_pp(const FwdParams& p, int D, int dtype, bool causal, hipStream_t stream);
 hipError_t launch_combine(const FwdParams& p, int D, bool is_bf16, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& bp, int D, bool is_bf16, bool causal, hipStream_t stream);
 }
 
 namespace {
@@ -68,6 +69,7 @@ attn::FwdParams make_params(const void* q, const void* k, const void* v, void* o
     p.n_split = 1;
     p.part_o = nullptr;
     p.part_ml = nullptr;
+    p.lse = nullptr;
     p.q = q; p.k = k; p.v = v; p.out = out;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Sq = Sq; p.Skv = Skv;
     p.G = Hq / Hkv;
@@ -145,10 +147,11 @@ MfmaKernel mfma_kernel() {
 // strides: NULL (dense) or q, k, v, out element strides (batch, seq, head).
 hipError_t launch_mfma(const void* q, const void* k, const void* v, void* out,
                        int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale_log2,
-                       float out_mul, int dtype, int causal, const int64_t* strides, hipStream_t stream) {
-    // Head dimension 32 and strided layouts exist only in the four- and
-    // eight-wave kernel.
-    const bool four_or_eight = D == 32 || strides;
+                       float out_mul, int dtype, int causal, const int64_t* strides, hipStream_t stream,
+                       float* lse = nullptr) {
+    // Head dimension 32, strided layouts and the log-sum-exp output exist
+    // only in the four- and eight-wave kernel.
+    const bool four_or_eight = D == 32 || strides || lse;
     const MfmaKernel kern = (four_or_eight && (mfma_kernel() == kPingPong || mfma_kernel() == kRows64))
                                 ? kFourWave : mfma_kernel();
     const int rpw = kern == kRows64 ? 64 : 32;
@@ -163,6 +166,7 @@ hipError_t launch_mfma(const void* q, const void* k, const void* v, void* out,
     } else {
         set_dense_strides(p, D);
     }
+    p.lse = lse;
     const bool masked = causal != 0;
     switch (kern) {
         case kRows64: return attn::launch_fwd_rb2(p, D, dtype, masked, stream);
@@ -205,6 +209,39 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out,
     } else {
         e = launch_mfma(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, nonzero_multiplier(scale * kLog2e), 1.0f,
                         dtype, causal, nullptr, stream);
+    }
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+extern "C" int attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* lse,
+                            int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                            float scale, int causal, int dtype, hipStream_t stream) {
+    int eb;
+    switch (dtype) {
+        case ATTN_F32: eb = 4; break;
+        case ATTN_BF16: case ATTN_F16: eb = 2; break;
+        default: return ATTN_ERR_DTYPE;
+    }
+    if (!lse) return ATTN_ERR_NULL;
+    bool noop;
+    const int st = validate(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, scale, causal, eb, eb, &noop);
+    if (st != ATTN_OK || noop) return st;
+    if ((uintptr_t)lse & 3) return ATTN_ERR_ALIGN;
+    const int64_t nl = (int64_t)B * Hq * Sq * 4;
+    const int64_t nq = (int64_t)B * Sq * Hq * D * eb, nk = (int64_t)B * Skv * Hkv * D * eb;
+    if (ranges_overlap(lse, nl, q, nq) || ranges_overlap(lse, nl, k, nk) || ranges_overlap(lse, nl, v, nk) ||
+        ranges_overlap(lse, nl, out, nq))
+        return ATTN_ERR_ALIAS;
+    hipError_t e;
+    if (dtype == ATTN_F32) {
+        attn::FwdParams p = make_params(q, k, v, out, B, Hq, Hkv, Sq, Skv,
+                                        nonzero_multiplier(scale * kLog2e), 1.0f, causal, false, 32, 4);
+        set_dense_strides(p, D);
+        p.lse = lse;
+        e = attn::launch_fwd_f32(p, D, causal != 0, stream);
+    } else {
+        e = launch_mfma(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, nonzero_multiplier(scale * kLog2e), 1.0f,
+                        dtype, causal, nullptr, stream, lse);
     }
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
@@ -360,6 +397,72 @@ extern "C" int attn_fwd_strided(const void* q, const void* k, const void* v, voi
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+extern "C" size_t attn_bwd_workspace(int B, int Hq, int Sq) {
+    if (B <= 0 || Hq <= 0 || Sq <= 0) return 0;
+    return (size_t)B * Hq * Sq * sizeof(float);
+}
+
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv,
+                        int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                        float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+    if (dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_DTYPE;
+    if (B < 0 || Sq < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Skv < 0) return ATTN_ERR_SHAPE;
+    // Pointers of empty tensors may be NULL (the query side when B * Sq == 0,
+    // the key side when B * Skv == 0).
+    if ((int64_t)B * Sq > 0 && (!q || !out || !dout || !lse || !dq)) return ATTN_ERR_NULL;
+    if ((int64_t)B * Skv > 0 && (!k || !v || !dk || !dv)) return ATTN_ERR_NULL;
+    if (Hq % Hkv != 0) return ATTN_ERR_GROUP;
+    if (D != 32 && D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+    if (!isfinite(scale)) return ATTN_ERR_SCALE;
+    if (causal < 0 || causal > 2) return ATTN_ERR_CAUSAL;
+    if ((int64_t)B * Sq > 0 && Skv < 1) return ATTN_ERR_SHAPE;
+    if (causal == 2 && Sq > Skv) return ATTN_ERR_CAUSAL;
+    const int64_t nq = (int64_t)B * Sq * Hq * D, nk = (int64_t)B * Skv * Hkv * D;
+    if (nq >= kMaxElems || nk >= kMaxElems) return ATTN_ERR_SHAPE;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)dout | (uintptr_t)dq |
+         (uintptr_t)dk | (uintptr_t)dv) & 15)
+        return ATTN_ERR_ALIGN;
+    if ((uintptr_t)lse & 3) return ATTN_ERR_ALIGN;
+    if ((int64_t)B * (Sq + Skv) == 0) return ATTN_OK;   // nothing to write
+    const size_t need = attn_bwd_workspace(B, Hq, Sq);
+    if (need > 0 && (!workspace || ((uintptr_t)workspace & 15) || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+    // Outputs (dq, dk, dv, workspace) must not overlap inputs or each other.
+    const int64_t nl = (int64_t)B * Hq * Sq * 4;
+    const void* in_p[6] = {q, k, v, out, dout, lse};
+    const int64_t in_n[6] = {nq * 2, nk * 2, nk * 2, nq * 2, nq * 2, nl};
+    void* out_p[3] = {dq, dk, dv};
+    const int64_t out_n[3] = {nq * 2, nk * 2, nk * 2};
+    for (int o = 0; o < 3; ++o) {
+        for (int i = 0; i < 6; ++i)
+            if (ranges_overlap(out_p[o], out_n[o], in_p[i], in_n[i])) return ATTN_ERR_ALIAS;
+        for (int o2 = o + 1; o2 < 3; ++o2)
+            if (ranges_overlap(out_p[o], out_n[o], out_p[o2], out_n[o2])) return ATTN_ERR_ALIAS;
+        if (ranges_overlap(out_p[o], out_n[o], workspace, (int64_t)need)) return ATTN_ERR_WORKSPACE;
+    }
+    for (int i = 0; i < 6; ++i)
+        if (ranges_overlap(workspace, (int64_t)need, in_p[i], in_n[i])) return ATTN_ERR_WORKSPACE;
+    attn::BwdParams bp;
+    bp.f = make_params(q, k, v, (void*)out, B, Hq, Hkv, Sq > 0 ? Sq : 1, Skv, scale * kLog2e, 1.0f,
+                       causal, true, 32, 4, true);
+    set_dense_strides(bp.f, D);
+    if (Sq == 0) {   // no query rows: dK = dV = 0, the dQ kernel has nothing to do
+        bp.f.Sq = 0;
+        bp.f.n_row_blocks = 0;
+    }
+    bp.dout = dout;
+    bp.lse = lse;
+    bp.delta = (float*)workspace;
+    bp.dq = dq;
+    bp.dk = dk;
+    bp.dv = dv;
+    bp.scale = scale;
+    bp.n_kblocks = (Skv + 127) / 128;
+    const hipError_t e = attn::launch_bwd(bp, D, dtype == ATTN_BF16, causal != 0, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 extern "C" const char* attn_strerror(int status) {
     switch (status) {
         case ATTN_OK: return "success";
@@ -367,15 +470,15 @@ extern "C" const char* attn_strerror(int status) {
         case ATTN_ERR_SHAPE: return "invalid shape (B, Sq >= 0; Hq, Hkv, D > 0; Skv >= 1 unless B*Sq == 0; < 2^31 elements per tensor)";
         case ATTN_ERR_GROUP: return "Hq is not a multiple of Hkv";
         case ATTN_ERR_HEAD_DIM: return "head dimension D must be 32, 64 or 128 (64 or 128 for E4M3 inputs)";
-        case ATTN_ERR_DTYPE: return "unsupported dtype (attn_fwd takes F32, BF16, F16; E4M3 goes through attn_fwd_fp8)";
+        case ATTN_ERR_DTYPE: return "unsupported dtype (attn_fwd takes F32, BF16, F16; E4M3 goes through attn_fwd_fp8; the split and backward entry points take BF16, F16)";
         case ATTN_ERR_ALIGN: return "q, k, v and out must be 16-byte aligned";
-        case ATTN_ERR_ALIAS: return "out overlaps an input";
+        case ATTN_ERR_ALIAS: return "an output (out, lse or a gradient) overlaps an input or another output";
         case ATTN_ERR_SCALE: return "scale or a descale is not finite";
         case ATTN_ERR_HIP: return "HIP kernel launch failed";
         case ATTN_ERR_CAUSAL: return "causal must be 0, 1 or 2 (2, bottom-right alignment, needs Sq <= Skv)";
         case ATTN_ERR_SPLIT: return "n_split must be between 1 and ATTN_MAX_SPLIT";
         case ATTN_ERR_STRIDE: return "a stride is negative or too large, or out's strides make two elements share memory";
-        case ATTN_ERR_WORKSPACE: return "workspace is NULL, not 16-byte aligned, smaller than attn_split_workspace(), or overlaps an input or the output";
+        case ATTN_ERR_WORKSPACE: return "workspace is NULL, not 16-byte aligned, smaller than the size function returns (attn_split_workspace / attn_bwd_workspace), or overlaps an input or an output";
         default: return "unknown status";
     }
 }

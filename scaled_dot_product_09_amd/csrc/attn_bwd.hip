@@ -1,0 +1,451 @@
+// attn_bwd.hip — backward pass of the fused attention on gfx950 matrix cores.
+//
+// Gradients of out = softmax(scale * Q K^T [+ causal mask]) V (codelab
+// "Accelerate attention on GPU with cuDNN and TransformerEngine", §1: the
+// formula, and the scale that keeps the softmax's gradients from vanishing;
+// §7 mask; §9 head grouping). With the weights rebuilt from the forward's
+// row log-sum-exp, P = exp(S - lse), and Delta_i = rowsum(dO_i * O_i), which
+// equals rowsum(P_i * dP_i):
+//
+//     dP = dO V^T,  dS = P * (dP - Delta),  dV = P^T dO,
+//     dK = scale dS^T Q,  dQ = scale dS K
+//
+// (dK and dV of a KV head summed over the query heads of its group).
+//
+// Two kernels, no atomics, deterministic:
+//   * bwd_dq_kernel: the forward's workgroup map (32 query rows per wave),
+//     looping over 64-key tiles staged in LDS: S^T = K Q^T, dP^T = V dO^T,
+//     dS^T, and dQ^T += K^T dS^T, with the dS^T accumulator used directly as
+//     the second operand (the K^T operand is gathered in the same key order
+//     by the LDS transpose read). It also forms Delta for its rows and
+//     stores it for the second kernel.
+//   * bwd_dkdv_kernel: one workgroup per 128 keys of one KV head (32 keys
+//     per wave, K and V operands held in registers), looping over the query
+//     heads of the group and 32-row query steps staged in LDS: S = Q K^T,
+//     dP = dO V^T, dS, then dV += P^T dO and dK += dS^T Q with P^T and dS^T
+//     taken straight from the accumulators.
+// S and dP are thus computed twice, 7 matrix products instead of 5. The
+// alternative, one kernel adding dQ into an fp32 buffer with atomics, moves
+// Sq * D * 4 bytes per 128 keys through the atomic units; measured on
+// MI355X they sustain about 1.4 TB/s in that pattern, which at S = 4096
+// would take about three times as long as all the products.
+
+#include "mfma_common.h"
+
+namespace attn {
+
+namespace {
+
+constexpr float kLog2eF = 1.4426950408889634f;
+
+template <typename T>
+__device__ inline float dot2(uint32_t a, uint32_t b, float c) {
+    if constexpr (std::is_same_v<T, __bf16>)
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+    else
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+}
+
+template <typename T>
+__device__ inline T round_to(float x) { return (T)x; }
+
+// Transpose read of 16 keys (rows base + 4h + {0..3} and base + 8 + 4h +
+// {0..3}) of one 32-column block: the operand layout that pairs with an
+// accumulator used as the other operand (see the forward kernel).
+template <typename frag>
+__device__ inline frag tr_read(const uint8_t* base, uint32_t off_lo, uint32_t off_hi) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base + off_lo));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base + off_hi));
+    return __builtin_bit_cast(frag, (s16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// dQ (and Delta): one workgroup = 4 waves x 32 query slots, the forward's map.
+// ---------------------------------------------------------------------------
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams bp) {
+    using Tr = Traits<T>;
+    using frag = typename Tr::qk_frag;
+    const FwdParams& p = bp.f;
+    constexpr int ROWB = D * 2;             // bytes of one row of K, V, Q, dO
+    constexpr int NC = ROWB / 16;           // 16-byte chunks per row
+    constexpr int KSTEPS = D / 16;          // k-steps of S^T and dP^T
+    constexpr int BN = 64;                  // keys per tile
+    constexpr int NKB = BN / 32, NDB = D / 32;
+    constexpr int TILE = BN * ROWB;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_k0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_k1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_v0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_v1[TILE];
+
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, n = lane & 31;
+
+    const WorkItem wi = map_workgroup(p, CAUSAL);
+    const int HS = p.head_stride;
+    const int slot = wave * 32 + n;
+    const int hq = wi.hq0 + (slot / HS) % p.gpack;
+    const int qrow = wi.row_base + (slot / (HS * p.gpack)) * HS + slot % HS;
+    const bool wave_idle =
+        __builtin_amdgcn_readfirstlane(wi.row_base + (wave * 32 / (HS * p.gpack)) * HS) >= p.Sq;
+    const int Sq = p.Sq, Skv = p.Skv;
+    const bool row_ok = qrow < Sq;
+
+    // This lane's query row: Q^T and dO^T operands (16 bytes per k-step,
+    // chunk 2 ks + h) and its part of Delta = dO . O.
+    const size_t roff = (size_t)wi.b * p.sq[0] + (size_t)qrow * p.sq[1] + (size_t)hq * p.sq[2];
+    frag qf[KSTEPS], gf[KSTEPS];
+    float dsum = 0.f;
+    {
+        const uint8_t* qsrc = (const uint8_t*)((const T*)p.q + roff);
+        const uint8_t* gsrc = (const uint8_t*)((const T*)bp.dout + roff);
+        const uint8_t* osrc = (const uint8_t*)((const T*)p.out + roff);
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            u32x4 xq = {0, 0, 0, 0}, xg = {0, 0, 0, 0}, xo = {0, 0, 0, 0};
+            if (row_ok) {
+                const int off = (2 * ks + h) * 16;
+                xq = *(const u32x4*)(qsrc + off);
+                xg = *(const u32x4*)(gsrc + off);
+                xo = *(const u32x4*)(osrc + off);
+            }
+            qf[ks] = __builtin_bit_cast(frag, xq);
+            gf[ks] = __builtin_bit_cast(frag, xg);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dsum = dot2<T>(xg[e], xo[e], dsum);
+        }
+    }
+    const float delta = xor32_sum(dsum);
+    const size_t srow = ((size_t)wi.b * p.Hq + hq) * Sq + qrow;
+    if (row_ok && h == 0) bp.delta[srow] = delta;
+    const float lse2 = row_ok ? bp.lse[srow] * kLog2eF : 0.f;
+    const float c2 = p.scale_log2;            // scale * log2(e), any sign
+    const int coff = p.causal_off;
+
+    int n_tiles = (Skv + BN - 1) / BN;
+    if (CAUSAL) {
+        const int last_row = min(wi.row_base + p.rows_per_wg, Sq) - 1 + coff;
+        n_tiles = min(n_tiles, last_row / BN + 1);
+    }
+    n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
+
+    const uint8_t* kbase = (const uint8_t*)((const T*)p.k + wi.b * p.sk[0] + wi.hkv * p.sk[2]);
+    const uint8_t* vbase = (const uint8_t*)((const T*)p.v + wi.b * p.sv[0] + wi.hkv * p.sv[2]);
+    TileDma<ROWB, BN, 4> kdma, vdma;
+    kdma.init(kbase, (uint32_t)(p.sk[1] * 2), wave, lane, kSwzKV);   // read as rows and transposed
+    vdma.init(vbase, (uint32_t)(p.sv[1] * 2), wave, lane, kSwzK);    // read as rows
+
+    // Row reads (first operand of S^T = K Q^T and dP^T = V dO^T): lane (h, n)
+    // reads row 32 kb + n, chunk 2 ks + h; the k-step only flips chunk bits
+    // above h, so the offset is a lane base XOR (ks << 5).
+    const uint32_t krd = n * ROWB + ((h ^ kv_swz<NC>(n)) << 4);
+    const uint32_t vrd = n * ROWB + ((h ^ k_swz<NC>(n)) << 4);
+    // Transpose reads of K (first operand of dQ^T = K^T dS^T): lane L of a
+    // 16-lane group addresses row 4h + L / 4 (and that + 8) at byte
+    // 64 db + 32 G16 + 8 (L % 4) of the row.
+    const int L16 = lane & 15, G16 = (lane >> 4) & 1;
+    const int rlo = 4 * h + (L16 >> 2), rhi = rlo + 8;
+    uint32_t tlo[NDB], thi[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        const int cb = db * 64 + 32 * G16 + 8 * (L16 & 3);
+        tlo[db] = rlo * ROWB + ((((cb >> 4) ^ kv_swz<NC>(rlo)) << 4) | (cb & 15));
+        thi[db] = rhi * ROWB + ((((cb >> 4) ^ kv_swz<NC>(rhi)) << 4) | (cb & 15));
+    }
+
+    f32x16 dq[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dq[db][i] = 0.f;
+
+    kdma.issue(0, Skv, lds_k0, wave);
+    vdma.issue(0, Skv, lds_v0, wave);
+    for (int j = 0; j < n_tiles; ++j) {
+        const uint8_t* kt = (j & 1) ? lds_k1 : lds_k0;
+        const uint8_t* vt = (j & 1) ? lds_v1 : lds_v0;
+        dma_barrier();   // tile j has landed; every wave is done with tile j - 1
+        if (j + 1 < n_tiles) {
+            kdma.issue((j + 1) * BN, Skv, (j & 1) ? lds_k0 : lds_k1, wave);
+            vdma.issue((j + 1) * BN, Skv, (j & 1) ? lds_v0 : lds_v1, wave);
+        }
+        if (wave_idle) continue;
+        f32x16 s[NKB], dp[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) { s[kb][i] = 0.f; dp[kb][i] = 0.f; }
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const frag ka = __builtin_bit_cast(frag, *(const u32x4*)(kt + kb * 32 * ROWB + (krd ^ (ks << 5))));
+                const frag va = __builtin_bit_cast(frag, *(const u32x4*)(vt + kb * 32 * ROWB + (vrd ^ (ks << 5))));
+                s[kb] = Tr::qk(ka, qf[ks], s[kb]);
+                dp[kb] = Tr::qk(va, gf[ks], dp[kb]);
+            }
+        }
+        // dS^T = P^T (dP^T - Delta), P^T = 2^(c2 s - lse2) on visible keys,
+        // rounded to the input type in pairs of consecutive keys.
+        uint32_t pw[NKB][8];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            const int key0 = j * BN + kb * 32 + 4 * h;        // key of element i: key0 + 8 (i / 4) + i % 4
+            int lim = Skv - 1 - key0;
+            if (CAUSAL) lim = min(lim, qrow + coff - key0);
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) {
+                const int ko = 8 * (i >> 2) + (i & 3);
+                const float p0 = ko <= lim ? __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -lse2)) : 0.f;
+                const float p1 = ko + 1 <= lim ? __builtin_amdgcn_exp2f(fmaf(s[kb][i + 1], c2, -lse2)) : 0.f;
+                pw[kb][i / 2] = Tr::pack(p0 * (dp[kb][i] - delta), p1 * (dp[kb][i + 1] - delta));
+            }
+        }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const frag sf = __builtin_bit_cast(frag, (u32x4){pw[kb][4 * s2], pw[kb][4 * s2 + 1],
+                                                                 pw[kb][4 * s2 + 2], pw[kb][4 * s2 + 3]});
+                const uint8_t* base = kt + (kb * 32 + 16 * s2) * ROWB;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    dq[db] = Tr::qk(tr_read<frag>(base, tlo[db], thi[db]), sf, dq[db]);
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // no copy may still be in flight when the workgroup ends
+
+    if (row_ok) {
+        const float sc = bp.scale;
+        T* dst = (T*)bp.dq + roff;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int d0 = db * 32 + 8 * jj + 4 * h;
+                const uint32_t w0 = Tr::pack(dq[db][4 * jj] * sc, dq[db][4 * jj + 1] * sc);
+                const uint32_t w1 = Tr::pack(dq[db][4 * jj + 2] * sc, dq[db][4 * jj + 3] * sc);
+                *(u32x2*)(dst + d0) = (u32x2){w0, w1};
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup = 128 keys of one KV head, 32 per wave.
+// ---------------------------------------------------------------------------
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams bp) {
+    using Tr = Traits<T>;
+    using frag = typename Tr::qk_frag;
+    const FwdParams& p = bp.f;
+    constexpr int ROWB = D * 2, NC = ROWB / 16, KSTEPS = D / 16, NDB = D / 32;
+    constexpr int BM = 32;                             // query rows per step
+    constexpr int TILE = BM * ROWB;
+    constexpr int NWQ = TILE / 1024 >= 4 ? 4 : TILE / 1024;   // waves copying a Q / dO tile
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_q0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_q1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_g0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_g1[TILE];
+    __shared__ __attribute__((aligned(16))) float lds_lse[2][BM];
+    __shared__ __attribute__((aligned(16))) float lds_del[2][BM];
+
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, n = lane & 31;
+
+    // Key blocks are the fastest index: with a causal mask the first blocks
+    // see the most query rows, and they go out first.
+    int id = (int)__builtin_amdgcn_workgroup_id_x();
+    const int kblk = id % bp.n_kblocks;
+    id /= bp.n_kblocks;
+    const int hkv = id % p.Hkv, b = id / p.Hkv;
+    const int Sq = p.Sq, Skv = p.Skv, G = p.G;
+    const int kw0 = kblk * 128 + 32 * wave;            // this wave's first key
+    const int key = kw0 + n;                           // the key of lane column n
+
+    // K and V as second operands of S = Q K^T and dP = dO V^T: lane (h, n)
+    // holds 16 bytes (chunk 2 ks + h) of key n, for the whole kernel.
+    frag kf[KSTEPS], vf[KSTEPS];
+    {
+        const int kr = min(key, Skv - 1);
+        const uint8_t* ksrc = (const uint8_t*)((const T*)p.k + b * p.sk[0] + (size_t)kr * p.sk[1] + hkv * p.sk[2]);
+        const uint8_t* vsrc = (const uint8_t*)((const T*)p.v + b * p.sv[0] + (size_t)kr * p.sv[1] + hkv * p.sv[2]);
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            kf[ks] = __builtin_bit_cast(frag, *(const u32x4*)(ksrc + (2 * ks + h) * 16));
+            vf[ks] = __builtin_bit_cast(frag, *(const u32x4*)(vsrc + (2 * ks + h) * 16));
+        }
+    }
+
+    const int coff = p.causal_off;
+    const float c2 = p.scale_log2;
+    const int n_qs = (Sq + BM - 1) / BM;
+    // First query step holding a row that sees a key of this block.
+    const int qs0 = CAUSAL ? min(n_qs, max(0, kblk * 128 - coff) / BM) : 0;
+    const int per_head = n_qs - qs0;
+    const int n_steps = G * per_head;
+
+    TileDma<ROWB, BM, NWQ> qdma, gdma;
+    const uint32_t qrow_b = (uint32_t)(p.sq[1] * 2);
+    auto issue_step = [&](int t, uint8_t* qt, uint8_t* gt) {
+        if (wave < NWQ) {
+            const int g = t / per_head, r0 = (qs0 + t % per_head) * BM;
+            const size_t hoff = (size_t)b * p.sq[0] + (size_t)(hkv * G + g) * p.sq[2];
+            qdma.init((const uint8_t*)((const T*)p.q + hoff), qrow_b, wave, lane, kSwzKV);
+            gdma.init((const uint8_t*)((const T*)bp.dout + hoff), qrow_b, wave, lane, kSwzKV);
+            qdma.issue(r0, Sq, qt, wave);
+            gdma.issue(r0, Sq, gt, wave);
+        }
+    };
+    // lse (times log2 e) and Delta of the step's 32 rows: lanes 0..31 of wave 0.
+    auto load_stats = [&](int t, float& l, float& d) {
+        const int g = t / per_head, r = (qs0 + t % per_head) * BM + n;
+        const size_t idx = ((size_t)b * p.Hq + hkv * G + g) * Sq + r;
+        l = r < Sq ? bp.lse[idx] * kLog2eF : 0.f;
+        d = r < Sq ? bp.delta[idx] : 0.f;
+    };
+
+    // Row reads of the Q and dO tiles (first operand of S and dP): row n,
+    // chunk 2 ks + h. Transpose reads (second operand of dV and dK): rows
+    // 4h + L / 4 and + 8 at byte 64 db + 32 G16 + 8 (L % 4).
+    const uint32_t qrd = n * ROWB + ((h ^ kv_swz<NC>(n)) << 4);
+    const int L16 = lane & 15, G16 = (lane >> 4) & 1;
+    const int rlo = 4 * h + (L16 >> 2), rhi = rlo + 8;
+    uint32_t tlo[NDB], thi[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        const int cb = db * 64 + 32 * G16 + 8 * (L16 & 3);
+        tlo[db] = rlo * ROWB + ((((cb >> 4) ^ kv_swz<NC>(rlo)) << 4) | (cb & 15));
+        thi[db] = rhi * ROWB + ((((cb >> 4) ^ kv_swz<NC>(rhi)) << 4) | (cb & 15));
+    }
+
+    f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { dk[db][i] = 0.f; dv[db][i] = 0.f; }
+
+    float st_l = 0.f, st_d = 0.f;
+    if (n_steps > 0) {
+        issue_step(0, lds_q0, lds_g0);
+        if (wave == 0 && h == 0) {
+            load_stats(0, st_l, st_d);
+            lds_lse[0][n] = st_l;
+            lds_del[0][n] = st_d;
+        }
+    }
+    for (int t = 0; t < n_steps; ++t) {
+        const int buf = t & 1;
+        const uint8_t* qt = buf ? lds_q1 : lds_q0;
+        const uint8_t* gt = buf ? lds_g1 : lds_g0;
+        dma_barrier();   // step t's tiles and statistics are in LDS; step t - 1 is done everywhere
+        if (t + 1 < n_steps) {
+            issue_step(t + 1, buf ? lds_q0 : lds_q1, buf ? lds_g0 : lds_g1);
+            if (wave == 0 && h == 0) load_stats(t + 1, st_l, st_d);
+        }
+        const int r0 = (qs0 + t % per_head) * BM;
+
+        f32x16 s, dp;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { s[i] = 0.f; dp[i] = 0.f; }
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            const frag qa = __builtin_bit_cast(frag, *(const u32x4*)(qt + (qrd ^ (ks << 5))));
+            const frag ga = __builtin_bit_cast(frag, *(const u32x4*)(gt + (qrd ^ (ks << 5))));
+            s = Tr::qk(qa, kf[ks], s);
+            dp = Tr::qk(ga, vf[ks], dp);
+        }
+        // Element i of lane (h, n): query r0 + 8 (i / 4) + 4h + i % 4, key kw0 + n.
+        f32x4 ls[4], ds[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            ls[jj] = *(const f32x4*)&lds_lse[buf][8 * jj + 4 * h];
+            ds[jj] = *(const f32x4*)&lds_del[buf][8 * jj + 4 * h];
+        }
+        // Rows r0 + qo see this lane's key iff qo >= qlim (and the row and key exist).
+        int qlim = CAUSAL ? key - coff - r0 - 4 * h : -(1 << 30);
+        const int qend = Sq - r0 - 4 * h;   // rows at offsets >= qend do not exist
+        const bool key_ok = key < Skv;
+        uint32_t pw[8], sw[8];
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+            const int qo = 8 * (i >> 2) + (i & 3);
+            const bool v0 = key_ok && qo >= qlim && qo < qend;
+            const bool v1 = key_ok && qo + 1 >= qlim && qo + 1 < qend;
+            const float l0 = ls[i >> 2][i & 3], l1 = ls[i >> 2][(i & 3) + 1];
+            const float p0 = v0 ? __builtin_amdgcn_exp2f(fmaf(s[i], c2, -l0)) : 0.f;
+            const float p1 = v1 ? __builtin_amdgcn_exp2f(fmaf(s[i + 1], c2, -l1)) : 0.f;
+            pw[i / 2] = Tr::pack(p0, p1);
+            sw[i / 2] = Tr::pack(p0 * (dp[i] - ds[i >> 2][i & 3]), p1 * (dp[i + 1] - ds[i >> 2][(i & 3) + 1]));
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const frag pa = __builtin_bit_cast(frag, (u32x4){pw[4 * s2], pw[4 * s2 + 1], pw[4 * s2 + 2], pw[4 * s2 + 3]});
+            const frag sa = __builtin_bit_cast(frag, (u32x4){sw[4 * s2], sw[4 * s2 + 1], sw[4 * s2 + 2], sw[4 * s2 + 3]});
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                dv[db] = Tr::qk(pa, tr_read<frag>(gt + 16 * s2 * ROWB, tlo[db], thi[db]), dv[db]);
+                dk[db] = Tr::qk(sa, tr_read<frag>(qt + 16 * s2 * ROWB, tlo[db], thi[db]), dk[db]);
+            }
+        }
+        if (t + 1 < n_steps && wave == 0 && h == 0) {
+            lds_lse[buf ^ 1][n] = st_l;
+            lds_del[buf ^ 1][n] = st_d;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+
+    // Element i of the accumulators: key kw0 + 8 (i / 4) + 4h + i % 4, column 32 db + n.
+    const float sc = bp.scale;
+    T* dkb = (T*)bp.dk + b * p.sk[0] + hkv * p.sk[2];
+    T* dvb = (T*)bp.dv + b * p.sv[0] + hkv * p.sv[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int kr = kw0 + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (kr < Skv) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                dkb[(size_t)kr * p.sk[1] + 32 * db + n] = round_to<T>(dk[db][i] * sc);
+                dvb[(size_t)kr * p.sv[1] + 32 * db + n] = round_to<T>(dv[db][i]);
+            }
+        }
+    }
+}
+
+template <typename T, int D>
+static hipError_t launch_bwd_typed(const BwdParams& bp, bool causal, hipStream_t stream) {
+    const FwdParams& p = bp.f;
+    const unsigned gq = (unsigned)(p.n_units * p.n_row_blocks);
+    const unsigned gk = (unsigned)(p.B * p.Hkv * bp.n_kblocks);
+    if (gq > 0) {
+        if (causal) hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), dim3(gq), dim3(256), 0, stream, bp);
+        else hipLaunchKernelGGL((bwd_dq_kernel<T, D, false>), dim3(gq), dim3(256), 0, stream, bp);
+    }
+    if (gk > 0) {
+        if (causal) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), dim3(gk), dim3(256), 0, stream, bp);
+        else hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false>), dim3(gk), dim3(256), 0, stream, bp);
+    }
+    return hipGetLastError();
+}
+
+// bf16 (is_bf16) or f16, D = 32, 64 or 128. The dQ kernel runs first: it
+// writes Delta, which the dK / dV kernel reads.
+hipError_t launch_bwd(const BwdParams& bp, int D, bool is_bf16, bool causal, hipStream_t stream) {
+    if (is_bf16) {
+        return D == 32 ? launch_bwd_typed<__bf16, 32>(bp, causal, stream)
+             : D == 64 ? launch_bwd_typed<__bf16, 64>(bp, causal, stream)
+                       : launch_bwd_typed<__bf16, 128>(bp, causal, stream);
+    }
+    return D == 32 ? launch_bwd_typed<_Float16, 32>(bp, causal, stream)
+         : D == 64 ? launch_bwd_typed<_Float16, 64>(bp, causal, stream)
+                   : launch_bwd_typed<_Float16, 128>(bp, causal, stream);
+}
+
+}  // namespace attn

@@ -100,6 +100,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
     }
 
     if (row < Sq) {
+        // Row log-sum-exp: sum_j e^(scale s_j) = 2^m_run l_run.
+        if (p.lse && part == 0) p.lse[((size_t)b * p.Hq + hq) * Sq + row] = (m_run + log2f(l_run)) * kLn2;
         const float inv = p.out_mul / l_run;
         float* orow = (float*)p.out + b * p.so[0] + row * p.so[1] + hq * p.so[2] + part * 32;
         for (int d = 0; d < 32; d += 4)

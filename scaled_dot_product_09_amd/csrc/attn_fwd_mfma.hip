@@ -183,8 +183,8 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
     constexpr int NWV = (BN * VROWB / 1024) % NWAVES == 0 ? NWAVES : 4;
     TileDma<KROWB, BN, NWK> kdma;
     TileDma<VROWB, BN, NWV> vdma;
-    kdma.init(kbase, (uint32_t)krow_b, wave % NWK, lane, true);
-    if constexpr (Tr::V_DMA) vdma.init(vbase, (uint32_t)vrow_b, wave % NWV, lane, false);
+    kdma.init(kbase, (uint32_t)krow_b, wave % NWK, lane, kSwzK);
+    if constexpr (Tr::V_DMA) vdma.init(vbase, (uint32_t)vrow_b, wave % NWV, lane, kSwzV);
     auto issue_k = [&](int j, uint8_t* kt) {
         if (NWK == NWAVES || wave < NWK) kdma.issue(j * BN, Skv, kt, wave);
     };
@@ -502,6 +502,10 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
         return;
     }
     const float inv = p.out_mul / l;
+    // Row log-sum-exp: the weights are 2^(c s - m_run) with c = scale log2(e),
+    // so sum_j e^(scale s_j) = 2^m_run l and its logarithm is (m_run + log2 l) ln 2.
+    if (p.lse && qrow < Sq && h == 0)
+        p.lse[((size_t)wi.b * p.Hq + hq) * Sq + qrow] = (m_run + __builtin_amdgcn_logf(l)) * kLn2;
     if (qrow < Sq) {
         out_t* orow = (out_t*)p.out + wi.b * p.so[0] + qrow * p.so[1] + hq * p.so[2];
         for (int db = 0; db < NDB; ++db) {

@@ -100,8 +100,8 @@ __global__ __launch_bounds__(256, 1) void fwd_rb2_kernel(FwdParams p) {
     u32x2 vstage[V_ST];
     TileDma<KROWB, BN> kdma;
     TileDma<VROWB, BN> vdma;
-    kdma.init(kbase, (uint32_t)kstride_b, wave, lane, true);
-    if constexpr (Tr::V_DMA) vdma.init(vbase, (uint32_t)kstride_b, wave, lane, false);
+    kdma.init(kbase, (uint32_t)kstride_b, wave, lane, kSwzK);
+    if constexpr (Tr::V_DMA) vdma.init(vbase, (uint32_t)kstride_b, wave, lane, kSwzV);
     auto issue_k = [&](int j) { kdma.issue(j * BN, Skv, kbuf(j), wave); };
     auto issue_v = [&](int j) {
         if constexpr (Tr::V_DMA) {

@@ -146,8 +146,8 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdParams p) {
     u32x2 vstage[V_ST];
     TileDma<KROWB, BN> kdma;
     TileDma<VROWB, BN> vdma;
-    kdma.init(kbase, (uint32_t)kstride_b, wq, lane, true);
-    if constexpr (Tr::V_DMA) vdma.init(vbase, (uint32_t)kstride_b, wq, lane, false);
+    kdma.init(kbase, (uint32_t)kstride_b, wq, lane, kSwzK);
+    if constexpr (Tr::V_DMA) vdma.init(vbase, (uint32_t)kstride_b, wq, lane, kSwzV);
     auto issue_k = [&](int j, uint8_t* kt) INLINE { kdma.issue(j * BN, Skv, kt, wq); };
     auto issue_v = [&](int j, uint8_t* vt) INLINE {
         if constexpr (Tr::V_DMA) {

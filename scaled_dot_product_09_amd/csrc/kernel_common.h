@@ -41,6 +41,24 @@ struct FwdParams {
     int n_split;        // key ranges per (unit, row block); 1 = no split
     float* part_o;      // n_split > 1: unnormalised partial outputs [n_split][B][Sq][Hq][D]
     float* part_ml;     // n_split > 1: (running max, weight sum) pairs [n_split][B][Sq][Hq][2]
+    float* lse;         // null, or the natural-log row log-sum-exp of the scaled scores, [B][Hq][Sq]
+};
+
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Backward pass: the forward's block (q, k, v, out = the forward's output,
+// shapes, slot map, scale_log2 = scale log2(e), causal_off) plus the
+// gradient tensors. dout and dq have q's layout, dk and dv k's.
+struct BwdParams {
+    FwdParams f;
+    const void* dout;   // (B, Sq, Hq, D) gradient of the loss with respect to out
+    const float* lse;   // [B][Hq][Sq] natural-log row log-sum-exp from the forward
+    float* delta;       // [B][Hq][Sq] workspace: rowsum(dout * out), written by the dQ kernel
+    void* dq;           // (B, Sq, Hq, D)
+    void* dk;           // (B, Skv, Hkv, D)
+    void* dv;           // (B, Skv, Hkv, D)
+    float scale;        // the softmax scale (multiplies dQ and dK)
+    int n_kblocks;      // key blocks of the dK / dV kernel, ceil(Skv / 128)
 };
 
 struct WorkItem {

@@ -114,10 +114,29 @@ template <> struct Traits<fp8_t> {
 //  * K rows are read by 32 lanes at one chunk index and 32 different rows
 //    (the A operand of S^T = K Q^T): consecutive rows get different masks.
 //  * V rows are read by the transpose read: per half-wave 4 rows x 4 chunks.
+//  * Tiles read both ways (row reads by 16 lanes per pass, transpose reads
+//    of 4 rows x 64 bytes per half-wave) use kv_swz: it maps 16 consecutive
+//    rows at one chunk index to 16 different chunk positions (bank groups)
+//    and 4 consecutive rows starting at a multiple of 4 to 4 different
+//    64-byte column groups. With u = r / (16 / NCH) (the row's 256-byte
+//    bank window) and G = NCH / 4 column groups per row, the mask is
+//    ((u mod G) << 2) | ((u / G) mod 4); it repeats every 16 rows.
 template <int NCH>   // chunks per row
 __device__ inline int k_swz(int r) { return (r / (16 / NCH)) % NCH; }
 template <int NCH>
 __device__ inline int v_swz(int r) { return 4 * ((r / (16 / NCH)) % (NCH / 4)); }
+template <int NCH>
+__device__ inline int kv_swz(int r) {
+    const int u = r / (16 / NCH);
+    return ((u % (NCH / 4)) << 2) | ((u / (NCH / 4)) % 4);
+}
+
+enum SwzKind { kSwzK, kSwzV, kSwzKV };
+
+template <int NCH>
+__device__ inline int swz(SwzKind kind, int r) {
+    return kind == kSwzK ? k_swz<NCH>(r) : kind == kSwzV ? v_swz<NCH>(r) : kv_swz<NCH>(r);
+}
 
 // Copying one K or V tile (NROWS rows of ROWB bytes) from HBM straight into
 // LDS, by NW waves. Each buffer_load_dwordx4 ... lds moves 1 KiB: lane l lands
@@ -135,8 +154,8 @@ struct TileDma {
     static constexpr int ROW_STEP = NW * RPI;           // rows between a wave's instructions
     static_assert(NINSTR % NW == 0, "tile must split evenly over the copying waves");
     // Instruction t of this wave covers rows r0 + ROW_STEP t. ROW_STEP is a
-    // multiple of 256 / NCH, so both swizzles give the same mask for every t
-    // (they depend on r / (16 / NCH) modulo at most NCH, and ROW_STEP /
+    // multiple of 256 / NCH, so every swizzle gives the same mask for every t
+    // (they depend on r / (16 / NCH) modulo at most 16, and ROW_STEP /
     // (16 / NCH) is a multiple of 16): one lane offset serves all of the
     // wave's instructions.
     __amdgpu_buffer_rsrc_t rs;  // the whole head: base of its row 0, no range limit
@@ -145,11 +164,11 @@ struct TileDma {
     uint32_t cb;                // lane's byte offset inside its row
     int r0;                     // lane's tile row, instruction 0
 
-    __device__ void init(const uint8_t* head, uint32_t row_bytes_stride, int wave, int lane, bool kswz) {
+    __device__ void init(const uint8_t* head, uint32_t row_bytes_stride, int wave, int lane, SwzKind kind) {
         gstride = row_bytes_stride;
         rs = __builtin_amdgcn_make_buffer_rsrc((void*)head, 0, -1, kBufferWord3);
         r0 = wave * RPI + lane / NCH;
-        const int c = (lane % NCH) ^ (kswz ? k_swz<NCH>(r0) : v_swz<NCH>(r0));
+        const int c = (lane % NCH) ^ swz<NCH>(kind, r0);
         cb = (uint32_t)c * 16;
         off = (uint32_t)r0 * gstride + cb;
     }

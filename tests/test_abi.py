@@ -77,6 +77,53 @@ def test_fp8_rejected_before_launch(kw, status):
     assert call_fp8(**kw) == status
 
 
+L_ = 0x600000   # fake lse buffer
+
+
+def call_lse(q=Q, k=K, v=V, o=O, lse=L_, B=2, Hq=8, Hkv=2, Sq=64, Skv=64, D=128, scale=0.125, causal=1,
+             dtype=attn.ATTN_BF16):
+    return attn.attn_fwd_lse(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lse=0), -1), (dict(q=0), -1), (dict(D=80), -4), (dict(Hq=3, Hkv=2), -3), (dict(causal=3), -10),
+    (dict(dtype=attn.ATTN_FP8_E4M3), -5), (dict(lse=L_ + 2), -6),
+    (dict(lse=Q + 64), -7), (dict(lse=O + 4), -7), (dict(lse=K - 16), -7), (dict(o=Q), -7),
+])
+def test_lse_rejected_before_launch(kw, status):
+    assert call_lse(**kw) == status
+
+
+DO_, DQ_, DK_, DV_, WB_ = 0x900000, 0xA00000, 0xB00000, 0xC00000, 0xD00000
+
+
+def call_bwd(q=Q, k=K, v=V, o=O, do=DO_, lse=L_, dq=DQ_, dk=DK_, dv=DV_, B=2, Hq=8, Hkv=2, Sq=64, Skv=64, D=128,
+             scale=0.125, causal=1, dtype=attn.ATTN_BF16, ws=WB_, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = attn.attn_bwd_workspace(B, Hq, Sq)
+    return attn.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype, ws,
+                         ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(do=0), -1), (dict(lse=0), -1), (dict(dq=0), -1), (dict(dk=0), -1), (dict(dv=0), -1), (dict(o=0), -1),
+    (dict(B=-1), -2), (dict(Skv=0), -2), (dict(Hq=6, Hkv=4), -3), (dict(D=96), -4), (dict(D=256), -4),
+    (dict(dtype=attn.ATTN_F32), -5), (dict(dtype=attn.ATTN_FP8_E4M3), -5),
+    (dict(dq=DQ_ + 8), -6), (dict(do=DO_ + 2), -6), (dict(lse=L_ + 1), -6),
+    (dict(dq=Q), -7), (dict(dk=K + 16), -7), (dict(dv=DO_), -7), (dict(dq=L_), -7), (dict(dv=DK_ + 64), -7),
+    (dict(scale=float("nan")), -8), (dict(causal=3), -10), (dict(causal=2, Sq=65, Skv=64), -10),
+    (dict(ws=0), -12), (dict(ws=WB_ + 4), -12), (dict(ws_bytes=100), -12), (dict(ws=DQ_), -12), (dict(ws=Q), -12),
+])
+def test_bwd_rejected_before_launch(kw, status):
+    assert call_bwd(**kw) == status
+
+
+def test_bwd_workspace_size():
+    assert attn.attn_bwd_workspace(2, 8, 64) == 2 * 8 * 64 * 4
+    assert attn.attn_bwd_workspace(0, 8, 64) == 0
+    assert attn.attn_bwd_workspace(2, 8, 0) == 0
+
+
 W = 0x800000   # fake 16-byte aligned workspace, far from the tensors
 
 
@@ -153,6 +200,10 @@ def test_empty_problem_is_a_noop():
     assert call_split(Sq=0, ws=0) == 0
     assert call_split(n_split=1, B=0, ws=0) == 0
     assert call_strided(Sq=0) == 0
+    assert call_lse(B=0) == 0
+    assert call_bwd(B=0, ws=0) == 0
+    assert call_bwd(Sq=0, Skv=0, ws=0) == 0
+    assert call_bwd(B=0, q=0, k=0, v=0, o=0, do=0, lse=0, dq=0, dk=0, dv=0, ws=0) == 0
 
 
 def test_python_wrapper_rejects_host_tensors():

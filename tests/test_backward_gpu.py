@@ -1,0 +1,190 @@
+"""GPU parity of the row log-sum-exp output and of the backward pass, against
+the fp64 oracle (oracle.sdpa_lse, oracle.sdpa_backward).
+
+The oracle sees the same seeded input codes (decoded by its own codecs) and
+computes the exact gradients of sum(dout * sdpa(q, k, v)); nothing it uses
+comes from the GPU. The GPU backward takes the GPU forward's out and lse, as
+a training step would.
+
+Bounds. lse: 1e-5 for float32 inputs; 2e-2 for bf16 / f16 (the forward sums
+weights rounded to the input type: relative error of the row sum below
+2^-8, so |d lse| < 4e-3). Gradients (bf16 / f16): max-abs error at most
+2e-2 * max(1, max |exact|) per tensor: P and dS enter the products rounded
+to the input type (relative 2^-9 each), Delta uses the rounded forward
+output, and each gradient is rounded once (relative 2^-9); 2e-2 is the
+forward's bf16 bound, taken relative to the tensor's own scale where that
+exceeds 1.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from scaled_dot_product_09_amd import attn, workload
+from scaled_dot_product_09_amd.workload import Workload
+from tests import helpers
+
+pytestmark = pytest.mark.gpu
+
+LSE_TOL = {"f32": 1e-5, "bf16": 2e-2, "f16": 2e-2}
+
+
+def W(dtype, B, Hq, Hkv, Sq, Skv, D, causal, seed=5):
+    tag = {False: "", True: "_causal", "bottom_right": "_br"}[causal]
+    return Workload(f"{dtype}_b{B}_hq{Hq}_hkv{Hkv}_sq{Sq}_skv{Skv}_d{D}{tag}", dtype, B, Hq, Hkv, Sq, Skv, D,
+                    causal, seed)
+
+
+def draw_dout(w, seed_offset=1000):
+    g = workload.draw_normal(w.seed + seed_offset, [(w.B, w.Sq, w.Hq, w.D)])[0]
+    return torch.from_numpy(g).to(workload.TORCH_DTYPE[w.dtype])
+
+
+def grad_tol(ref):
+    return 2e-2 * max(1.0, float(np.max(np.abs(ref))) if ref.size else 1.0)
+
+
+@pytest.fixture(params=["w4", "w8"])
+def kernel(request, monkeypatch):
+    monkeypatch.setenv("ATTN_KERNEL", request.param)
+    return request.param
+
+
+LSE_CASES = [
+    W("f32", 1, 4, 2, 100, 100, 64, True),
+    W("f32", 2, 2, 1, 33, 70, 128, "bottom_right"),
+    W("f32", 1, 2, 2, 50, 20, 32, False),
+    W("bf16", 2, 8, 2, 300, 300, 128, True),
+    W("bf16", 1, 4, 1, 7, 500, 128, "bottom_right"),
+    W("bf16", 1, 4, 4, 130, 257, 64, False),
+    W("bf16", 1, 4, 2, 200, 200, 32, True),
+    W("f16", 1, 8, 2, 100, 100, 128, True),
+]
+
+
+@pytest.mark.parametrize("w", LSE_CASES, ids=lambda w: w.name)
+def test_lse_parity(w, kernel):
+    print(f"case {w.name} kernel {kernel}", flush=True)
+    q, k, v, _ = workload.make_inputs(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out, lse = attn.fwd_lse(qd, kd, vd, causal=w.causal, scale=w.scale)
+    ref_out = attn.fwd(qd, kd, vd, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out)            # same kernel, same output
+    want = oracle.sdpa_lse(helpers.to_f64(q, w.dtype), helpers.to_f64(k, w.dtype), scale=w.scale, causal=w.causal)
+    err = helpers.max_abs_err(lse.cpu().numpy().astype(np.float64), want)
+    print(f"  lse max-abs {err:.3e}", flush=True)
+    assert err <= LSE_TOL[w.dtype], err
+
+
+def run_backward(w, q, k, v, g, *, scale=None):
+    dev = torch.device("cuda:0")
+    scale = w.scale if scale is None else scale
+    qd, kd, vd, gd = q.to(dev), k.to(dev), v.to(dev), g.to(dev)
+    out, lse = attn.fwd_lse(qd, kd, vd, causal=w.causal, scale=scale)
+    dq, dk, dv = attn.bwd(qd, kd, vd, out, gd, lse, causal=w.causal, scale=scale)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def check_grads(w, got, want):
+    for name, a, b in zip(("dq", "dk", "dv"), got, want):
+        a = helpers.out_to_f64(a)
+        err, tol = helpers.max_abs_err(a, b), grad_tol(b)
+        print(f"  {name} max-abs {err:.3e} (max |exact| {np.max(np.abs(b)) if b.size else 0:.3f}, bound {tol:.3e})",
+              flush=True)
+        assert err <= tol, (name, err, tol)
+
+
+BWD_CASES = [
+    W("bf16", 1, 4, 2, 200, 200, 128, True),        # ragged in every tiling (64-key tiles, 128-key blocks, 32-row steps)
+    W("bf16", 2, 4, 4, 130, 130, 64, False),
+    W("bf16", 1, 8, 1, 77, 300, 128, "bottom_right"),   # MQA, Sq < Skv
+    W("bf16", 1, 2, 1, 300, 77, 64, True),          # top-left mask with Sq > Skv: rows past Skv see every key
+    W("bf16", 1, 4, 2, 256, 256, 32, True),
+    W("bf16", 1, 4, 1, 5, 400, 128, "bottom_right"),    # decode shape: rows of several heads share a wave
+    W("bf16", 1, 8, 2, 1, 1, 64, False),            # one key: dq = dk = 0
+    W("bf16", 2, 4, 2, 64, 64, 128, False),
+    W("f16", 1, 8, 2, 160, 160, 128, True),
+    W("f16", 1, 4, 4, 97, 150, 64, "bottom_right"),
+]
+
+
+@pytest.mark.parametrize("w", BWD_CASES, ids=lambda w: w.name)
+def test_backward_parity(w):
+    print(f"case {w.name}", flush=True)
+    q, k, v, _ = workload.make_inputs(w)
+    g = draw_dout(w)
+    got = run_backward(w, q, k, v, g)
+    want = oracle.sdpa_backward(*(helpers.to_f64(x, w.dtype) for x in (q, k, v, g)), scale=w.scale,
+                                causal=w.causal)
+    check_grads(w, got, want)
+
+
+def test_backward_negative_and_zero_scale():
+    w = W("bf16", 1, 4, 2, 96, 96, 64, True)
+    q, k, v, _ = workload.make_inputs(w)
+    g = draw_dout(w)
+    for scale in (-0.2, 0.0):
+        print(f"scale {scale}", flush=True)
+        got = run_backward(w, q, k, v, g, scale=scale)
+        want = oracle.sdpa_backward(*(helpers.to_f64(x, w.dtype) for x in (q, k, v, g)), scale=scale,
+                                    causal=w.causal)
+        check_grads(w, got, want)
+
+
+def test_backward_no_query_rows_zeroes_dk_dv():
+    """Sq = 0: nothing reads the keys, so dk and dv are written as 0."""
+    dev = torch.device("cuda:0")
+    q = torch.zeros(1, 0, 4, 64, dtype=torch.bfloat16, device=dev)
+    k = torch.randn(1, 50, 2, 64, device=dev).to(torch.bfloat16)
+    lse = torch.zeros(1, 4, 0, device=dev)
+    dk = torch.full_like(k, 7.0)
+    dv = torch.full_like(k, 7.0)
+    attn.bwd(q, k, k, q, q, lse, causal=False, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert torch.all(dk == 0) and torch.all(dv == 0)
+
+
+def test_backward_is_deterministic():
+    w = W("bf16", 1, 8, 2, 300, 300, 128, True)
+    q, k, v, _ = workload.make_inputs(w)
+    g = draw_dout(w)
+    a = run_backward(w, q, k, v, g)
+    b = run_backward(w, q, k, v, g)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_backward_full_size_headline():
+    """Causal GQA, B=2, Hq=32, Hkv=8, S=4096, D=128, bf16: every gradient of
+    one (batch, KV head) group against the oracle (its four query heads
+    and the shared K/V head), and two sums that hold exactly for every
+    group: the key gradients of a KV head sum to zero over the keys, and its
+    value gradients sum to the group's dout summed over the rows."""
+    w = workload.WORKLOADS[workload.HEADLINE]
+    print(f"case {w.name}", flush=True)
+    q, k, v, _ = workload.make_inputs(w)
+    g = draw_dout(w)
+    dq, dk, dv = run_backward(w, q, k, v, g)
+    G = w.Hq // w.Hkv
+    b, hkv = 1, 5
+    hs = slice(hkv * G, (hkv + 1) * G)
+    want = oracle.sdpa_backward(helpers.to_f64(q[b:b + 1, :, hs], "bf16"),
+                                helpers.to_f64(k[b:b + 1, :, hkv:hkv + 1], "bf16"),
+                                helpers.to_f64(v[b:b + 1, :, hkv:hkv + 1], "bf16"),
+                                helpers.to_f64(g[b:b + 1, :, hs], "bf16"), scale=w.scale, causal=True)
+    got = (dq[b:b + 1, :, hs], dk[b:b + 1, :, hkv:hkv + 1], dv[b:b + 1, :, hkv:hkv + 1])
+    check_grads(w, got, want)
+    # Sums over keys (float64 of the rounded gradients) for every (batch, KV head).
+    dk64 = dk.double().sum(dim=1).cpu().numpy()
+    dv64 = dv.double().sum(dim=1).cpu().numpy()
+    gsum = helpers.to_f64(g, "bf16").sum(axis=1).reshape(w.B, w.Hkv, G, w.D).sum(axis=2)
+    err_k = float(np.max(np.abs(dk64)))
+    err_v = float(np.max(np.abs(dv64 - gsum)))
+    print(f"  |sum_j dk| max {err_k:.3e}; |sum_j dv - sum_i dout| max {err_v:.3e}", flush=True)
+    # Each of the 4096 rounded terms is off by at most 2^-9 of its size.
+    assert err_k <= 4096 * 2.0 ** -9 * float(dk.abs().max()), err_k
+    assert err_v <= 4096 * 2.0 ** -9 * float(dv.abs().max()) + 1e-3 * float(np.max(np.abs(gsum))), err_v
