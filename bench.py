@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s and % of MFMA peak at S=4096 causal GQA bf16"
+METRIC_BWD = "attention bwd TFLOP/s (2.5x the forward's FLOPs: the five products of the gradients)"
 # MI355X published dense peaks (TFLOP/s) by arithmetic type of the products.
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "f32": 157.3}
 PEAK_KIND = {"bf16": "mfma", "f16": "mfma", "e4m3": "mfma", "f32": "alu"}
@@ -124,6 +125,21 @@ def time_workload(w, steps, warmup, rotate=True, settle_s=SETTLE_S):
                  descales=desc if fp8 else None, stream=stream.cuda_stream,
                  n_split=n_split if ws is not None else None, workspace=ws)
 
+    if w.direction == "bwd":
+        # Backward: the forward's out and lse are made once per input set,
+        # outside the timed region; a step is one attn_bwd call.
+        g = workload.make_dout(w).to(dev)
+        bsets = []
+        for qd, kd, vd, od in sets:
+            od, lse = attn.fwd_lse(qd, kd, vd, causal=w.causal, scale=w.scale, out=od)
+            bsets.append((qd, kd, vd, od, lse, torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)))
+        bws = torch.empty(max(attn.attn_bwd_workspace(w.B, w.Hq, w.Sq), 16), dtype=torch.uint8, device=dev)
+
+        def step(i):  # noqa: F811
+            qd, kd, vd, od, lse, dq, dk, dv = bsets[i % nsets]
+            attn.bwd(qd, kd, vd, od, g, lse, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=bws,
+                     stream=stream.cuda_stream)
+
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -150,8 +166,8 @@ def time_workload(w, steps, warmup, rotate=True, settle_s=SETTLE_S):
 
 
 def result_line(w, t, steps, warmup, n_gpus, cpu=None, warm=None):
-    from scaled_dot_product_09_amd.workload import metric_flops, io_bytes
-    flops = metric_flops(w.B, w.Hq, w.Sq, w.Skv, w.D, w.causal)
+    from scaled_dot_product_09_amd.workload import workload_flops, io_bytes
+    flops = workload_flops(w)
     ms = t["ms_per_step"]
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
@@ -168,12 +184,13 @@ def result_line(w, t, steps, warmup, n_gpus, cpu=None, warm=None):
                 "frac": round(tflops / peak, 4)}
     roof.update({"traffic": load_traffic(w.name), "algorithmic_bytes": nbytes})
     line = {
-        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": n_gpus,
+        "metric": METRIC if w.direction == "fwd" else METRIC_BWD, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": n_gpus,
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq, "Skv": w.Skv,
                    "D": w.D, "causal": w.causal, "input_dtype": w.dtype, "output_dtype": w.out_dtype,
-                   "parallelism": "single GPU", "rotating_input_sets": N_BUFFER_SETS, "layout": w.layout},
+                   "parallelism": "single GPU", "rotating_input_sets": N_BUFFER_SETS, "layout": w.layout,
+                   "direction": w.direction},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "median_ms": round(t["median_ms"], 5), "min_ms": round(t["min_ms"], 5),
         "settle_steps": t["settle_steps"],

@@ -21,7 +21,8 @@
 //     stores it for the second kernel.
 //   * bwd_dkdv_kernel: one workgroup per 128 keys of one KV head (32 keys
 //     per wave, K and V operands held in registers), looping over the query
-//     heads of the group and 32-row query steps staged in LDS: S = Q K^T,
+//     heads of the group and 64-row query steps staged in LDS (three stages,
+//     copies two steps ahead): S = Q K^T,
 //     dP = dO V^T, dS, then dV += P^T dO and dK += dS^T Q with P^T and dS^T
 //     taken straight from the accumulators.
 // S and dP are thus computed twice, 7 matrix products instead of 5. The
@@ -163,17 +164,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams bp) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) dq[db][i] = 0.f;
 
-    kdma.issue(0, Skv, lds_k0, wave);
-    vdma.issue(0, Skv, lds_v0, wave);
-    for (int j = 0; j < n_tiles; ++j) {
-        const uint8_t* kt = (j & 1) ? lds_k1 : lds_k0;
-        const uint8_t* vt = (j & 1) ? lds_v1 : lds_v0;
+    // One tile: kt / vt hold tile j, kn / vn receive tile j + 1. The buffers
+    // are distinct LDS objects passed as __restrict__ pointers into an
+    // inlined body, which lets the compiler see that the copies into kn / vn
+    // never alias the reads of kt / vt; otherwise it makes those reads wait
+    // for the copies, and no copy overlaps the tile's products.
+    auto tile = [&](int j, const uint8_t* __restrict__ kt, const uint8_t* __restrict__ vt,
+                    uint8_t* __restrict__ kn, uint8_t* __restrict__ vn) __attribute__((always_inline)) {
         dma_barrier();   // tile j has landed; every wave is done with tile j - 1
         if (j + 1 < n_tiles) {
-            kdma.issue((j + 1) * BN, Skv, (j & 1) ? lds_k0 : lds_k1, wave);
-            vdma.issue((j + 1) * BN, Skv, (j & 1) ? lds_v0 : lds_v1, wave);
+            kdma.issue((j + 1) * BN, Skv, kn, wave);
+            vdma.issue((j + 1) * BN, Skv, vn, wave);
         }
-        if (wave_idle) continue;
+        if (wave_idle) return;
         f32x16 s[NKB], dp[NKB];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -217,7 +220,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams bp) {
                     dq[db] = Tr::qk(tr_read<frag>(base, tlo[db], thi[db]), sf, dq[db]);
             }
         }
+    };
+
+    kdma.issue(0, Skv, lds_k0, wave);
+    vdma.issue(0, Skv, lds_v0, wave);
+    int j = 0;
+    for (; j + 2 <= n_tiles; j += 2) {
+        tile(j, lds_k0, lds_v0, lds_k1, lds_v1);
+        tile(j + 1, lds_k1, lds_v1, lds_k0, lds_v0);
     }
+    if (j < n_tiles) tile(j, lds_k0, lds_v0, lds_k1, lds_v1);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // no copy may still be in flight when the workgroup ends
 
     if (row_ok) {
@@ -245,27 +257,33 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams bp) {
     using frag = typename Tr::qk_frag;
     const FwdParams& p = bp.f;
     constexpr int ROWB = D * 2, NC = ROWB / 16, KSTEPS = D / 16, NDB = D / 32;
-    constexpr int BM = 32;                             // query rows per step
+    constexpr int BM = 64;                             // query rows per step (two 32-row blocks)
+    constexpr int NMB = BM / 32;
     constexpr int TILE = BM * ROWB;
-    constexpr int NWQ = TILE / 1024 >= 4 ? 4 : TILE / 1024;   // waves copying a Q / dO tile
+    // One LDS object per stage and tensor (see the step body below).
     __shared__ __attribute__((aligned(1024))) uint8_t lds_q0[TILE];
     __shared__ __attribute__((aligned(1024))) uint8_t lds_q1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_q2[TILE];
     __shared__ __attribute__((aligned(1024))) uint8_t lds_g0[TILE];
     __shared__ __attribute__((aligned(1024))) uint8_t lds_g1[TILE];
-    __shared__ __attribute__((aligned(16))) float lds_lse[2][BM];
-    __shared__ __attribute__((aligned(16))) float lds_del[2][BM];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_g2[TILE];
+    __shared__ __attribute__((aligned(16))) float lds_s0[2 * BM];   // [lse, Delta][row]
+    __shared__ __attribute__((aligned(16))) float lds_s1[2 * BM];
+    __shared__ __attribute__((aligned(16))) float lds_s2[2 * BM];
 
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, n = lane & 31;
 
-    // Key blocks are the fastest index: with a causal mask the first blocks
-    // see the most query rows, and they go out first.
-    int id = (int)__builtin_amdgcn_workgroup_id_x();
-    const int kblk = id % bp.n_kblocks;
-    id /= bp.n_kblocks;
-    const int hkv = id % p.Hkv, b = id / p.Hkv;
+    // Key blocks are the slowest index, so with a causal mask the blocks
+    // that see the most query rows (the first ones) go out first, for every
+    // (batch, KV head) alike; the workgroups of one (batch, KV head) then
+    // sit on the same XCD (workgroup i runs on XCD i % 8).
+    const int id = (int)__builtin_amdgcn_workgroup_id_x();
+    const int nbh = p.B * p.Hkv;
+    const int kblk = id / nbh;
+    const int hkv = (id % nbh) % p.Hkv, b = (id % nbh) / p.Hkv;
     const int Sq = p.Sq, Skv = p.Skv, G = p.G;
     const int kw0 = kblk * 128 + 32 * wave;            // this wave's first key
     const int key = kw0 + n;                           // the key of lane column n
@@ -292,29 +310,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams bp) {
     const int per_head = n_qs - qs0;
     const int n_steps = G * per_head;
 
-    TileDma<ROWB, BM, NWQ> qdma, gdma;
+    // Copies of one step: the Q and dO tiles (all four waves), the rows' lse
+    // (wave 0) and Delta (wave 1), each lane of those one row (rows past the
+    // end repeat the last row; they are masked).
+    TileDma<ROWB, BM, 4> qdma, gdma;
+    constexpr int NV = 2 * TileDma<ROWB, BM, 4>::PER_WAVE;   // tile copy instructions per wave and step
+    static_assert(NV + 1 < 16, "the wait below encodes the count in four bits");
     const uint32_t qrow_b = (uint32_t)(p.sq[1] * 2);
-    auto issue_step = [&](int t, uint8_t* qt, uint8_t* gt) {
-        if (wave < NWQ) {
-            const int g = t / per_head, r0 = (qs0 + t % per_head) * BM;
-            const size_t hoff = (size_t)b * p.sq[0] + (size_t)(hkv * G + g) * p.sq[2];
-            qdma.init((const uint8_t*)((const T*)p.q + hoff), qrow_b, wave, lane, kSwzKV);
-            gdma.init((const uint8_t*)((const T*)bp.dout + hoff), qrow_b, wave, lane, kSwzKV);
-            qdma.issue(r0, Sq, qt, wave);
-            gdma.issue(r0, Sq, gt, wave);
+    auto issue_step = [&](int t, uint8_t* qd, uint8_t* gd, float* sd) __attribute__((always_inline)) {
+        const int g = t / per_head, r0 = (qs0 + t % per_head) * BM;
+        const int hq = hkv * G + g;
+        const size_t hoff = (size_t)b * p.sq[0] + (size_t)hq * p.sq[2];
+        qdma.init((const uint8_t*)((const T*)p.q + hoff), qrow_b, wave, lane, kSwzKV);
+        gdma.init((const uint8_t*)((const T*)bp.dout + hoff), qrow_b, wave, lane, kSwzKV);
+        qdma.issue(r0, Sq, qd, wave);
+        gdma.issue(r0, Sq, gd, wave);
+        if (wave < 2) {
+            const float* src = (wave == 0 ? bp.lse : bp.delta) + ((size_t)b * p.Hq + hq) * Sq;
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, -1, kBufferWord3);
+            const uint32_t off = (uint32_t)min(r0 + lane, Sq - 1) * 4;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(sd + wave * BM), 4, off, 0, 0, 0);
         }
     };
-    // lse (times log2 e) and Delta of the step's 32 rows: lanes 0..31 of wave 0.
-    auto load_stats = [&](int t, float& l, float& d) {
-        const int g = t / per_head, r = (qs0 + t % per_head) * BM + n;
-        const size_t idx = ((size_t)b * p.Hq + hkv * G + g) * Sq + r;
-        l = r < Sq ? bp.lse[idx] * kLog2eF : 0.f;
-        d = r < Sq ? bp.delta[idx] : 0.f;
-    };
 
-    // Row reads of the Q and dO tiles (first operand of S and dP): row n,
-    // chunk 2 ks + h. Transpose reads (second operand of dV and dK): rows
-    // 4h + L / 4 and + 8 at byte 64 db + 32 G16 + 8 (L % 4).
+    // Row reads of the Q and dO tiles (first operand of S and dP): row
+    // 32 mb + n, chunk 2 ks + h. Transpose reads (second operand of dV and
+    // dK): rows 4h + L / 4 and + 8 at byte 64 db + 32 G16 + 8 (L % 4).
     const uint32_t qrd = n * ROWB + ((h ^ kv_swz<NC>(n)) << 4);
     const int L16 = lane & 15, G16 = (lane >> 4) & 1;
     const int rlo = 4 * h + (L16 >> 2), rhi = rlo + 8;
@@ -332,74 +353,100 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams bp) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) { dk[db][i] = 0.f; dv[db][i] = 0.f; }
 
-    float st_l = 0.f, st_d = 0.f;
-    if (n_steps > 0) {
-        issue_step(0, lds_q0, lds_g0);
-        if (wave == 0 && h == 0) {
-            load_stats(0, st_l, st_d);
-            lds_lse[0][n] = st_l;
-            lds_del[0][n] = st_d;
-        }
-    }
-    for (int t = 0; t < n_steps; ++t) {
-        const int buf = t & 1;
-        const uint8_t* qt = buf ? lds_q1 : lds_q0;
-        const uint8_t* gt = buf ? lds_g1 : lds_g0;
-        dma_barrier();   // step t's tiles and statistics are in LDS; step t - 1 is done everywhere
+    // Step t reads stage t % 3 (qt, gt, stt) and, after the barrier, starts
+    // the copies of step t + 2 into stage (t + 2) % 3 (qn, gn, sn), the one
+    // step t - 1 used. Distinct LDS objects passed as __restrict__ pointers
+    // into an inlined body let the compiler see that those copies never
+    // alias this step's reads (otherwise the reads would wait for them).
+    auto step = [&](int t, const uint8_t* __restrict__ qt, const uint8_t* __restrict__ gt,
+                    const float* __restrict__ stt, uint8_t* __restrict__ qn, uint8_t* __restrict__ gn,
+                    float* __restrict__ sn) __attribute__((always_inline)) {
+        // Step t's copies have landed (each wave waits for its own, the
+        // barrier for everyone's), and every wave is done with step t - 1,
+        // whose stage the copies of step t + 2 reuse.
+        // Copies complete in issue order, so waiting until no more than step
+        // t + 1's own copies are outstanding (NV per wave, plus one for the
+        // statistics in waves 0 and 1) means step t's have landed.
         if (t + 1 < n_steps) {
-            issue_step(t + 1, buf ? lds_q0 : lds_q1, buf ? lds_g0 : lds_g1);
-            if (wave == 0 && h == 0) load_stats(t + 1, st_l, st_d);
+            if (wave < 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (NV + 1));
+            else __builtin_amdgcn_s_waitcnt(0x0F70 | NV);
+        } else {
+            __builtin_amdgcn_s_waitcnt(0x0F70);
         }
+        __syncthreads();
+        if (t + 2 < n_steps) issue_step(t + 2, qn, gn, sn);
         const int r0 = (qs0 + t % per_head) * BM;
 
-        f32x16 s, dp;
+        f32x16 s[NMB], dp[NMB];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { s[i] = 0.f; dp[i] = 0.f; }
+        for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) { s[mb][i] = 0.f; dp[mb][i] = 0.f; }
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
-            const frag qa = __builtin_bit_cast(frag, *(const u32x4*)(qt + (qrd ^ (ks << 5))));
-            const frag ga = __builtin_bit_cast(frag, *(const u32x4*)(gt + (qrd ^ (ks << 5))));
-            s = Tr::qk(qa, kf[ks], s);
-            dp = Tr::qk(ga, vf[ks], dp);
-        }
-        // Element i of lane (h, n): query r0 + 8 (i / 4) + 4h + i % 4, key kw0 + n.
-        f32x4 ls[4], ds[4];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            ls[jj] = *(const f32x4*)&lds_lse[buf][8 * jj + 4 * h];
-            ds[jj] = *(const f32x4*)&lds_del[buf][8 * jj + 4 * h];
-        }
-        // Rows r0 + qo see this lane's key iff qo >= qlim (and the row and key exist).
-        int qlim = CAUSAL ? key - coff - r0 - 4 * h : -(1 << 30);
-        const int qend = Sq - r0 - 4 * h;   // rows at offsets >= qend do not exist
-        const bool key_ok = key < Skv;
-        uint32_t pw[8], sw[8];
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-            const int qo = 8 * (i >> 2) + (i & 3);
-            const bool v0 = key_ok && qo >= qlim && qo < qend;
-            const bool v1 = key_ok && qo + 1 >= qlim && qo + 1 < qend;
-            const float l0 = ls[i >> 2][i & 3], l1 = ls[i >> 2][(i & 3) + 1];
-            const float p0 = v0 ? __builtin_amdgcn_exp2f(fmaf(s[i], c2, -l0)) : 0.f;
-            const float p1 = v1 ? __builtin_amdgcn_exp2f(fmaf(s[i + 1], c2, -l1)) : 0.f;
-            pw[i / 2] = Tr::pack(p0, p1);
-            sw[i / 2] = Tr::pack(p0 * (dp[i] - ds[i >> 2][i & 3]), p1 * (dp[i + 1] - ds[i >> 2][(i & 3) + 1]));
-        }
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            const frag pa = __builtin_bit_cast(frag, (u32x4){pw[4 * s2], pw[4 * s2 + 1], pw[4 * s2 + 2], pw[4 * s2 + 3]});
-            const frag sa = __builtin_bit_cast(frag, (u32x4){sw[4 * s2], sw[4 * s2 + 1], sw[4 * s2 + 2], sw[4 * s2 + 3]});
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                dv[db] = Tr::qk(pa, tr_read<frag>(gt + 16 * s2 * ROWB, tlo[db], thi[db]), dv[db]);
-                dk[db] = Tr::qk(sa, tr_read<frag>(qt + 16 * s2 * ROWB, tlo[db], thi[db]), dk[db]);
+            for (int mb = 0; mb < NMB; ++mb) {
+                const uint32_t o = mb * 32 * ROWB + (qrd ^ (ks << 5));
+                s[mb] = Tr::qk(__builtin_bit_cast(frag, *(const u32x4*)(qt + o)), kf[ks], s[mb]);
+                dp[mb] = Tr::qk(__builtin_bit_cast(frag, *(const u32x4*)(gt + o)), vf[ks], dp[mb]);
             }
         }
-        if (t + 1 < n_steps && wave == 0 && h == 0) {
-            lds_lse[buf ^ 1][n] = st_l;
-            lds_del[buf ^ 1][n] = st_d;
+        // Element i of block mb, lane (h, n): query r0 + 32 mb + 8 (i / 4) + 4h + i % 4, key kw0 + n.
+        // It is visible iff the key exists, the row exists and (causal) key <= row + coff.
+        const bool key_ok = key < Skv;
+        uint32_t pw[NMB][8], sw[NMB][8];
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+            const int qb = r0 + 32 * mb + 4 * h;
+            const int qlim = CAUSAL ? key - coff - qb : -(1 << 30);   // offsets >= qlim see the key
+            const int qend = Sq - qb;                                  // offsets >= qend do not exist
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const f32x4 l4 = *(const f32x4*)&stt[32 * mb + 8 * jj + 4 * h];
+                const f32x4 d4 = *(const f32x4*)&stt[BM + 32 * mb + 8 * jj + 4 * h];
+                float pr[4], dsr[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int qo = 8 * jj + e;
+                    const int i = 4 * jj + e;
+                    const bool vis = key_ok && qo >= qlim && qo < qend;
+                    pr[e] = vis ? __builtin_amdgcn_exp2f(fmaf(s[mb][i], c2, -l4[e] * kLog2eF)) : 0.f;
+                    dsr[e] = pr[e] * (dp[mb][i] - d4[e]);
+                }
+                pw[mb][2 * jj] = Tr::pack(pr[0], pr[1]);
+                pw[mb][2 * jj + 1] = Tr::pack(pr[2], pr[3]);
+                sw[mb][2 * jj] = Tr::pack(dsr[0], dsr[1]);
+                sw[mb][2 * jj + 1] = Tr::pack(dsr[2], dsr[3]);
+            }
         }
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const frag pa = __builtin_bit_cast(frag, (u32x4){pw[mb][4 * s2], pw[mb][4 * s2 + 1],
+                                                                 pw[mb][4 * s2 + 2], pw[mb][4 * s2 + 3]});
+                const frag sa = __builtin_bit_cast(frag, (u32x4){sw[mb][4 * s2], sw[mb][4 * s2 + 1],
+                                                                 sw[mb][4 * s2 + 2], sw[mb][4 * s2 + 3]});
+                const uint32_t rb = (32 * mb + 16 * s2) * ROWB;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    dv[db] = Tr::qk(pa, tr_read<frag>(gt + rb, tlo[db], thi[db]), dv[db]);
+                    dk[db] = Tr::qk(sa, tr_read<frag>(qt + rb, tlo[db], thi[db]), dk[db]);
+                }
+            }
+        }
+    };
+
+    if (n_steps > 0) issue_step(0, lds_q0, lds_g0, lds_s0);
+    if (n_steps > 1) issue_step(1, lds_q1, lds_g1, lds_s1);
+    int t = 0;
+    for (; t + 3 <= n_steps; t += 3) {
+        step(t, lds_q0, lds_g0, lds_s0, lds_q2, lds_g2, lds_s2);
+        step(t + 1, lds_q1, lds_g1, lds_s1, lds_q0, lds_g0, lds_s0);
+        step(t + 2, lds_q2, lds_g2, lds_s2, lds_q1, lds_g1, lds_s1);
     }
+    if (t < n_steps) step(t, lds_q0, lds_g0, lds_s0, lds_q2, lds_g2, lds_s2);
+    if (t + 1 < n_steps) step(t + 1, lds_q1, lds_g1, lds_s1, lds_q0, lds_g0, lds_s0);
     __builtin_amdgcn_s_waitcnt(0x0F70);
 
     // Element i of the accumulators: key kw0 + 8 (i / 4) + 4h + i % 4, column 32 db + n.

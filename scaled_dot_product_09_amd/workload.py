@@ -25,8 +25,8 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "PAGE_SHAPES", "draw_normal", "make_inputs", "metric_flops", "io_bytes",
-           "to_layout"]
+__all__ = ["Workload", "WORKLOADS", "PAGE_SHAPES", "draw_normal", "make_inputs", "make_dout", "metric_flops",
+           "bwd_metric_flops", "workload_flops", "io_bytes", "to_layout"]
 
 DTYPES = ("f32", "bf16", "f16", "e4m3")
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16,
@@ -50,6 +50,7 @@ class Workload:
     note: str = field(default="", compare=False)
     n_split: object = None  # None: attn_fwd; "auto" or an int: the split-key entry point
     layout: str = "bshd"    # storage of q, k, v, out on the GPU: "bshd" (dense) or "bhsd" (transposed views)
+    direction: str = "fwd"  # "fwd": the forward pass; "bwd": the backward pass (attn_bwd) of that forward
 
     @property
     def scale(self):
@@ -95,6 +96,12 @@ WORKLOADS = {w.name: w for w in [
              "head dim 32; seed 32"),
     Workload("bf16_gqa_b2_hq32_hkv8_s4096_d128_causal_bhsd", "bf16", 2, 32, 8, 4096, 4096, 128, True, 42,
              "headline shape, (B, H, S, D) storage, strided entry point", layout="bhsd"),
+    # Backward pass (the gradients the scale of §1 exists to keep alive) of
+    # the headline and of the MHA head-dim-64 forward; dout drawn by make_dout.
+    Workload("bf16_gqa_b2_hq32_hkv8_s4096_d128_causal_bwd", "bf16", 2, 32, 8, 4096, 4096, 128, True, 42,
+             "backward of the headline forward", direction="bwd"),
+    Workload("bf16_mha_b4_h16_s2048_d64_causal_bwd", "bf16", 4, 16, 16, 2048, 2048, 64, True, 2048,
+             "backward, MHA, head dim 64", direction="bwd"),
 ]}
 
 HEADLINE = "bf16_gqa_b2_hq32_hkv8_s4096_d128_causal"
@@ -142,6 +149,14 @@ def make_inputs(w, *, seed=None, shapes=None):
     return t[0], t[1], t[2], (1.0, 1.0, 1.0)
 
 
+def make_dout(w, seed_offset=1000):
+    """The loss gradient dout for a backward workload: N(0, 1) float32 of q's
+    shape from the seed w.seed + 1000 (first child stream), rounded to the
+    input type like q."""
+    g = draw_normal(w.seed + seed_offset, [(w.B, w.Sq, w.Hq, w.D)])[0]
+    return torch.from_numpy(g).to(TORCH_DTYPE[w.dtype])
+
+
 def to_layout(x, layout):
     """A (B, S, H, D) tensor in the workload's storage: itself for "bshd"; for
     "bhsd" a (B, S, H, D) view of dense (B, H, S, D) storage of the same
@@ -166,8 +181,27 @@ def metric_flops(B, Hq, Sq, Skv, D, causal):
     return f / 2 if causal else f
 
 
+def bwd_metric_flops(B, Hq, Sq, Skv, D, causal):
+    """Backward FLOPs as counted for the metric: the five products the
+    gradients need (S = Q K^T, dP = dO V^T, dV = P^T dO, dK = dS^T Q,
+    dQ = dS K), i.e. 2.5 times the forward's two. The kernels compute S and
+    dP twice (7 products); the recomputation is not counted."""
+    return 2.5 * metric_flops(B, Hq, Sq, Skv, D, causal)
+
+
+def workload_flops(w):
+    f = metric_flops if w.direction == "fwd" else bwd_metric_flops
+    return f(w.B, w.Hq, w.Sq, w.Skv, w.D, w.causal)
+
+
 def io_bytes(w):
-    """Algorithmic HBM bytes of one call: Q, K, V read once, O written once."""
+    """Algorithmic HBM bytes of one call. Forward: Q, K, V read once, O
+    written once. Backward: Q, K, V, O, dO and the row log-sum-exp read once,
+    dQ, dK, dV written once (and the per-row Delta written and read)."""
     e = ELEM_BYTES[w.dtype]
     o = ELEM_BYTES[w.out_dtype]
-    return (w.B * w.Sq * w.Hq * w.D * (e + o) + 2 * w.B * w.Skv * w.Hkv * w.D * e)
+    nq, nk = w.B * w.Sq * w.Hq * w.D, w.B * w.Skv * w.Hkv * w.D
+    if w.direction == "bwd":
+        rows = w.B * w.Hq * w.Sq
+        return 4 * nq * e + 4 * nk * e + 3 * rows * 4
+    return nq * (e + o) + 2 * nk * e

@@ -36,11 +36,6 @@ def W(dtype, B, Hq, Hkv, Sq, Skv, D, causal, seed=5):
                     causal, seed)
 
 
-def draw_dout(w, seed_offset=1000):
-    g = workload.draw_normal(w.seed + seed_offset, [(w.B, w.Sq, w.Hq, w.D)])[0]
-    return torch.from_numpy(g).to(workload.TORCH_DTYPE[w.dtype])
-
-
 def grad_tol(ref):
     return 2e-2 * max(1.0, float(np.max(np.abs(ref))) if ref.size else 1.0)
 
@@ -116,7 +111,7 @@ BWD_CASES = [
 def test_backward_parity(w):
     print(f"case {w.name}", flush=True)
     q, k, v, _ = workload.make_inputs(w)
-    g = draw_dout(w)
+    g = workload.make_dout(w)
     got = run_backward(w, q, k, v, g)
     want = oracle.sdpa_backward(*(helpers.to_f64(x, w.dtype) for x in (q, k, v, g)), scale=w.scale,
                                 causal=w.causal)
@@ -126,7 +121,7 @@ def test_backward_parity(w):
 def test_backward_negative_and_zero_scale():
     w = W("bf16", 1, 4, 2, 96, 96, 64, True)
     q, k, v, _ = workload.make_inputs(w)
-    g = draw_dout(w)
+    g = workload.make_dout(w)
     for scale in (-0.2, 0.0):
         print(f"scale {scale}", flush=True)
         got = run_backward(w, q, k, v, g, scale=scale)
@@ -151,7 +146,7 @@ def test_backward_no_query_rows_zeroes_dk_dv():
 def test_backward_is_deterministic():
     w = W("bf16", 1, 8, 2, 300, 300, 128, True)
     q, k, v, _ = workload.make_inputs(w)
-    g = draw_dout(w)
+    g = workload.make_dout(w)
     a = run_backward(w, q, k, v, g)
     b = run_backward(w, q, k, v, g)
     for x, y in zip(a, b):
@@ -164,10 +159,10 @@ def test_backward_full_size_headline():
     and the shared K/V head), and two sums that hold exactly for every
     group: the key gradients of a KV head sum to zero over the keys, and its
     value gradients sum to the group's dout summed over the rows."""
-    w = workload.WORKLOADS[workload.HEADLINE]
+    w = workload.WORKLOADS["bf16_gqa_b2_hq32_hkv8_s4096_d128_causal_bwd"]
     print(f"case {w.name}", flush=True)
     q, k, v, _ = workload.make_inputs(w)
-    g = draw_dout(w)
+    g = workload.make_dout(w)
     dq, dk, dv = run_backward(w, q, k, v, g)
     G = w.Hq // w.Hkv
     b, hkv = 1, 5
