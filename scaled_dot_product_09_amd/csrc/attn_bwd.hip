@@ -377,63 +377,95 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams bp) {
         if (t + 2 < n_steps) issue_step(t + 2, qn, gn, sn);
         const int r0 = (qs0 + t % per_head) * BM;
 
+        // Four phases, each a run of MFMAs with operands fetched from LDS two
+        // MFMA pairs ahead (one wave per SIMD: nothing else hides the LDS
+        // latency), and the vector work of one 32-row block riding along the
+        // MFMAs of the other:
+        //   1: S, dP of block 0        2: S, dP of block 1 + weights of block 0
+        //   3: dV, dK of block 0 + weights of block 1        4: dV, dK of block 1
         f32x16 s[NMB], dp[NMB];
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) { s[mb][i] = 0.f; dp[mb][i] = 0.f; }
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-            for (int mb = 0; mb < NMB; ++mb) {
-                const uint32_t o = mb * 32 * ROWB + (qrd ^ (ks << 5));
-                s[mb] = Tr::qk(__builtin_bit_cast(frag, *(const u32x4*)(qt + o)), kf[ks], s[mb]);
-                dp[mb] = Tr::qk(__builtin_bit_cast(frag, *(const u32x4*)(gt + o)), vf[ks], dp[mb]);
-            }
-        }
+
         // Element i of block mb, lane (h, n): query r0 + 32 mb + 8 (i / 4) + 4h + i % 4, key kw0 + n.
         // It is visible iff the key exists, the row exists and (causal) key <= row + coff.
         const bool key_ok = key < Skv;
         uint32_t pw[NMB][8], sw[NMB][8];
+        f32x4 l4[4], d4[4];   // lse and Delta of the rows of the block being weighted
+        auto load_stats = [&](int mb) __attribute__((always_inline)) {
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
+            for (int jj = 0; jj < 4; ++jj) {
+                l4[jj] = *(const f32x4*)&stt[32 * mb + 8 * jj + 4 * h];
+                d4[jj] = *(const f32x4*)&stt[BM + 32 * mb + 8 * jj + 4 * h];
+            }
+        };
+        // Weights P = 2^(c2 s - lse log2 e) and dS = P (dP - Delta) of
+        // elements i0 .. i0 + cnt - 1 of block mb, rounded in pairs.
+        auto weights = [&](int mb, int i0, int cnt) __attribute__((always_inline)) {
             const int qb = r0 + 32 * mb + 4 * h;
             const int qlim = CAUSAL ? key - coff - qb : -(1 << 30);   // offsets >= qlim see the key
             const int qend = Sq - qb;                                  // offsets >= qend do not exist
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const f32x4 l4 = *(const f32x4*)&stt[32 * mb + 8 * jj + 4 * h];
-                const f32x4 d4 = *(const f32x4*)&stt[BM + 32 * mb + 8 * jj + 4 * h];
-                float pr[4], dsr[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int qo = 8 * jj + e;
-                    const int i = 4 * jj + e;
-                    const bool vis = key_ok && qo >= qlim && qo < qend;
-                    pr[e] = vis ? __builtin_amdgcn_exp2f(fmaf(s[mb][i], c2, -l4[e] * kLog2eF)) : 0.f;
-                    dsr[e] = pr[e] * (dp[mb][i] - d4[e]);
-                }
-                pw[mb][2 * jj] = Tr::pack(pr[0], pr[1]);
-                pw[mb][2 * jj + 1] = Tr::pack(pr[2], pr[3]);
-                sw[mb][2 * jj] = Tr::pack(dsr[0], dsr[1]);
-                sw[mb][2 * jj + 1] = Tr::pack(dsr[2], dsr[3]);
+            for (int i = i0; i < i0 + cnt; i += 2) {
+                const int jj = i >> 2, e = i & 3;
+                const int qo = 8 * jj + e;
+                const bool v0 = key_ok && qo >= qlim && qo < qend;
+                const bool v1 = key_ok && qo + 1 >= qlim && qo + 1 < qend;
+                const float p0 = v0 ? __builtin_amdgcn_exp2f(fmaf(s[mb][i], c2, -l4[jj][e] * kLog2eF)) : 0.f;
+                const float p1 = v1 ? __builtin_amdgcn_exp2f(fmaf(s[mb][i + 1], c2, -l4[jj][e + 1] * kLog2eF)) : 0.f;
+                pw[mb][i / 2] = Tr::pack(p0, p1);
+                sw[mb][i / 2] = Tr::pack(p0 * (dp[mb][i] - d4[jj][e]), p1 * (dp[mb][i + 1] - d4[jj][e + 1]));
             }
+        };
+
+        // Phases 1-2: u = mb KSTEPS + ks.
+        constexpr int U = NMB * KSTEPS;
+        constexpr int PER_U = 16 / KSTEPS;                 // elements of block 0 weighted per k-step of block 1
+        auto ldq = [&](int u) __attribute__((always_inline)) {
+            return __builtin_bit_cast(frag, *(const u32x4*)(qt + (u / KSTEPS) * 32 * ROWB + (qrd ^ ((u % KSTEPS) << 5))));
+        };
+        auto ldg = [&](int u) __attribute__((always_inline)) {
+            return __builtin_bit_cast(frag, *(const u32x4*)(gt + (u / KSTEPS) * 32 * ROWB + (qrd ^ ((u % KSTEPS) << 5))));
+        };
+        frag qa[3], ga[3];
+        qa[0] = ldq(0); ga[0] = ldg(0);
+        qa[1] = ldq(1); ga[1] = ldg(1);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (u + 2 < U) { qa[(u + 2) % 3] = ldq(u + 2); ga[(u + 2) % 3] = ldg(u + 2); }
+            const int mb = u / KSTEPS, ks = u % KSTEPS;
+            if (u == KSTEPS) load_stats(0);
+            s[mb] = Tr::qk(qa[u % 3], kf[ks], s[mb]);
+            dp[mb] = Tr::qk(ga[u % 3], vf[ks], dp[mb]);
+            if (mb == 1) weights(0, ks * PER_U, PER_U);
+            __builtin_amdgcn_sched_barrier(0);
         }
+
+        // Phases 3-4: v = (mb 2 + s2) NDB + db.
+        constexpr int V = NMB * 2 * NDB;
+        constexpr int PER_V = 16 / (2 * NDB);              // elements of block 1 weighted per MFMA pair of block 0
+        auto ldt = [&](const uint8_t* tile, int v) __attribute__((always_inline)) {
+            const int mb = v / (2 * NDB), s2 = (v / NDB) % 2, db = v % NDB;
+            return tr_read<frag>(tile + (32 * mb + 16 * s2) * ROWB, tlo[db], thi[db]);
+        };
+        frag tg[3], tq[3];
+        tg[0] = ldt(gt, 0); tq[0] = ldt(qt, 0);
+        tg[1] = ldt(gt, 1); tq[1] = ldt(qt, 1);
+        load_stats(1);
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const frag pa = __builtin_bit_cast(frag, (u32x4){pw[mb][4 * s2], pw[mb][4 * s2 + 1],
-                                                                 pw[mb][4 * s2 + 2], pw[mb][4 * s2 + 3]});
-                const frag sa = __builtin_bit_cast(frag, (u32x4){sw[mb][4 * s2], sw[mb][4 * s2 + 1],
-                                                                 sw[mb][4 * s2 + 2], sw[mb][4 * s2 + 3]});
-                const uint32_t rb = (32 * mb + 16 * s2) * ROWB;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    dv[db] = Tr::qk(pa, tr_read<frag>(gt + rb, tlo[db], thi[db]), dv[db]);
-                    dk[db] = Tr::qk(sa, tr_read<frag>(qt + rb, tlo[db], thi[db]), dk[db]);
-                }
-            }
+        for (int v = 0; v < V; ++v) {
+            if (v + 2 < V) { tg[(v + 2) % 3] = ldt(gt, v + 2); tq[(v + 2) % 3] = ldt(qt, v + 2); }
+            const int mb = v / (2 * NDB), s2 = (v / NDB) % 2, db = v % NDB;
+            const frag pa = __builtin_bit_cast(frag, (u32x4){pw[mb][4 * s2], pw[mb][4 * s2 + 1],
+                                                             pw[mb][4 * s2 + 2], pw[mb][4 * s2 + 3]});
+            const frag sa = __builtin_bit_cast(frag, (u32x4){sw[mb][4 * s2], sw[mb][4 * s2 + 1],
+                                                             sw[mb][4 * s2 + 2], sw[mb][4 * s2 + 3]});
+            dv[db] = Tr::qk(pa, tg[v % 3], dv[db]);
+            dk[db] = Tr::qk(sa, tq[v % 3], dk[db]);
+            if (mb == 0) weights(1, v * PER_V, PER_V);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
