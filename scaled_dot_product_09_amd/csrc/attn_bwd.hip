@@ -177,48 +177,72 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams bp) {
             vdma.issue((j + 1) * BN, Skv, vn, wave);
         }
         if (wave_idle) return;
+        // Four phases with operands fetched from LDS two MFMA pairs ahead,
+        // and the weights of one 32-key block computed alongside the other
+        // block's MFMAs:
+        //   1: S^T, dP^T of block 0     2: S^T, dP^T of block 1 + weights of block 0
+        //   3: dQ^T from block 0 + weights of block 1     4: dQ^T from block 1
         f32x16 s[NKB], dp[NKB];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) { s[kb][i] = 0.f; dp[kb][i] = 0.f; }
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                const frag ka = __builtin_bit_cast(frag, *(const u32x4*)(kt + kb * 32 * ROWB + (krd ^ (ks << 5))));
-                const frag va = __builtin_bit_cast(frag, *(const u32x4*)(vt + kb * 32 * ROWB + (vrd ^ (ks << 5))));
-                s[kb] = Tr::qk(ka, qf[ks], s[kb]);
-                dp[kb] = Tr::qk(va, gf[ks], dp[kb]);
-            }
-        }
         // dS^T = P^T (dP^T - Delta), P^T = 2^(c2 s - lse2) on visible keys,
-        // rounded to the input type in pairs of consecutive keys.
+        // rounded to the input type in pairs of consecutive keys; elements
+        // i0 .. i0 + cnt - 1 of block kb.
         uint32_t pw[NKB][8];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
+        auto weights = [&](int kb, int i0, int cnt) __attribute__((always_inline)) {
             const int key0 = j * BN + kb * 32 + 4 * h;        // key of element i: key0 + 8 (i / 4) + i % 4
             int lim = Skv - 1 - key0;
             if (CAUSAL) lim = min(lim, qrow + coff - key0);
 #pragma unroll
-            for (int i = 0; i < 16; i += 2) {
+            for (int i = i0; i < i0 + cnt; i += 2) {
                 const int ko = 8 * (i >> 2) + (i & 3);
                 const float p0 = ko <= lim ? __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -lse2)) : 0.f;
                 const float p1 = ko + 1 <= lim ? __builtin_amdgcn_exp2f(fmaf(s[kb][i + 1], c2, -lse2)) : 0.f;
                 pw[kb][i / 2] = Tr::pack(p0 * (dp[kb][i] - delta), p1 * (dp[kb][i + 1] - delta));
             }
+        };
+        // Phases 1-2: u = kb KSTEPS + ks.
+        constexpr int U = NKB * KSTEPS;
+        constexpr int PER_U = 16 / KSTEPS;
+        auto ldk = [&](int u) __attribute__((always_inline)) {
+            return __builtin_bit_cast(frag, *(const u32x4*)(kt + (u / KSTEPS) * 32 * ROWB + (krd ^ ((u % KSTEPS) << 5))));
+        };
+        auto ldv = [&](int u) __attribute__((always_inline)) {
+            return __builtin_bit_cast(frag, *(const u32x4*)(vt + (u / KSTEPS) * 32 * ROWB + (vrd ^ ((u % KSTEPS) << 5))));
+        };
+        frag ka[3], va[3];
+        ka[0] = ldk(0); va[0] = ldv(0);
+        ka[1] = ldk(1); va[1] = ldv(1);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (u + 2 < U) { ka[(u + 2) % 3] = ldk(u + 2); va[(u + 2) % 3] = ldv(u + 2); }
+            const int kb = u / KSTEPS, ks = u % KSTEPS;
+            s[kb] = Tr::qk(ka[u % 3], qf[ks], s[kb]);
+            dp[kb] = Tr::qk(va[u % 3], gf[ks], dp[kb]);
+            if (kb == 1) weights(0, ks * PER_U, PER_U);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        // Phases 3-4: v = (kb 2 + s2) NDB + db.
+        constexpr int V = NKB * 2 * NDB;
+        constexpr int PER_V = 16 / (2 * NDB);
+        auto ldt = [&](int v) __attribute__((always_inline)) {
+            const int kb = v / (2 * NDB), s2 = (v / NDB) % 2, db = v % NDB;
+            return tr_read<frag>(kt + (kb * 32 + 16 * s2) * ROWB, tlo[db], thi[db]);
+        };
+        frag ta[3];
+        ta[0] = ldt(0);
+        ta[1] = ldt(1);
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const frag sf = __builtin_bit_cast(frag, (u32x4){pw[kb][4 * s2], pw[kb][4 * s2 + 1],
-                                                                 pw[kb][4 * s2 + 2], pw[kb][4 * s2 + 3]});
-                const uint8_t* base = kt + (kb * 32 + 16 * s2) * ROWB;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    dq[db] = Tr::qk(tr_read<frag>(base, tlo[db], thi[db]), sf, dq[db]);
-            }
+        for (int v = 0; v < V; ++v) {
+            if (v + 2 < V) ta[(v + 2) % 3] = ldt(v + 2);
+            const int kb = v / (2 * NDB), s2 = (v / NDB) % 2, db = v % NDB;
+            const frag sf = __builtin_bit_cast(frag, (u32x4){pw[kb][4 * s2], pw[kb][4 * s2 + 1],
+                                                             pw[kb][4 * s2 + 2], pw[kb][4 * s2 + 3]});
+            dq[db] = Tr::qk(ta[v % 3], sf, dq[db]);
+            if (kb == 0) weights(1, v * PER_V, PER_V);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
