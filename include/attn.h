@@ -248,8 +248,8 @@ int attn_fwd_strided(const void* q, const void* k, const void* v, void* out,
  *             sees get 0)
  *   dtype     ATTN_BF16 or ATTN_F16 (every tensor above but lse)
  *   workspace device buffer of at least attn_bwd_workspace(B, Hq, Sq)
- *             bytes, 16-byte aligned; holds Delta between the two kernels;
- *             contents on entry do not matter
+ *             bytes, 16-byte aligned; holds per-row values between the
+ *             two kernels; contents on entry do not matter
  *   workspace_bytes  its size
  *
  * The outputs and the workspace must not overlap an input or each other
@@ -265,8 +265,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
              float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
              hipStream_t stream);
 
-/* attn_bwd_workspace — bytes of workspace attn_bwd needs: B * Hq * Sq * 4
- * (one float32 Delta per query row); 0 for an empty problem. */
+/* attn_bwd_workspace — bytes of workspace attn_bwd needs: 2 * B * Hq * Sq * 4
+ * (per query row, float32 Delta and lse * log2(e)); 0 for an empty problem. */
 size_t attn_bwd_workspace(int B, int Hq, int Sq);
 
 /* attn_strerror — a static, human-readable description of a status code. */

@@ -399,7 +399,7 @@ extern "C" int attn_fwd_strided(const void* q, const void* k, const void* v, voi
 
 extern "C" size_t attn_bwd_workspace(int B, int Hq, int Sq) {
     if (B <= 0 || Hq <= 0 || Sq <= 0) return 0;
-    return (size_t)B * Hq * Sq * sizeof(float);
+    return (size_t)2 * B * Hq * Sq * sizeof(float);
 }
 
 extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
@@ -454,6 +454,7 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     bp.dout = dout;
     bp.lse = lse;
     bp.delta = (float*)workspace;
+    bp.lse2 = (float*)workspace + (size_t)B * Hq * Sq;
     bp.dq = dq;
     bp.dk = dk;
     bp.dv = dv;

@@ -60,6 +60,20 @@ __device__ inline frag tr_read(const uint8_t* base, uint32_t off_lo, uint32_t of
     return __builtin_bit_cast(frag, (s16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 }
 
+// acc += a b on the matrix cores with acc pinned to the accumulation
+// registers (AGPRs): for accumulators that only matrix instructions touch
+// until the end, so that everything the vector ALU reads can stay in
+// ordinary VGPRs. The leading s_nop covers the wait states between a vector
+// write of a or b (or of acc, at its initialisation) and the MFMA reading
+// it; consecutive uses of one accumulator are always several MFMAs apart.
+template <typename T, typename frag>
+__device__ inline void mfma_agpr(f32x16& acc, frag a, frag b) {
+    if constexpr (std::is_same_v<T, __bf16>)
+        asm("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    else
+        asm("s_nop 4\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -122,8 +136,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams bp) {
     }
     const float delta = xor32_sum(dsum);
     const size_t srow = ((size_t)wi.b * p.Hq + hq) * Sq + qrow;
-    if (row_ok && h == 0) bp.delta[srow] = delta;
     const float lse2 = row_ok ? bp.lse[srow] * kLog2eF : 0.f;
+    if (row_ok && h == 0) {   // for the dK / dV kernel
+        bp.delta[srow] = delta;
+        bp.lse2[srow] = lse2;
+    }
     const float c2 = p.scale_log2;            // scale * log2(e), any sign
     const int coff = p.causal_off;
 
@@ -191,16 +208,34 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams bp) {
         // rounded to the input type in pairs of consecutive keys; elements
         // i0 .. i0 + cnt - 1 of block kb.
         uint32_t pw[NKB][8];
-        auto weights = [&](int kb, int i0, int cnt) __attribute__((always_inline)) {
-            const int key0 = j * BN + kb * 32 + 4 * h;        // key of element i: key0 + 8 (i / 4) + i % 4
-            int lim = Skv - 1 - key0;
-            if (CAUSAL) lim = min(lim, qrow + coff - key0);
+        // Key of element i of block kb: key0 + 8 (i / 4) + i % 4, visible iff
+        // its offset 8 (i / 4) + i % 4 <= lim. Blocks where every element of
+        // every lane is visible (offsets reach 27) skip the test.
+        int lim[NKB];
+        bool masked[NKB];
 #pragma unroll
-            for (int i = i0; i < i0 + cnt; i += 2) {
-                const int ko = 8 * (i >> 2) + (i & 3);
-                const float p0 = ko <= lim ? __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -lse2)) : 0.f;
-                const float p1 = ko + 1 <= lim ? __builtin_amdgcn_exp2f(fmaf(s[kb][i + 1], c2, -lse2)) : 0.f;
-                pw[kb][i / 2] = Tr::pack(p0 * (dp[kb][i] - delta), p1 * (dp[kb][i + 1] - delta));
+        for (int kb = 0; kb < NKB; ++kb) {
+            const int key0 = j * BN + kb * 32 + 4 * h;
+            lim[kb] = Skv - 1 - key0;
+            if (CAUSAL) lim[kb] = min(lim[kb], qrow + coff - key0);
+            masked[kb] = __builtin_amdgcn_ballot_w64(lim[kb] < 27) != 0;
+        }
+        auto weights = [&](int kb, int i0, int cnt) __attribute__((always_inline)) {
+            if (masked[kb]) {
+#pragma unroll
+                for (int i = i0; i < i0 + cnt; i += 2) {
+                    const int ko = 8 * (i >> 2) + (i & 3);
+                    const float p0 = ko <= lim[kb] ? __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -lse2)) : 0.f;
+                    const float p1 = ko + 1 <= lim[kb] ? __builtin_amdgcn_exp2f(fmaf(s[kb][i + 1], c2, -lse2)) : 0.f;
+                    pw[kb][i / 2] = Tr::pack(p0 * (dp[kb][i] - delta), p1 * (dp[kb][i + 1] - delta));
+                }
+            } else {
+#pragma unroll
+                for (int i = i0; i < i0 + cnt; i += 2) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -lse2));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][i + 1], c2, -lse2));
+                    pw[kb][i / 2] = Tr::pack(p0 * (dp[kb][i] - delta), p1 * (dp[kb][i + 1] - delta));
+                }
             }
         };
         // Phases 1-2: u = kb KSTEPS + ks.
@@ -282,6 +317,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams bp) {
     const FwdParams& p = bp.f;
     constexpr int ROWB = D * 2, NC = ROWB / 16, KSTEPS = D / 16, NDB = D / 32;
     constexpr int BM = 64;                             // query rows per step (two 32-row blocks)
+    // With D = 128 the kernel needs more than the 256 VGPRs: dK and dV, which
+    // only MFMAs touch in the loop, live in AGPRs.
+    constexpr bool ACC_AGPR = D == 128;
+    // LDS operands are fetched PF MFMA pairs ahead of their use.
+    constexpr int PF = 3, RING = PF + 1;
     constexpr int NMB = BM / 32;
     constexpr int TILE = BM * ROWB;
     // One LDS object per stage and tensor (see the step body below).
@@ -334,9 +374,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams bp) {
     const int per_head = n_qs - qs0;
     const int n_steps = G * per_head;
 
-    // Copies of one step: the Q and dO tiles (all four waves), the rows' lse
-    // (wave 0) and Delta (wave 1), each lane of those one row (rows past the
-    // end repeat the last row; they are masked).
+    // Copies of one step: the Q and dO tiles (all four waves), the rows'
+    // lse log2(e) (wave 0) and Delta (wave 1), each lane of those one row
+    // (rows past the end repeat the last row; they are masked).
     TileDma<ROWB, BM, 4> qdma, gdma;
     constexpr int NV = 2 * TileDma<ROWB, BM, 4>::PER_WAVE;   // tile copy instructions per wave and step
     static_assert(NV + 1 < 16, "the wait below encodes the count in four bits");
@@ -350,7 +390,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams bp) {
         qdma.issue(r0, Sq, qd, wave);
         gdma.issue(r0, Sq, gd, wave);
         if (wave < 2) {
-            const float* src = (wave == 0 ? bp.lse : bp.delta) + ((size_t)b * p.Hq + hq) * Sq;
+            const float* src = (wave == 0 ? bp.lse2 : bp.delta) + ((size_t)b * p.Hq + hq) * Sq;
             const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, -1, kBufferWord3);
             const uint32_t off = (uint32_t)min(r0 + lane, Sq - 1) * 4;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(sd + wave * BM), 4, off, 0, 0, 0);
@@ -401,7 +441,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams bp) {
         if (t + 2 < n_steps) issue_step(t + 2, qn, gn, sn);
         const int r0 = (qs0 + t % per_head) * BM;
 
-        // Four phases, each a run of MFMAs with operands fetched from LDS two
+        // Four phases, each a run of MFMAs with operands fetched from LDS PF
         // MFMA pairs ahead (one wave per SIMD: nothing else hides the LDS
         // latency), and the vector work of one 32-row block riding along the
         // MFMAs of the other:
@@ -417,30 +457,45 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams bp) {
         // It is visible iff the key exists, the row exists and (causal) key <= row + coff.
         const bool key_ok = key < Skv;
         uint32_t pw[NMB][8], sw[NMB][8];
-        f32x4 l4[4], d4[4];   // lse and Delta of the rows of the block being weighted
+        // Weights P = 2^(c2 s - lse log2 e) and dS = P (dP - Delta) of
+        // elements i0 .. i0 + cnt - 1 of block mb, rounded in pairs.
+        // Row offsets (8 (i / 4) + i % 4, up to 27) at or above qlim see the
+        // key; at or above qend the row does not exist. Blocks where no lane
+        // has a hidden element skip the test.
+        int qlim[NMB], qend[NMB];
+        bool masked[NMB];
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+            const int qb = r0 + 32 * mb + 4 * h;
+            qlim[mb] = CAUSAL ? key - coff - qb : -(1 << 30);
+            qend[mb] = key_ok ? Sq - qb : -(1 << 30);
+            masked[mb] = __builtin_amdgcn_ballot_w64(qlim[mb] > 0 || qend[mb] <= 27) != 0;
+        }
+        // The rows' lse log2(e) and Delta: four 16-byte LDS reads per block,
+        // issued ahead of the weights that use them.
+        f32x4 lst[NMB][4], dst[NMB][4];
         auto load_stats = [&](int mb) __attribute__((always_inline)) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                l4[jj] = *(const f32x4*)&stt[32 * mb + 8 * jj + 4 * h];
-                d4[jj] = *(const f32x4*)&stt[BM + 32 * mb + 8 * jj + 4 * h];
+                lst[mb][jj] = *(const f32x4*)&stt[32 * mb + 8 * jj + 4 * h];
+                dst[mb][jj] = *(const f32x4*)&stt[BM + 32 * mb + 8 * jj + 4 * h];
             }
         };
         // Weights P = 2^(c2 s - lse log2 e) and dS = P (dP - Delta) of
         // elements i0 .. i0 + cnt - 1 of block mb, rounded in pairs.
         auto weights = [&](int mb, int i0, int cnt) __attribute__((always_inline)) {
-            const int qb = r0 + 32 * mb + 4 * h;
-            const int qlim = CAUSAL ? key - coff - qb : -(1 << 30);   // offsets >= qlim see the key
-            const int qend = Sq - qb;                                  // offsets >= qend do not exist
 #pragma unroll
             for (int i = i0; i < i0 + cnt; i += 2) {
                 const int jj = i >> 2, e = i & 3;
-                const int qo = 8 * jj + e;
-                const bool v0 = key_ok && qo >= qlim && qo < qend;
-                const bool v1 = key_ok && qo + 1 >= qlim && qo + 1 < qend;
-                const float p0 = v0 ? __builtin_amdgcn_exp2f(fmaf(s[mb][i], c2, -l4[jj][e] * kLog2eF)) : 0.f;
-                const float p1 = v1 ? __builtin_amdgcn_exp2f(fmaf(s[mb][i + 1], c2, -l4[jj][e + 1] * kLog2eF)) : 0.f;
+                float p0 = __builtin_amdgcn_exp2f(fmaf(s[mb][i], c2, -lst[mb][jj][e]));
+                float p1 = __builtin_amdgcn_exp2f(fmaf(s[mb][i + 1], c2, -lst[mb][jj][e + 1]));
+                if (masked[mb]) {
+                    const int qo = 8 * jj + e;
+                    p0 = (qo >= qlim[mb] && qo < qend[mb]) ? p0 : 0.f;
+                    p1 = (qo + 1 >= qlim[mb] && qo + 1 < qend[mb]) ? p1 : 0.f;
+                }
                 pw[mb][i / 2] = Tr::pack(p0, p1);
-                sw[mb][i / 2] = Tr::pack(p0 * (dp[mb][i] - d4[jj][e]), p1 * (dp[mb][i + 1] - d4[jj][e + 1]));
+                sw[mb][i / 2] = Tr::pack(p0 * (dp[mb][i] - dst[mb][jj][e]), p1 * (dp[mb][i + 1] - dst[mb][jj][e + 1]));
             }
         };
 
@@ -453,17 +508,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams bp) {
         auto ldg = [&](int u) __attribute__((always_inline)) {
             return __builtin_bit_cast(frag, *(const u32x4*)(gt + (u / KSTEPS) * 32 * ROWB + (qrd ^ ((u % KSTEPS) << 5))));
         };
-        frag qa[3], ga[3];
-        qa[0] = ldq(0); ga[0] = ldg(0);
-        qa[1] = ldq(1); ga[1] = ldg(1);
+        frag qa[RING], ga[RING];
+#pragma unroll
+        for (int u = 0; u < PF; ++u) { qa[u] = ldq(u); ga[u] = ldg(u); }
+        load_stats(0);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (u + 2 < U) { qa[(u + 2) % 3] = ldq(u + 2); ga[(u + 2) % 3] = ldg(u + 2); }
+            if (u + PF < U) { qa[(u + PF) % RING] = ldq(u + PF); ga[(u + PF) % RING] = ldg(u + PF); }
             const int mb = u / KSTEPS, ks = u % KSTEPS;
-            if (u == KSTEPS) load_stats(0);
-            s[mb] = Tr::qk(qa[u % 3], kf[ks], s[mb]);
-            dp[mb] = Tr::qk(ga[u % 3], vf[ks], dp[mb]);
-            if (mb == 1) weights(0, ks * PER_U, PER_U);
+            s[mb] = Tr::qk(qa[u % RING], kf[ks], s[mb]);
+            dp[mb] = Tr::qk(ga[u % RING], vf[ks], dp[mb]);
+            if (mb == 1) {
+                weights(0, ks * PER_U, PER_U);
+                if (ks == KSTEPS - 1) load_stats(1);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
 
@@ -474,20 +532,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams bp) {
             const int mb = v / (2 * NDB), s2 = (v / NDB) % 2, db = v % NDB;
             return tr_read<frag>(tile + (32 * mb + 16 * s2) * ROWB, tlo[db], thi[db]);
         };
-        frag tg[3], tq[3];
-        tg[0] = ldt(gt, 0); tq[0] = ldt(qt, 0);
-        tg[1] = ldt(gt, 1); tq[1] = ldt(qt, 1);
-        load_stats(1);
+        frag tg[RING], tq[RING];
+#pragma unroll
+        for (int v = 0; v < PF; ++v) { tg[v] = ldt(gt, v); tq[v] = ldt(qt, v); }
 #pragma unroll
         for (int v = 0; v < V; ++v) {
-            if (v + 2 < V) { tg[(v + 2) % 3] = ldt(gt, v + 2); tq[(v + 2) % 3] = ldt(qt, v + 2); }
+            if (v + PF < V) { tg[(v + PF) % RING] = ldt(gt, v + PF); tq[(v + PF) % RING] = ldt(qt, v + PF); }
             const int mb = v / (2 * NDB), s2 = (v / NDB) % 2, db = v % NDB;
             const frag pa = __builtin_bit_cast(frag, (u32x4){pw[mb][4 * s2], pw[mb][4 * s2 + 1],
                                                              pw[mb][4 * s2 + 2], pw[mb][4 * s2 + 3]});
             const frag sa = __builtin_bit_cast(frag, (u32x4){sw[mb][4 * s2], sw[mb][4 * s2 + 1],
                                                              sw[mb][4 * s2 + 2], sw[mb][4 * s2 + 3]});
-            dv[db] = Tr::qk(pa, tg[v % 3], dv[db]);
-            dk[db] = Tr::qk(sa, tq[v % 3], dk[db]);
+            if constexpr (ACC_AGPR) {
+                mfma_agpr<T>(dv[db], pa, tg[v % RING]);
+                mfma_agpr<T>(dk[db], sa, tq[v % RING]);
+            } else {
+                dv[db] = Tr::qk(pa, tg[v % RING], dv[db]);
+                dk[db] = Tr::qk(sa, tq[v % RING], dk[db]);
+            }
             if (mb == 0) weights(1, v * PER_V, PER_V);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -504,6 +566,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams bp) {
     if (t < n_steps) step(t, lds_q0, lds_g0, lds_s0, lds_q2, lds_g2, lds_s2);
     if (t + 1 < n_steps) step(t + 1, lds_q1, lds_g1, lds_s1, lds_q0, lds_g0, lds_s0);
     __builtin_amdgcn_s_waitcnt(0x0F70);
+    if constexpr (ACC_AGPR) {
+        // Wait states between the last MFMA writing the accumulators and the
+        // vector reads below (more than the 32x32 MFMA's write latency).
+        static_assert(NDB == 4, "");
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+a"(dk[0]), "+a"(dk[1]), "+a"(dk[2]), "+a"(dk[3]),
+                       "+a"(dv[0]), "+a"(dv[1]), "+a"(dv[2]), "+a"(dv[3]));
+    }
 
     // Element i of the accumulators: key kw0 + 8 (i / 4) + 4h + i % 4, column 32 db + n.
     const float sc = bp.scale;

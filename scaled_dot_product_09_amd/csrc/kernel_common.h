@@ -54,6 +54,7 @@ struct BwdParams {
     const void* dout;   // (B, Sq, Hq, D) gradient of the loss with respect to out
     const float* lse;   // [B][Hq][Sq] natural-log row log-sum-exp from the forward
     float* delta;       // [B][Hq][Sq] workspace: rowsum(dout * out), written by the dQ kernel
+    float* lse2;        // [B][Hq][Sq] workspace: lse * log2(e), written by the dQ kernel
     void* dq;           // (B, Sq, Hq, D)
     void* dk;           // (B, Skv, Hkv, D)
     void* dv;           // (B, Skv, Hkv, D)

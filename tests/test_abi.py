@@ -119,7 +119,7 @@ def test_bwd_rejected_before_launch(kw, status):
 
 
 def test_bwd_workspace_size():
-    assert attn.attn_bwd_workspace(2, 8, 64) == 2 * 8 * 64 * 4
+    assert attn.attn_bwd_workspace(2, 8, 64) == 2 * 2 * 8 * 64 * 4
     assert attn.attn_bwd_workspace(0, 8, 64) == 0
     assert attn.attn_bwd_workspace(2, 8, 0) == 0
 
