@@ -42,6 +42,9 @@ from .codecs import (
     f64_to_bf16_bits,
     f64_to_e4m3_bits,
     e4m3_amax_scale,
+    e5m2_bits_to_f64,
+    f64_to_e5m2_bits,
+    e5m2_amax_scale,
 )
 
 __all__ = [
@@ -60,4 +63,7 @@ __all__ = [
     "f64_to_bf16_bits",
     "f64_to_e4m3_bits",
     "e4m3_amax_scale",
+    "e5m2_bits_to_f64",
+    "f64_to_e5m2_bits",
+    "e5m2_amax_scale",
 ]

@@ -17,6 +17,13 @@ library's interpretation of them:
   maximum of the abs-max history; a single forward call has a one-entry
   history, so the scale is 448 / amax(|x|), with amax == 0 giving scale 1.
 
+* E5M2 [Attention codelab §10]: 5 exponent bits and 2 mantissa bits, the
+  FP8 format the codelab names for the backward pass (gradients). Reading
+  taken: the OCP 8-bit floating point specification's E5M2, an IEEE-style
+  format: exponent bias 15, subnormals, infinities at S.11111.00, NaN at
+  S.11111.{01,10,11}, largest finite magnitude 57344. Its per-tensor scale
+  follows the same recipe as E4M3's: s = 57344 / amax(|x|).
+
 Every function is pinned in ``tests/test_codecs.py`` (all 65536 / 256 codes,
 closed forms, and a cross-check against torch's own converters).
 """
@@ -31,9 +38,14 @@ __all__ = [
     "f64_to_e4m3_bits",
     "e4m3_amax_scale",
     "E4M3_MAX",
+    "e5m2_bits_to_f64",
+    "f64_to_e5m2_bits",
+    "e5m2_amax_scale",
+    "E5M2_MAX",
 ]
 
 E4M3_MAX = 448.0
+E5M2_MAX = 57344.0
 
 
 def bf16_bits_to_f64(bits):
@@ -132,3 +144,52 @@ def e4m3_amax_scale(x):
     if amax == 0 or not np.isfinite(amax):
         return np.float32(1.0)
     return np.float32(np.float32(E4M3_MAX) / amax)
+
+
+def e5m2_bits_to_f64(bits):
+    """Decode OCP E5M2 codes to float64 from the field definitions.
+
+    value = (-1)^s * 2^(e-15) * (1 + m/4) for e in 1..30, (-1)^s * 2^-14 * (m/4)
+    for e == 0; e == 31 is infinity (m == 0) or NaN (m != 0).
+    """
+    b = np.asarray(bits).astype(np.int64) & 0xFF
+    sign = np.where((b >> 7) & 1, -1.0, 1.0)
+    e = (b >> 2) & 0x1F
+    m = (b & 0x3).astype(np.float64)
+    sub = sign * (m / 4.0) * 2.0 ** -14
+    nor = sign * (1.0 + m / 4.0) * np.exp2(e.astype(np.float64) - 15.0)
+    special = np.where(m == 0, sign * np.inf, np.nan)
+    return np.where(e == 0, sub, np.where(e == 31, special, nor))
+
+
+def f64_to_e5m2_bits(x):
+    """Encode values to E5M2 codes: nearest, ties to even code, saturating.
+
+    Among the finite E5M2 magnitudes pick the one nearest |x|; on a tie the
+    code whose lowest bit is 0; magnitudes beyond 57344 (infinities included)
+    saturate to 57344, as a scaled gradient must stay finite. NaN maps to
+    the NaN code S.11111.10.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    table = e5m2_bits_to_f64(np.arange(0x7C))          # the 124 finite non-negative values, by code
+    a = np.minimum(np.abs(x), E5M2_MAX)
+    a = np.where(np.isnan(a), 0.0, a)
+    hi = np.clip(np.searchsorted(table, a, side="left"), 0, len(table) - 1)
+    lo = np.clip(hi - 1, 0, len(table) - 1)
+    dlo = a - table[lo]
+    dhi = table[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a == table[hi], hi, code)
+    code = np.where(np.isnan(x), 0x7E, code)
+    sign = np.where(np.signbit(x), 0x80, 0)
+    return (code | sign).astype(np.uint8)
+
+
+def e5m2_amax_scale(x):
+    """Per-tensor quantisation scale s = 57344 / amax(|x|) as binary32
+    (amax == 0 gives 1); the dequantisation factor is 1 / s."""
+    amax = np.float32(np.max(np.abs(np.asarray(x, dtype=np.float32)))) if np.size(x) else np.float32(0)
+    if amax == 0 or not np.isfinite(amax):
+        return np.float32(1.0)
+    return np.float32(np.float32(E5M2_MAX) / amax)

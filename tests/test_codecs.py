@@ -1,8 +1,9 @@
 """The oracle's number-format codecs against the format definitions and torch.
 
-bfloat16 and float16 decode every one of the 65536 codes; E4M3 decodes all
-256 codes and is checked against the OCP E4M3 ("E4M3FN") definition at its
-landmark codes and against torch.float8_e4m3fn everywhere. The seeded input
+bfloat16 and float16 decode every one of the 65536 codes; E4M3 and E5M2
+decode all 256 codes and are checked against the OCP definitions at their
+landmark codes and against torch.float8_e4m3fn / torch.float8_e5m2
+everywhere. The seeded input
 generator's quantisation is checked against the oracle's own encoder.
 """
 
@@ -118,3 +119,47 @@ def test_generator_bf16_rounding_matches_oracle_encoder():
     q, k, v, _ = workload.make_inputs(w, shapes=shapes)
     for t, x in zip((q, k, v), workload.draw_normal(w.seed, shapes)):
         assert np.array_equal(t.view(torch.int16).numpy().view(np.uint16), oracle.f64_to_bf16_bits(x))
+
+
+def test_e5m2_decode_landmarks():
+    d = oracle.e5m2_bits_to_f64
+    assert d(0x3C) == 1.0                          # exponent field 15 = bias
+    assert d(0x7B) == 57344.0                      # S.11110.11, the largest finite: 1.75 * 2^15
+    assert d(0x04) == 2.0 ** -14                   # smallest normal
+    assert d(0x03) == 3 * 2.0 ** -16               # largest subnormal
+    assert d(0x01) == 2.0 ** -16                   # smallest subnormal
+    assert d(0x00) == 0.0 and np.signbit(d(0x80))
+    assert d(0x7C) == np.inf and d(0xFC) == -np.inf
+    assert np.isnan(d(0x7D)) and np.isnan(d(0x7E)) and np.isnan(d(0xFF))
+    assert d(0xBE) == -1.5
+    assert np.sum(np.isnan(d(np.arange(256)))) == 6 and np.sum(np.isinf(d(np.arange(256)))) == 2
+
+
+def test_e5m2_decode_all_codes_vs_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e5m2).double().numpy()
+    _same(oracle.e5m2_bits_to_f64(codes), ref)
+
+
+def test_e5m2_encode_roundtrip_ties_saturation():
+    codes = np.array([c for c in range(256) if (c & 0x7F) < 0x7C], dtype=np.uint8)
+    assert np.array_equal(oracle.f64_to_e5m2_bits(oracle.e5m2_bits_to_f64(codes)), codes)
+    e = oracle.f64_to_e5m2_bits
+    assert e(1.125) == 0x3C           # halfway between 1 (even code) and 1.25 -> 1
+    assert e(1.375) == 0x3E           # halfway between 1.25 and 1.5 (even) -> 1.5
+    assert e(2.0 ** -17) == 0x00      # halfway between 0 and 2^-16 -> 0 (even)
+    assert e(3 * 2.0 ** -17) == 0x02  # halfway between 2^-16 and 2^-15 -> 2^-15 (even)
+    assert e(61440.0) == 0x7B and e(1e9) == 0x7B and e(-np.inf) == 0xFB   # saturate to 57344
+
+
+def test_e5m2_encode_vs_torch():
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal(100000) * 1000).astype(np.float32)
+    x = np.clip(x, -57344, 57344)
+    ref = torch.from_numpy(x).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.f64_to_e5m2_bits(x), ref)
+
+
+def test_e5m2_amax_scale():
+    assert codecs.e5m2_amax_scale(np.array([0.5, -7.0], np.float32)) == np.float32(8192.0)
+    assert codecs.e5m2_amax_scale(np.zeros(3, np.float32)) == np.float32(1.0)
