@@ -127,18 +127,28 @@ def time_workload(w, steps, warmup, rotate=True, settle_s=SETTLE_S):
 
     if w.direction == "bwd":
         # Backward: the forward's out and lse are made once per input set,
-        # outside the timed region; a step is one attn_bwd call.
-        g = workload.make_dout(w).to(dev)
+        # outside the timed region; a step is one attn_bwd (attn_bwd_fp8 for
+        # E4M3 inputs with an E5M2 gradient) call.
+        g = workload.make_dout(w)
+        bdesc = None
+        if fp8:
+            g, gdesc = g
+            bdesc = (*desc, gdesc)
+        g = g.to(dev)
         bsets = []
         for qd, kd, vd, od in sets:
-            od, lse = attn.fwd_lse(qd, kd, vd, causal=w.causal, scale=w.scale, out=od)
-            bsets.append((qd, kd, vd, od, lse, torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)))
-        bws = torch.empty(max(attn.attn_bwd_workspace(w.B, w.Hq, w.Sq), 16), dtype=torch.uint8, device=dev)
+            od, lse = attn.fwd_lse(qd, kd, vd, causal=w.causal, scale=w.scale, out=od,
+                                   descales=desc if fp8 else None)
+            bsets.append((qd, kd, vd, od, lse, torch.empty_like(od), torch.empty(kd.shape, dtype=od.dtype, device=dev),
+                          torch.empty(vd.shape, dtype=od.dtype, device=dev)))
+        need = (attn.attn_bwd_fp8_workspace(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D) if fp8
+                else attn.attn_bwd_workspace(w.B, w.Hq, w.Sq))
+        bws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
 
         def step(i):  # noqa: F811
             qd, kd, vd, od, lse, dq, dk, dv = bsets[i % nsets]
             attn.bwd(qd, kd, vd, od, g, lse, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=bws,
-                     stream=stream.cuda_stream)
+                     stream=stream.cuda_stream, descales=bdesc)
 
     for i in range(warmup):
         step(i)
@@ -170,7 +180,10 @@ def result_line(w, t, steps, warmup, n_gpus, cpu=None, warm=None):
     flops = workload_flops(w)
     ms = t["ms_per_step"]
     tflops = flops / (ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[w.dtype]
+    # The products' arithmetic type: the FP8 backward widens its codes and
+    # multiplies in bf16.
+    compute = "bf16" if (w.direction == "bwd" and w.dtype == "e4m3") else w.dtype
+    peak = PEAK_TFLOPS[compute]
     nbytes = io_bytes(w)
     gbps = nbytes / (ms * 1e-3) / 1e9
     # Below the ridge point (peak flop/s over peak HBM bytes/s) the kernel is
@@ -180,7 +193,7 @@ def result_line(w, t, steps, warmup, n_gpus, cpu=None, warm=None):
         roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(gbps / PEAK_HBM_GBPS, 4)}
     else:
-        roof = {"bound": PEAK_KIND[w.dtype], "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+        roof = {"bound": PEAK_KIND[compute], "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(tflops / peak, 4)}
     roof.update({"traffic": load_traffic(w.name), "algorithmic_bytes": nbytes})
     line = {

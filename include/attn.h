@@ -159,6 +159,19 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* out,
                  hipStream_t stream);
 
 /*
+ * attn_fwd_fp8_lse — attn_fwd_fp8 that also stores the row log-sum-exp of
+ * the scaled scores on the dequantised inputs (scale * q_descale * k_descale
+ * * q.k), as attn_fwd_lse does: float32 [B][Hq][Sq], 4-byte aligned, not
+ * overlapping q, k, v or out. Arguments and errors otherwise as
+ * attn_fwd_fp8; the output equals attn_fwd_fp8's bit for bit.
+ */
+int attn_fwd_fp8_lse(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                     float scale, int causal,
+                     float q_descale, float k_descale, float v_descale,
+                     hipStream_t stream);
+
+/*
  * attn_fwd_split — attn_fwd with the keys of every query row cut into
  * n_split contiguous ranges that separate workgroups process, followed by a
  * combine kernel (split-key or "flash-decoding" form). For grids too small
@@ -268,6 +281,38 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
 /* attn_bwd_workspace — bytes of workspace attn_bwd needs: 2 * B * Hq * Sq * 4
  * (per query row, float32 Delta and lse * log2(e)); 0 for an empty problem. */
 size_t attn_bwd_workspace(int B, int Hq, int Sq);
+
+/*
+ * attn_bwd_fp8 — attn_bwd for the FP8 forward: q, k, v are the E4M3 codes
+ * attn_fwd_fp8 took, and the incoming gradient dout is in E5M2, the FP8
+ * format the codelab's §10 names for the backward pass (gradients): OCP
+ * E5M2, bias 15, largest finite 57344, with infinities and NaNs. Each has a
+ * per-tensor dequantisation factor (real value = code * descale), so the
+ * gradients are those of attn_bwd on q_descale * q, k_descale * k,
+ * v_descale * v and do_descale * dout.
+ *
+ *   out       attn_fwd_fp8's output (bfloat16), [B][Sq][Hq][D]
+ *   lse       attn_fwd_fp8_lse's row log-sum-exp, float32 [B][Hq][Sq]
+ *   dq, dk, dv  outputs, bfloat16, shapes of q, k, v
+ *   *_descale finite float32 factors
+ *   workspace at least attn_bwd_fp8_workspace(...) bytes, 16-byte aligned
+ *
+ * Every code is first widened to bfloat16 (exactly: both formats' values
+ * are bfloat16 values) into the workspace; the products then run as in
+ * attn_bwd on the codes, with the descales folded into the score scale, into
+ * dP and Delta, and into the final factors of dq, dk and dv. D is 64 or
+ * 128, as for attn_fwd_fp8. Other arguments and errors as attn_bwd.
+ */
+int attn_bwd_fp8(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv,
+                 int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale, int causal,
+                 float q_descale, float k_descale, float v_descale, float do_descale,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* attn_bwd_fp8_workspace — bytes of workspace attn_bwd_fp8 needs: bfloat16
+ * copies of q, k, v and dout (each padded to a multiple of 256 bytes) and
+ * attn_bwd_workspace(B, Hq, Sq); 0 for an empty problem. */
+size_t attn_bwd_fp8_workspace(int B, int Hq, int Hkv, int Sq, int Skv, int D);
 
 /* attn_strerror — a static, human-readable description of a status code. */
 const char* attn_strerror(int status);

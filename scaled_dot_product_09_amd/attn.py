@@ -9,8 +9,8 @@ raised.
 
 The names follow include/attn.h: ``attn_fwd``, ``attn_fwd_lse``, ``attn_fwd_fp8``,
 ``attn_fwd_split``, ``attn_split_workspace``, ``attn_split_suggest``,
-``attn_fwd_strided``, ``attn_bwd``, ``attn_bwd_workspace``,
-``attn_strerror``; :func:`fwd`, :func:`fwd_lse` and :func:`bwd` are the
+``attn_fwd_strided``, ``attn_bwd``, ``attn_bwd_workspace``, ``attn_fwd_fp8_lse``,
+``attn_bwd_fp8``, ``attn_bwd_fp8_workspace``, ``attn_strerror``; :func:`fwd`, :func:`fwd_lse` and :func:`bwd` are the
 tensor-level convenience wrappers.
 """
 
@@ -24,14 +24,16 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libattn.so")
 
 ATTN_F32, ATTN_BF16, ATTN_F16, ATTN_FP8_E4M3 = 0, 1, 2, 3
+FP8_GRAD_DTYPE = torch.float8_e5m2   # gradient input of attn_bwd_fp8
 DTYPE_CODE = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16,
               torch.float8_e4m3fn: ATTN_FP8_E4M3}
 STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_GROUP",
           -4: "ATTN_ERR_HEAD_DIM", -5: "ATTN_ERR_DTYPE", -6: "ATTN_ERR_ALIGN", -7: "ATTN_ERR_ALIAS",
           -8: "ATTN_ERR_SCALE", -9: "ATTN_ERR_HIP", -10: "ATTN_ERR_CAUSAL", -11: "ATTN_ERR_SPLIT",
           -12: "ATTN_ERR_WORKSPACE", -13: "ATTN_ERR_STRIDE"}
-EXPORTS = ("attn_fwd", "attn_fwd_lse", "attn_fwd_fp8", "attn_fwd_split", "attn_split_workspace", "attn_split_suggest",
-           "attn_fwd_strided", "attn_bwd", "attn_bwd_workspace", "attn_strerror")
+EXPORTS = ("attn_fwd", "attn_fwd_lse", "attn_fwd_fp8", "attn_fwd_fp8_lse", "attn_fwd_split", "attn_split_workspace", "attn_split_suggest",
+           "attn_fwd_strided", "attn_bwd", "attn_bwd_workspace", "attn_bwd_fp8", "attn_bwd_fp8_workspace",
+           "attn_strerror")
 # causal argument: 0 none, 1 lower triangle (top-left), 2 bottom-right (Sq <= Skv)
 CAUSAL_CODE = {False: 0, True: 1, "top_left": 1, "bottom_right": 2, 0: 0, 1: 1, 2: 2}
 
@@ -56,6 +58,12 @@ def lib():
         L.attn_fwd.restype = i
         L.attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
         L.attn_fwd_lse.restype = i
+        L.attn_fwd_fp8_lse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, f, f, f, vp]
+        L.attn_fwd_fp8_lse.restype = i
+        L.attn_bwd_fp8.argtypes = [vp] * 9 + [i, i, i, i, i, i, f, i, f, f, f, f, vp, ctypes.c_size_t, vp]
+        L.attn_bwd_fp8.restype = i
+        L.attn_bwd_fp8_workspace.argtypes = [i, i, i, i, i, i]
+        L.attn_bwd_fp8_workspace.restype = ctypes.c_size_t
         L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, f, f, f, vp]
         L.attn_fwd_fp8.restype = i
         L.attn_fwd_split.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, ctypes.c_size_t, vp]
@@ -131,6 +139,25 @@ def attn_bwd_workspace(B, Hq, Sq):
     return int(lib().attn_bwd_workspace(B, Hq, Sq))
 
 
+def attn_fwd_fp8_lse(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, q_descale, k_descale, v_descale,
+                     stream):
+    """Raw C call of the E4M3 forward with the row log-sum-exp output, returns the status code."""
+    return lib().attn_fwd_fp8_lse(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, float(scale), int(causal),
+                                  float(q_descale), float(k_descale), float(v_descale), stream)
+
+
+def attn_bwd_fp8(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, scale, causal, q_descale,
+                 k_descale, v_descale, do_descale, workspace, workspace_bytes, stream):
+    """Raw C call of the FP8 (E4M3 inputs, E5M2 gradient) backward pass, returns the status code."""
+    return lib().attn_bwd_fp8(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, float(scale),
+                              int(causal), float(q_descale), float(k_descale), float(v_descale),
+                              float(do_descale), workspace, int(workspace_bytes), stream)
+
+
+def attn_bwd_fp8_workspace(B, Hq, Hkv, Sq, Skv, D):
+    return int(lib().attn_bwd_fp8_workspace(B, Hq, Hkv, Sq, Skv, D))
+
+
 def _check(st):
     if st != 0:
         raise AttnError(st, attn_strerror(st))
@@ -154,31 +181,38 @@ def _causal_code(causal):
     return CAUSAL_CODE[causal]
 
 
-def fwd_lse(q, k, v, *, causal=False, scale=None, out=None, lse=None, stream=None):
+def fwd_lse(q, k, v, *, causal=False, scale=None, out=None, lse=None, stream=None, descales=None):
     """(out, lse): the forward of :func:`fwd` plus the float32 row log-sum-exp
     lse[b, h, i] = log sum_j exp(scale q.k) over the visible keys, shape
-    (B, Hq, Sq). Contiguous float32 / bfloat16 / float16 tensors."""
+    (B, Hq, Sq). Contiguous float32 / bfloat16 / float16 tensors, or
+    float8_e4m3fn with ``descales`` = (q, k, v) factors (bfloat16 output)."""
     _check_qkv(q, k, v)
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("fwd_lse takes contiguous (B, S, H, D) tensors")
-    if q.dtype == torch.float8_e4m3fn:
-        raise ValueError("fwd_lse takes float32, bfloat16 or float16")
+    fp8 = q.dtype == torch.float8_e4m3fn
+    if fp8 and descales is None:
+        raise ValueError("E4M3 inputs need descales=(q_descale, k_descale, v_descale)")
     B, Sq, Hq, D = q.shape
     Skv, Hkv = k.shape[1], k.shape[2]
     causal = _causal_code(causal)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
+    out_dtype = torch.bfloat16 if fp8 else q.dtype
     if out is None:
-        out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor of q's shape, dtype and device")
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    elif out.shape != q.shape or out.dtype != out_dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of q's shape and device, in the output dtype")
     if lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     elif lse.shape != (B, Hq, Sq) or lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 (B, Hq, Sq) tensor on q's device")
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    _check(attn_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                        B, Hq, Hkv, Sq, Skv, D, scale, causal, DTYPE_CODE[q.dtype], stream))
+    if fp8:
+        _check(attn_fwd_fp8_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                B, Hq, Hkv, Sq, Skv, D, scale, causal, *descales, stream))
+    else:
+        _check(attn_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                            B, Hq, Hkv, Sq, Skv, D, scale, causal, DTYPE_CODE[q.dtype], stream))
     return out, lse
 
 
@@ -255,23 +289,32 @@ def fwd(q, k, v, *, causal=False, scale=None, out=None, descales=None, stream=No
 
 
 def bwd(q, k, v, out, dout, lse, *, causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None,
-        stream=None):
+        stream=None, descales=None):
     """(dq, dk, dv): gradients of sum(dout * out) for out = fwd(q, k, v).
 
     ``out`` and ``lse`` come from :func:`fwd_lse` on the same inputs with the
     same ``causal`` and ``scale``; ``dout`` has out's shape. Contiguous
     bfloat16 / float16 tensors on one GPU; the gradients have the inputs'
-    shapes and dtype. ``workspace`` is a uint8 device tensor of at least
-    attn_bwd_workspace(B, Hq, Sq) bytes (allocated here if None).
+    shapes and dtype. FP8: q, k, v float8_e4m3fn, out bfloat16, dout
+    float8_e5m2, ``descales`` = (q, k, v, dout) factors; bfloat16 gradients
+    (attn_bwd_fp8). ``workspace`` is a uint8 device tensor of at least
+    attn_bwd_workspace(B, Hq, Sq) (FP8: attn_bwd_fp8_workspace(...)) bytes,
+    allocated here if None.
     """
     _check_qkv(q, k, v)
-    if q.dtype not in (torch.bfloat16, torch.float16):
-        raise ValueError("the backward pass takes bfloat16 or float16 tensors")
+    fp8 = q.dtype == torch.float8_e4m3fn
+    if not fp8 and q.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("the backward pass takes bfloat16, float16 or E4M3 (with an E5M2 dout) tensors")
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout), ("lse", lse)):
         if not t.is_contiguous() or t.device != q.device:
             raise ValueError(f"{name} must be contiguous and on q's device")
-    if out.shape != q.shape or dout.shape != q.shape or out.dtype != q.dtype or dout.dtype != q.dtype:
-        raise ValueError("out and dout must have q's shape and dtype")
+    out_dtype = torch.bfloat16 if fp8 else q.dtype
+    do_dtype = FP8_GRAD_DTYPE if fp8 else q.dtype
+    if out.shape != q.shape or dout.shape != q.shape or out.dtype != out_dtype or dout.dtype != do_dtype:
+        raise ValueError("out and dout must have q's shape; out in the forward's output dtype, dout in q's "
+                         "dtype (float8_e5m2 for E4M3 inputs)")
+    if fp8 and (descales is None or len(descales) != 4):
+        raise ValueError("E4M3 inputs need descales=(q_descale, k_descale, v_descale, dout_descale)")
     B, Sq, Hq, D = q.shape
     Skv, Hkv = k.shape[1], k.shape[2]
     if lse.shape != (B, Hq, Sq) or lse.dtype != torch.float32:
@@ -281,11 +324,12 @@ def bwd(q, k, v, out, dout, lse, *, causal=False, scale=None, dq=None, dk=None, 
     grads = []
     for name, g, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
         if g is None:
-            g = torch.empty_like(ref)
-        elif g.shape != ref.shape or g.dtype != ref.dtype or g.device != ref.device or not g.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous tensor of its input's shape, dtype and device")
+            g = torch.empty(ref.shape, dtype=out_dtype, device=ref.device)
+        elif g.shape != ref.shape or g.dtype != out_dtype or g.device != ref.device or not g.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor of its input's shape and device, in the "
+                             "gradient dtype")
         grads.append(g)
-    need = attn_bwd_workspace(B, Hq, Sq)
+    need = attn_bwd_fp8_workspace(B, Hq, Hkv, Sq, Skv, D) if fp8 else attn_bwd_workspace(B, Hq, Sq)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     elif workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != q.device:
@@ -293,7 +337,12 @@ def bwd(q, k, v, out, dout, lse, *, causal=False, scale=None, dq=None, dk=None, 
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     dq, dk, dv = grads
-    _check(attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Sq, Skv, D, scale, causal,
-                    DTYPE_CODE[q.dtype], workspace.data_ptr(), workspace.numel(), stream))
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
+    if fp8:
+        _check(attn_bwd_fp8(*ptrs, B, Hq, Hkv, Sq, Skv, D, scale, causal, *descales, workspace.data_ptr(),
+                            workspace.numel(), stream))
+    else:
+        _check(attn_bwd(*ptrs, B, Hq, Hkv, Sq, Skv, D, scale, causal, DTYPE_CODE[q.dtype], workspace.data_ptr(),
+                        workspace.numel(), stream))
     return dq, dk, dv

@@ -21,6 +21,7 @@ hipError_t launch_fwd_rb2(const FwdParams& p, int D, int dtype, bool causal, hip
 hipError_t launch_fwd_pp(const FwdParams& p, int D, int dtype, bool causal, hipStream_t stream);
 hipError_t launch_combine(const FwdParams& p, int D, bool is_bf16, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& bp, int D, bool is_bf16, bool causal, hipStream_t stream);
+hipError_t launch_widen_fp8(const void* in, void* out, int64_t n, bool e5m2, hipStream_t stream);
 }
 
 namespace {
@@ -263,6 +264,30 @@ extern "C" int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+extern "C" int attn_fwd_fp8_lse(const void* q, const void* k, const void* v, void* out, float* lse,
+                                int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                                float scale, int causal,
+                                float q_descale, float k_descale, float v_descale,
+                                hipStream_t stream) {
+    if (!lse) return ATTN_ERR_NULL;
+    bool noop;
+    const int st = validate(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, scale, causal, 1, 2, &noop);
+    if (st != ATTN_OK) return st;
+    if (!isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale)) return ATTN_ERR_SCALE;
+    if (noop) return ATTN_OK;
+    if ((uintptr_t)lse & 3) return ATTN_ERR_ALIGN;
+    const int64_t nl = (int64_t)B * Hq * Sq * 4;
+    const int64_t nq = (int64_t)B * Sq * Hq * D, nk = (int64_t)B * Skv * Hkv * D;
+    if (ranges_overlap(lse, nl, q, nq) || ranges_overlap(lse, nl, k, nk) || ranges_overlap(lse, nl, v, nk) ||
+        ranges_overlap(lse, nl, out, nq * 2))
+        return ATTN_ERR_ALIAS;
+    const float sl2 = scale * q_descale * k_descale * kLog2e;
+    if (!isfinite(sl2)) return ATTN_ERR_SCALE;
+    const hipError_t e = launch_mfma(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, nonzero_multiplier(sl2), v_descale,
+                                     ATTN_FP8_E4M3, causal, nullptr, stream, lse);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 extern "C" size_t attn_split_workspace(int B, int Hq, int Sq, int D, int n_split) {
     if (n_split <= 1 || B <= 0 || Hq <= 0 || Sq <= 0 || D <= 0) return 0;
     return (size_t)n_split * B * Sq * Hq * (size_t)(D + 2) * sizeof(float);
@@ -402,12 +427,40 @@ extern "C" size_t attn_bwd_workspace(int B, int Hq, int Sq) {
     return (size_t)2 * B * Hq * Sq * sizeof(float);
 }
 
-extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                        const float* lse, void* dq, void* dk, void* dv,
-                        int B, int Hq, int Hkv, int Sq, int Skv, int D,
-                        float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream) {
-    if (dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_DTYPE;
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Byte offsets of the FP8 backward's workspace: bf16 copies of q, k, v and
+// dout, then the per-row values of attn_bwd.
+struct Fp8BwdLayout {
+    size_t q, k, v, dout, rows, total;
+};
+
+Fp8BwdLayout fp8_bwd_layout(int B, int Hq, int Hkv, int Sq, int Skv, int D) {
+    Fp8BwdLayout L;
+    const size_t nq = (size_t)B * Sq * Hq * D, nk = (size_t)B * Skv * Hkv * D;
+    L.q = 0;
+    L.k = L.q + round_up(nq * 2);
+    L.v = L.k + round_up(nk * 2);
+    L.dout = L.v + round_up(nk * 2);
+    L.rows = L.dout + round_up(nq * 2);
+    L.total = L.rows + attn_bwd_workspace(B, Hq, Sq);
+    return L;
+}
+
+struct BwdScalars {
+    float scale_log2, dp_mul, delta_mul, dq_mul, dk_mul, dv_mul;
+};
+
+// Shared checks of both backward entry points. in_bytes: element size of q,
+// k, v and dout; out and the gradients are 16-bit. ws_need: workspace bytes.
+int bwd_validate(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
+                 int causal, int in_bytes, const void* workspace, size_t workspace_bytes, size_t ws_need,
+                 bool* noop) {
+    *noop = false;
     if (B < 0 || Sq < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Skv < 0) return ATTN_ERR_SHAPE;
     // Pointers of empty tensors may be NULL (the query side when B * Sq == 0,
     // the key side when B * Skv == 0).
@@ -425,13 +478,13 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
          (uintptr_t)dk | (uintptr_t)dv) & 15)
         return ATTN_ERR_ALIGN;
     if ((uintptr_t)lse & 3) return ATTN_ERR_ALIGN;
-    if ((int64_t)B * (Sq + Skv) == 0) return ATTN_OK;   // nothing to write
-    const size_t need = attn_bwd_workspace(B, Hq, Sq);
-    if (need > 0 && (!workspace || ((uintptr_t)workspace & 15) || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+    if ((int64_t)B * (Sq + Skv) == 0) { *noop = true; return ATTN_OK; }   // nothing to write
+    if (ws_need > 0 && (!workspace || ((uintptr_t)workspace & 15) || workspace_bytes < ws_need))
+        return ATTN_ERR_WORKSPACE;
     // Outputs (dq, dk, dv, workspace) must not overlap inputs or each other.
     const int64_t nl = (int64_t)B * Hq * Sq * 4;
     const void* in_p[6] = {q, k, v, out, dout, lse};
-    const int64_t in_n[6] = {nq * 2, nk * 2, nk * 2, nq * 2, nq * 2, nl};
+    const int64_t in_n[6] = {nq * in_bytes, nk * in_bytes, nk * in_bytes, nq * 2, nq * in_bytes, nl};
     void* out_p[3] = {dq, dk, dv};
     const int64_t out_n[3] = {nq * 2, nk * 2, nk * 2};
     for (int o = 0; o < 3; ++o) {
@@ -439,12 +492,19 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
             if (ranges_overlap(out_p[o], out_n[o], in_p[i], in_n[i])) return ATTN_ERR_ALIAS;
         for (int o2 = o + 1; o2 < 3; ++o2)
             if (ranges_overlap(out_p[o], out_n[o], out_p[o2], out_n[o2])) return ATTN_ERR_ALIAS;
-        if (ranges_overlap(out_p[o], out_n[o], workspace, (int64_t)need)) return ATTN_ERR_WORKSPACE;
+        if (ranges_overlap(out_p[o], out_n[o], workspace, (int64_t)ws_need)) return ATTN_ERR_WORKSPACE;
     }
     for (int i = 0; i < 6; ++i)
-        if (ranges_overlap(workspace, (int64_t)need, in_p[i], in_n[i])) return ATTN_ERR_WORKSPACE;
+        if (ranges_overlap(workspace, (int64_t)ws_need, in_p[i], in_n[i])) return ATTN_ERR_WORKSPACE;
+    return ATTN_OK;
+}
+
+// Enqueues the two backward kernels on 16-bit q, k, v, out, dout.
+int bwd_launch(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+               void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+               bool is_bf16, const BwdScalars& sc, float* rows, hipStream_t stream) {
     attn::BwdParams bp;
-    bp.f = make_params(q, k, v, (void*)out, B, Hq, Hkv, Sq > 0 ? Sq : 1, Skv, scale * kLog2e, 1.0f,
+    bp.f = make_params(q, k, v, (void*)out, B, Hq, Hkv, Sq > 0 ? Sq : 1, Skv, sc.scale_log2, 1.0f,
                        causal, true, 32, 4, true);
     set_dense_strides(bp.f, D);
     if (Sq == 0) {   // no query rows: dK = dV = 0, the dQ kernel has nothing to do
@@ -453,15 +513,77 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     }
     bp.dout = dout;
     bp.lse = lse;
-    bp.delta = (float*)workspace;
-    bp.lse2 = (float*)workspace + (size_t)B * Hq * Sq;
+    bp.delta = rows;
+    bp.lse2 = rows + (size_t)B * Hq * Sq;
     bp.dq = dq;
     bp.dk = dk;
     bp.dv = dv;
-    bp.scale = scale;
+    bp.dp_mul = sc.dp_mul;
+    bp.delta_mul = sc.delta_mul;
+    bp.dq_mul = sc.dq_mul;
+    bp.dk_mul = sc.dk_mul;
+    bp.dv_mul = sc.dv_mul;
     bp.n_kblocks = (Skv + 127) / 128;
-    const hipError_t e = attn::launch_bwd(bp, D, dtype == ATTN_BF16, causal != 0, stream);
+    const hipError_t e = attn::launch_bwd(bp, D, is_bf16, causal != 0, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv,
+                        int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                        float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+    if (dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_DTYPE;
+    bool noop;
+    const size_t need = (B > 0 && Hq > 0 && Sq > 0) ? attn_bwd_workspace(B, Hq, Sq) : 0;
+    const int st = bwd_validate(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, scale, causal, 2,
+                                workspace, workspace_bytes, need, &noop);
+    if (st != ATTN_OK || noop) return st;
+    const BwdScalars sc = {scale * kLog2e, 1.0f, 1.0f, scale, scale, 1.0f};
+    return bwd_launch(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, causal, dtype == ATTN_BF16, sc,
+                      (float*)workspace, stream);
+}
+
+extern "C" size_t attn_bwd_fp8_workspace(int B, int Hq, int Hkv, int Sq, int Skv, int D) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq < 0 || Skv < 0 || D <= 0 || (int64_t)Sq + Skv == 0) return 0;
+    return fp8_bwd_layout(B, Hq, Hkv, Sq, Skv, D).total;
+}
+
+extern "C" int attn_bwd_fp8(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                            const float* lse, void* dq, void* dk, void* dv,
+                            int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale, int causal,
+                            float q_descale, float k_descale, float v_descale, float do_descale,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    bool noop;
+    const bool shape_ok = B >= 0 && Sq >= 0 && Skv >= 0 && Hq > 0 && Hkv > 0 && D > 0;
+    const size_t need = shape_ok ? attn_bwd_fp8_workspace(B, Hq, Hkv, Sq, Skv, D) : 0;
+    const int st = bwd_validate(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, scale, causal, 1,
+                                workspace, workspace_bytes, need, &noop);
+    if (st != ATTN_OK) return st;
+    if (D == 32) return ATTN_ERR_HEAD_DIM;   // as attn_fwd_fp8, whose out and lse it takes
+    if (!isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale) || !isfinite(do_descale))
+        return ATTN_ERR_SCALE;
+    if (noop) return ATTN_OK;
+    // On the codes: S = (scale qd kd) q.k, dP = (dd vd) dout.v, Delta = dd
+    // rowsum(dout * out), dq = (scale kd) dS k, dk = (scale qd) dS^T q,
+    // dv = dd P^T dout.
+    const BwdScalars sc = {scale * q_descale * k_descale * kLog2e, do_descale * v_descale, do_descale,
+                           scale * k_descale, scale * q_descale, do_descale};
+    if (!isfinite(sc.scale_log2) || !isfinite(sc.dp_mul) || !isfinite(sc.dq_mul) || !isfinite(sc.dk_mul))
+        return ATTN_ERR_SCALE;
+    const Fp8BwdLayout L = fp8_bwd_layout(B, Hq, Hkv, Sq, Skv, D);
+    uint8_t* ws = (uint8_t*)workspace;
+    const int64_t nq = (int64_t)B * Sq * Hq * D, nk = (int64_t)B * Skv * Hkv * D;
+    hipError_t e = hipSuccess;
+    if (nq > 0) e = attn::launch_widen_fp8(q, ws + L.q, nq, false, stream);
+    if (e == hipSuccess && nk > 0) e = attn::launch_widen_fp8(k, ws + L.k, nk, false, stream);
+    if (e == hipSuccess && nk > 0) e = attn::launch_widen_fp8(v, ws + L.v, nk, false, stream);
+    if (e == hipSuccess && nq > 0) e = attn::launch_widen_fp8(dout, ws + L.dout, nq, true, stream);
+    if (e != hipSuccess) return ATTN_ERR_HIP;
+    return bwd_launch(ws + L.q, ws + L.k, ws + L.v, out, ws + L.dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D,
+                      causal, true, sc, (float*)(ws + L.rows), stream);
 }
 
 extern "C" const char* attn_strerror(int status) {

@@ -134,7 +134,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams bp) {
             for (int e = 0; e < 4; ++e) dsum = dot2<T>(xg[e], xo[e], dsum);
         }
     }
-    const float delta = xor32_sum(dsum);
+    const float delta = bp.delta_mul * xor32_sum(dsum);
+    const float dp_mul = bp.dp_mul;
     const size_t srow = ((size_t)wi.b * p.Hq + hq) * Sq + qrow;
     const float lse2 = row_ok ? bp.lse[srow] * kLog2eF : 0.f;
     if (row_ok && h == 0) {   // for the dK / dV kernel
@@ -227,14 +228,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams bp) {
                     const int ko = 8 * (i >> 2) + (i & 3);
                     const float p0 = ko <= lim[kb] ? __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -lse2)) : 0.f;
                     const float p1 = ko + 1 <= lim[kb] ? __builtin_amdgcn_exp2f(fmaf(s[kb][i + 1], c2, -lse2)) : 0.f;
-                    pw[kb][i / 2] = Tr::pack(p0 * (dp[kb][i] - delta), p1 * (dp[kb][i + 1] - delta));
+                    pw[kb][i / 2] = Tr::pack(p0 * fmaf(dp[kb][i], dp_mul, -delta),
+                                             p1 * fmaf(dp[kb][i + 1], dp_mul, -delta));
                 }
             } else {
 #pragma unroll
                 for (int i = i0; i < i0 + cnt; i += 2) {
                     const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -lse2));
                     const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][i + 1], c2, -lse2));
-                    pw[kb][i / 2] = Tr::pack(p0 * (dp[kb][i] - delta), p1 * (dp[kb][i + 1] - delta));
+                    pw[kb][i / 2] = Tr::pack(p0 * fmaf(dp[kb][i], dp_mul, -delta),
+                                             p1 * fmaf(dp[kb][i + 1], dp_mul, -delta));
                 }
             }
         };
@@ -292,7 +295,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams bp) {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // no copy may still be in flight when the workgroup ends
 
     if (row_ok) {
-        const float sc = bp.scale;
+        const float sc = bp.dq_mul;
         T* dst = (T*)bp.dq + roff;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
@@ -368,6 +371,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams bp) {
 
     const int coff = p.causal_off;
     const float c2 = p.scale_log2;
+    const float dp_mul = bp.dp_mul;
     const int n_qs = (Sq + BM - 1) / BM;
     // First query step holding a row that sees a key of this block.
     const int qs0 = CAUSAL ? min(n_qs, max(0, kblk * 128 - coff) / BM) : 0;
@@ -495,7 +499,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams bp) {
                     p1 = (qo + 1 >= qlim[mb] && qo + 1 < qend[mb]) ? p1 : 0.f;
                 }
                 pw[mb][i / 2] = Tr::pack(p0, p1);
-                sw[mb][i / 2] = Tr::pack(p0 * (dp[mb][i] - dst[mb][jj][e]), p1 * (dp[mb][i + 1] - dst[mb][jj][e + 1]));
+                sw[mb][i / 2] = Tr::pack(p0 * fmaf(dp[mb][i], dp_mul, -dst[mb][jj][e]),
+                                         p1 * fmaf(dp[mb][i + 1], dp_mul, -dst[mb][jj][e + 1]));
             }
         };
 
@@ -576,7 +581,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams bp) {
     }
 
     // Element i of the accumulators: key kw0 + 8 (i / 4) + 4h + i % 4, column 32 db + n.
-    const float sc = bp.scale;
+    const float sk_mul = bp.dk_mul, sv_mul = bp.dv_mul;
     T* dkb = (T*)bp.dk + b * p.sk[0] + hkv * p.sk[2];
     T* dvb = (T*)bp.dv + b * p.sv[0] + hkv * p.sv[2];
 #pragma unroll
@@ -585,11 +590,47 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams bp) {
         if (kr < Skv) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                dkb[(size_t)kr * p.sk[1] + 32 * db + n] = round_to<T>(dk[db][i] * sc);
-                dvb[(size_t)kr * p.sv[1] + 32 * db + n] = round_to<T>(dv[db][i]);
+                dkb[(size_t)kr * p.sk[1] + 32 * db + n] = round_to<T>(dk[db][i] * sk_mul);
+                dvb[(size_t)kr * p.sv[1] + 32 * db + n] = round_to<T>(dv[db][i] * sv_mul);
             }
         }
     }
+}
+
+// FP8 codes (E4M3, or E5M2 with E5M2 = true) widened to bfloat16, exactly:
+// both formats' values are bfloat16 values (fewer exponent and mantissa
+// bits). 16 codes per thread; n is a multiple of 16.
+template <bool E5M2>
+__global__ __launch_bounds__(256) void widen_fp8_kernel(const uint8_t* __restrict__ in, __bf16* __restrict__ out,
+                                                        int64_t n16) {
+    const int64_t t = (int64_t)__builtin_amdgcn_workgroup_id_x() * 256 + __builtin_amdgcn_workitem_id_x();
+    if (t >= n16) return;
+    const u32x4 c = *(const u32x4*)(in + t * 16);
+    uint32_t w[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f32x2 lo, hi;
+        if constexpr (E5M2) {
+            lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)c[e], false);
+            hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)c[e], true);
+        } else {
+            lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[e], false);
+            hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[e], true);
+        }
+        w[2 * e] = pack2_bf16(lo[0], lo[1]);
+        w[2 * e + 1] = pack2_bf16(hi[0], hi[1]);
+    }
+    *(u32x4*)(out + t * 16) = (u32x4){w[0], w[1], w[2], w[3]};
+    *(u32x4*)(out + t * 16 + 8) = (u32x4){w[4], w[5], w[6], w[7]};
+}
+
+hipError_t launch_widen_fp8(const void* in, void* out, int64_t n, bool e5m2, hipStream_t stream) {
+    const int64_t n16 = n / 16;
+    if (n16 == 0) return hipSuccess;
+    const dim3 grid((unsigned)((n16 + 255) / 256)), block(256);
+    if (e5m2) hipLaunchKernelGGL((widen_fp8_kernel<true>), grid, block, 0, stream, (const uint8_t*)in, (__bf16*)out, n16);
+    else hipLaunchKernelGGL((widen_fp8_kernel<false>), grid, block, 0, stream, (const uint8_t*)in, (__bf16*)out, n16);
+    return hipGetLastError();
 }
 
 template <typename T, int D>

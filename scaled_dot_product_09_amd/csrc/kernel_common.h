@@ -58,7 +58,11 @@ struct BwdParams {
     void* dq;           // (B, Sq, Hq, D)
     void* dk;           // (B, Skv, Hkv, D)
     void* dv;           // (B, Skv, Hkv, D)
-    float scale;        // the softmax scale (multiplies dQ and dK)
+    // Scalar factors (all 1 but dq_mul = dk_mul = scale for 16-bit inputs;
+    // for FP8 codes they fold in the per-tensor dequantisation factors):
+    //   dP = dp_mul (dout v^T), Delta = delta_mul rowsum(dout * out),
+    //   dq = dq_mul (dS k), dk = dk_mul (dS^T q), dv = dv_mul (P^T dout).
+    float dp_mul, delta_mul, dq_mul, dk_mul, dv_mul;
     int n_kblocks;      // key blocks of the dK / dV kernel, ceil(Skv / 128)
 };
 

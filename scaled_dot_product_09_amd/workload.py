@@ -102,6 +102,8 @@ WORKLOADS = {w.name: w for w in [
              "backward of the headline forward", direction="bwd"),
     Workload("bf16_mha_b4_h16_s2048_d64_causal_bwd", "bf16", 4, 16, 16, 2048, 2048, 64, True, 2048,
              "backward, MHA, head dim 64", direction="bwd"),
+    Workload("e4m3_mha_b4_h16_s4096_d128_causal_bwd", "e4m3", 4, 16, 16, 4096, 4096, 128, True, 9000,
+             "backward of the FP8 forward: E4M3 q, k, v, E5M2 dout, bf16 gradients", direction="bwd"),
 ]}
 
 HEADLINE = "bf16_gqa_b2_hq32_hkv8_s4096_d128_causal"
@@ -149,11 +151,21 @@ def make_inputs(w, *, seed=None, shapes=None):
     return t[0], t[1], t[2], (1.0, 1.0, 1.0)
 
 
+E5M2_MAX = 57344.0
+
+
 def make_dout(w, seed_offset=1000):
     """The loss gradient dout for a backward workload: N(0, 1) float32 of q's
     shape from the seed w.seed + 1000 (first child stream), rounded to the
-    input type like q."""
+    input type like q. For E4M3 workloads the gradient is FP8 E5M2 instead:
+    returns (codes, descale), with the per-tensor scale s = 57344 / amax in
+    float32, codes = nearest-even E5M2 of g * s (torch's converter), and
+    descale = 1 / s."""
     g = draw_normal(w.seed + seed_offset, [(w.B, w.Sq, w.Hq, w.D)])[0]
+    if w.dtype == "e4m3":
+        amax = np.float32(np.max(np.abs(g))) if g.size else np.float32(0)
+        s = np.float32(1.0) if amax == 0 else np.float32(np.float32(E5M2_MAX) / amax)
+        return torch.from_numpy(g * s).to(torch.float8_e5m2), float(np.float32(1.0) / s)
     return torch.from_numpy(g).to(TORCH_DTYPE[w.dtype])
 
 
@@ -203,5 +215,6 @@ def io_bytes(w):
     nq, nk = w.B * w.Sq * w.Hq * w.D, w.B * w.Skv * w.Hkv * w.D
     if w.direction == "bwd":
         rows = w.B * w.Hq * w.Sq
-        return 4 * nq * e + 4 * nk * e + 3 * rows * 4
+        g = 2   # gradients are 16-bit (bf16 for FP8 inputs)
+        return nq * (e + o + e + g) + nk * (2 * e + 2 * g) + 3 * rows * 4
     return nq * (e + o) + 2 * nk * e

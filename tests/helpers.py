@@ -16,7 +16,8 @@ TOL = {"f32": 1e-5, "bf16": 2e-2, "f16": 2e-2, "e4m3": 6e-2}
 
 
 def to_f64(t, dtype, descale=1.0):
-    """Decode a CPU tensor of input codes into float64 with the oracle's codecs."""
+    """Decode a CPU tensor of input codes (bf16 / f16 / E4M3 / E5M2 bits, or
+    float32) into float64 with the oracle's codecs, times descale for FP8."""
     t = t.contiguous()
     if dtype == "f32":
         return t.numpy().astype(np.float64)
@@ -26,6 +27,8 @@ def to_f64(t, dtype, descale=1.0):
         return oracle.f16_bits_to_f64(t.view(torch.int16).numpy())
     if dtype == "e4m3":
         return oracle.e4m3_bits_to_f64(t.view(torch.uint8).numpy()) * np.float64(np.float32(descale))
+    if dtype == "e5m2":
+        return oracle.e5m2_bits_to_f64(t.view(torch.uint8).numpy()) * np.float64(np.float32(descale))
     raise ValueError(dtype)
 
 

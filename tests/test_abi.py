@@ -118,6 +118,41 @@ def test_bwd_rejected_before_launch(kw, status):
     assert call_bwd(**kw) == status
 
 
+def call_bwd_fp8(q=Q, k=K, v=V, o=O, do=DO_, lse=L_, dq=DQ_, dk=DK_, dv=DV_, B=2, Hq=8, Hkv=2, Sq=64, Skv=64,
+                 D=128, scale=0.125, causal=1, qd=0.01, kd=0.01, vd=0.01, dd=0.001, ws=WB_, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = attn.attn_bwd_fp8_workspace(B, Hq, Hkv, Sq, Skv, D)
+    return attn.attn_bwd_fp8(q, k, v, o, do, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, scale, causal, qd, kd, vd, dd,
+                             ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(do=0), -1), (dict(lse=0), -1), (dict(q=0), -1), (dict(D=96), -4), (dict(D=32), -4),
+    (dict(Hq=6, Hkv=4), -3), (dict(dq=DQ_ + 8), -6), (dict(dq=Q), -7), (dict(dk=DO_), -7),
+    (dict(qd=float("nan")), -8), (dict(dd=float("inf")), -8), (dict(scale=float("inf")), -8), (dict(causal=7), -10),
+    (dict(ws=0), -12), (dict(ws_bytes=1000), -12), (dict(ws=DV_), -12),
+])
+def test_bwd_fp8_rejected_before_launch(kw, status):
+    assert call_bwd_fp8(**kw) == status
+
+
+def test_fwd_fp8_lse_rejected_before_launch():
+    L = attn
+    assert L.attn_fwd_fp8_lse(Q, K, V, O, 0, 2, 8, 2, 64, 64, 128, 0.125, 1, 0.01, 0.01, 0.01, None) == -1
+    assert L.attn_fwd_fp8_lse(Q, K, V, O, L_ + 2, 2, 8, 2, 64, 64, 128, 0.125, 1, 0.01, 0.01, 0.01, None) == -6
+    assert L.attn_fwd_fp8_lse(Q, K, V, O, O + 64, 2, 8, 2, 64, 64, 128, 0.125, 1, 0.01, 0.01, 0.01, None) == -7
+    assert L.attn_fwd_fp8_lse(Q, K, V, O, L_, 2, 8, 2, 64, 64, 128, 0.125, 1, float("nan"), 0.01, 0.01, None) == -8
+    assert L.attn_fwd_fp8_lse(Q, K, V, O, L_, 0, 8, 2, 64, 64, 128, 0.125, 1, 0.01, 0.01, 0.01, None) == 0
+
+
+def test_bwd_fp8_workspace_size():
+    # bf16 copies of q, k, v, dout (each rounded up to 256 bytes) and the per-row values.
+    nq, nk = 2 * 64 * 8 * 128, 2 * 64 * 2 * 128
+    r = lambda x: (x + 255) // 256 * 256
+    assert attn.attn_bwd_fp8_workspace(2, 8, 2, 64, 64, 128) == 2 * r(nq * 2) + 2 * r(nk * 2) + 2 * 2 * 8 * 64 * 4
+    assert attn.attn_bwd_fp8_workspace(0, 8, 2, 64, 64, 128) == 0
+
+
 def test_bwd_workspace_size():
     assert attn.attn_bwd_workspace(2, 8, 64) == 2 * 2 * 8 * 64 * 4
     assert attn.attn_bwd_workspace(0, 8, 64) == 0

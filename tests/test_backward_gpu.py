@@ -27,7 +27,7 @@ from tests import helpers
 
 pytestmark = pytest.mark.gpu
 
-LSE_TOL = {"f32": 1e-5, "bf16": 2e-2, "f16": 2e-2}
+LSE_TOL = {"f32": 1e-5, "bf16": 2e-2, "f16": 2e-2, "e4m3": 2e-2}
 
 
 def W(dtype, B, Hq, Hkv, Sq, Skv, D, causal, seed=5):
@@ -55,20 +55,24 @@ LSE_CASES = [
     W("bf16", 1, 4, 4, 130, 257, 64, False),
     W("bf16", 1, 4, 2, 200, 200, 32, True),
     W("f16", 1, 8, 2, 100, 100, 128, True),
+    W("e4m3", 1, 4, 2, 150, 150, 128, True),
+    W("e4m3", 1, 4, 1, 9, 300, 64, "bottom_right"),
 ]
 
 
 @pytest.mark.parametrize("w", LSE_CASES, ids=lambda w: w.name)
 def test_lse_parity(w, kernel):
     print(f"case {w.name} kernel {kernel}", flush=True)
-    q, k, v, _ = workload.make_inputs(w)
+    q, k, v, desc = workload.make_inputs(w)
     dev = torch.device("cuda:0")
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    out, lse = attn.fwd_lse(qd, kd, vd, causal=w.causal, scale=w.scale)
-    ref_out = attn.fwd(qd, kd, vd, causal=w.causal, scale=w.scale)
+    fp8 = w.dtype == "e4m3"
+    out, lse = attn.fwd_lse(qd, kd, vd, causal=w.causal, scale=w.scale, descales=desc if fp8 else None)
+    ref_out = attn.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, descales=desc if fp8 else None)
     torch.cuda.synchronize()
     assert torch.equal(out, ref_out)            # same kernel, same output
-    want = oracle.sdpa_lse(helpers.to_f64(q, w.dtype), helpers.to_f64(k, w.dtype), scale=w.scale, causal=w.causal)
+    want = oracle.sdpa_lse(helpers.to_f64(q, w.dtype, desc[0]), helpers.to_f64(k, w.dtype, desc[1]), scale=w.scale,
+                           causal=w.causal)
     err = helpers.max_abs_err(lse.cpu().numpy().astype(np.float64), want)
     print(f"  lse max-abs {err:.3e}", flush=True)
     assert err <= LSE_TOL[w.dtype], err
@@ -115,6 +119,33 @@ def test_backward_parity(w):
     got = run_backward(w, q, k, v, g)
     want = oracle.sdpa_backward(*(helpers.to_f64(x, w.dtype) for x in (q, k, v, g)), scale=w.scale,
                                 causal=w.causal)
+    check_grads(w, got, want)
+
+
+FP8_CASES = [
+    W("e4m3", 1, 4, 2, 200, 200, 128, True),
+    W("e4m3", 1, 4, 4, 130, 257, 64, False),
+    W("e4m3", 1, 8, 1, 33, 300, 128, "bottom_right"),
+    W("e4m3", 2, 4, 2, 64, 64, 64, True),
+]
+
+
+@pytest.mark.parametrize("w", FP8_CASES, ids=lambda w: w.name)
+def test_backward_fp8_parity(w):
+    """E4M3 q, k, v and an E5M2 dout, each with its per-tensor descale; the
+    oracle differentiates on the decoded values. Same bound as bf16: the
+    codes are widened exactly and the descales only scale."""
+    print(f"case {w.name}", flush=True)
+    q, k, v, desc = workload.make_inputs(w)
+    g, gdesc = workload.make_dout(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, gd = q.to(dev), k.to(dev), v.to(dev), g.to(dev)
+    out, lse = attn.fwd_lse(qd, kd, vd, causal=w.causal, scale=w.scale, descales=desc)
+    got = attn.bwd(qd, kd, vd, out, gd, lse, causal=w.causal, scale=w.scale, descales=(*desc, gdesc))
+    torch.cuda.synchronize()
+    want = oracle.sdpa_backward(helpers.to_f64(q, "e4m3", desc[0]), helpers.to_f64(k, "e4m3", desc[1]),
+                                helpers.to_f64(v, "e4m3", desc[2]), helpers.to_f64(g, "e5m2", gdesc),
+                                scale=w.scale, causal=w.causal)
     check_grads(w, got, want)
 
 

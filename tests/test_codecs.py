@@ -163,3 +163,14 @@ def test_e5m2_encode_vs_torch():
 def test_e5m2_amax_scale():
     assert codecs.e5m2_amax_scale(np.array([0.5, -7.0], np.float32)) == np.float32(8192.0)
     assert codecs.e5m2_amax_scale(np.zeros(3, np.float32)) == np.float32(1.0)
+
+
+def test_generator_e5m2_gradient_matches_oracle_encoder():
+    from dataclasses import replace
+    w = replace(workload.WORKLOADS["e4m3_mha_b4_h16_s4096_d128_causal_bwd"], B=1, Sq=48, Hq=2)
+    codes, desc = workload.make_dout(w)
+    g = workload.draw_normal(w.seed + 1000, [(1, 48, 2, 128)])[0]
+    s = codecs.e5m2_amax_scale(g)
+    assert np.array_equal(codes.view(torch.uint8).numpy(), oracle.f64_to_e5m2_bits(np.float32(g * s)))
+    assert desc == float(np.float32(1.0) / s)
+    assert np.max(np.abs(oracle.e5m2_bits_to_f64(codes.view(torch.uint8).numpy()))) == 57344.0
