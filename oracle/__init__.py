@@ -35,6 +35,7 @@ values). No function here is "parity unpinned".
 
 from .attention import attention_weights, sdpa, sdpa_rows, sdpa_one_row, brute_sdpa, kv_head_of, query_shift
 from .backward import sdpa_lse, sdpa_backward
+from .fp8_scaling import AMAX_HISTORY_LEN, DelayedScalingState, quantize_with_scale
 from .codecs import (
     bf16_bits_to_f64,
     f16_bits_to_f64,
@@ -57,6 +58,9 @@ __all__ = [
     "query_shift",
     "sdpa_lse",
     "sdpa_backward",
+    "AMAX_HISTORY_LEN",
+    "DelayedScalingState",
+    "quantize_with_scale",
     "bf16_bits_to_f64",
     "f16_bits_to_f64",
     "e4m3_bits_to_f64",
