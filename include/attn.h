@@ -66,7 +66,9 @@ enum attn_dtype {
     ATTN_F32 = 0,      /* q, k, v, out: float32                    */
     ATTN_BF16 = 1,     /* q, k, v, out: bfloat16                   */
     ATTN_F16 = 2,      /* q, k, v, out: IEEE binary16              */
-    ATTN_FP8_E4M3 = 3  /* q, k, v: E4M3 codes; out: bfloat16       */
+    ATTN_FP8_E4M3 = 3, /* q, k, v: E4M3 codes; out: bfloat16       */
+    ATTN_FP8_E5M2 = 4  /* OCP E5M2 codes (gradients; see attn_bwd_fp8
+                          and the FP8 scaling state)                 */
 };
 
 enum attn_status {
@@ -313,6 +315,85 @@ int attn_bwd_fp8(const void* q, const void* k, const void* v, const void* out, c
  * copies of q, k, v and dout (each padded to a multiple of 256 bytes) and
  * attn_bwd_workspace(B, Hq, Sq); 0 for an empty problem. */
 size_t attn_bwd_fp8_workspace(int B, int Hq, int Hkv, int Sq, int Skv, int D);
+
+/*
+ * attn_bwd_fp8_dev — attn_bwd_fp8 with the four dequantisation factors read
+ * on the device, from float32 device pointers (4-byte aligned), when the
+ * kernels start: e.g. the scale_inv words of FP8 scaling states, so that no
+ * factor travels through the host. The factors must be finite, and so must
+ * their products with scale. Arguments and errors otherwise as
+ * attn_bwd_fp8 (ATTN_ERR_NULL for a NULL factor pointer). The result
+ * equals attn_bwd_fp8's with the same factor values, bit for bit.
+ */
+int attn_bwd_fp8_dev(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv,
+                     int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale, int causal,
+                     const float* q_descale, const float* k_descale, const float* v_descale,
+                     const float* do_descale, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/*
+ * FP8 delayed scaling, kept on the device.
+ *
+ * The codelab's §10 runs FP8 attention under TransformerEngine's delayed
+ * scaling recipe: per tensor, a history of the last 1024 absolute maxima,
+ * reduced with max, margin 0, E4M3 for the forward pass and E5M2 for the
+ * backward pass. One state per tensor lives in caller-owned device memory,
+ * ATTN_FP8_STATE_BYTES bytes, 16-byte aligned, as 32-bit words:
+ *
+ *     [0] scale       (float32) the factor a cast multiplies by
+ *     [1] scale_inv   (float32) 1 / scale: the dequantisation factor
+ *     [2] step        (uint32)  steps completed
+ *     [3] format      (uint32)  0 = E4M3, 1 = E5M2
+ *     [4 .. 4 + 1024) amax history (float32), slot = step mod 1024
+ *
+ * A step: attn_fp8_quantize for each tensor (cast with the current scale,
+ * i.e. the one derived from earlier steps; record this step's amax), the
+ * attention call with the scale_inv words as device factors
+ * (attn_fwd_fp8_dev / attn_bwd_fp8_dev, pointer = state + 4 bytes), then
+ * attn_fp8_update. Nothing is read back by the host.
+ */
+#define ATTN_AMAX_HISTORY 1024
+#define ATTN_FP8_STATE_BYTES (16 + 4 * ATTN_AMAX_HISTORY)
+
+/* attn_fp8_state_bytes — ATTN_FP8_STATE_BYTES, for bindings. */
+size_t attn_fp8_state_bytes(void);
+
+/* attn_fp8_state_init — n_states consecutive states (ATTN_FP8_STATE_BYTES
+ * apart) set to scale = scale_inv = 1, step 0, an all-zero history, and
+ * format ATTN_FP8_E4M3 or ATTN_FP8_E5M2 (else ATTN_ERR_DTYPE). One kernel,
+ * no memset (safe inside captured graphs). */
+int attn_fp8_state_init(void* states, int n_states, int format, hipStream_t stream);
+
+/* attn_fp8_quantize — codes[i] = FP8 code (the state's format) of
+ * float32(x[i] * scale), nearest-even, saturating at the largest finite
+ * value (448 or 57344; NaN stays NaN), for n elements of x (x_dtype
+ * ATTN_F32, ATTN_BF16 or ATTN_F16), and amax(|x|) of the call folded (max)
+ * into the history slot of the state's current step. x, codes and state
+ * 16-byte aligned and mutually disjoint. Several calls may share a step
+ * (their amaxes combine). */
+int attn_fp8_quantize(const void* x, int x_dtype, void* codes, int64_t n, void* state, hipStream_t stream);
+
+/* attn_fp8_update — for n_states consecutive states: amax = max of the
+ * history; if finite and positive, scale = fmax / amax and scale_inv =
+ * 1 / scale (binary32, correctly rounded); then step + 1 and the history
+ * slot of the new step cleared. */
+int attn_fp8_update(void* states, int n_states, hipStream_t stream);
+
+/*
+ * attn_fwd_fp8_dev — attn_fwd_fp8 (with an optional row log-sum-exp output,
+ * as attn_fwd_fp8_lse; lse may be NULL) whose three dequantisation factors
+ * are read on the device from float32 device pointers (4-byte aligned):
+ * e.g. the scale_inv words of the q, k and v FP8 scaling states. The factors
+ * must be finite, and so must scale times the q and k factors. Arguments and
+ * errors otherwise as attn_fwd_fp8 (ATTN_ERR_NULL for a NULL factor
+ * pointer). The output equals attn_fwd_fp8's with the same factor values,
+ * bit for bit.
+ */
+int attn_fwd_fp8_dev(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale, int causal,
+                     const float* q_descale, const float* k_descale, const float* v_descale,
+                     hipStream_t stream);
 
 /* attn_strerror — a static, human-readable description of a status code. */
 const char* attn_strerror(int status);

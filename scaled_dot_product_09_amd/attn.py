@@ -23,7 +23,8 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libattn.so")
 
-ATTN_F32, ATTN_BF16, ATTN_F16, ATTN_FP8_E4M3 = 0, 1, 2, 3
+ATTN_F32, ATTN_BF16, ATTN_F16, ATTN_FP8_E4M3, ATTN_FP8_E5M2 = 0, 1, 2, 3, 4
+FP8_STATE_BYTES = 16 + 4 * 1024   # one delayed-scaling state (see include/attn.h)
 FP8_GRAD_DTYPE = torch.float8_e5m2   # gradient input of attn_bwd_fp8
 DTYPE_CODE = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16,
               torch.float8_e4m3fn: ATTN_FP8_E4M3}
@@ -33,7 +34,8 @@ STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR
           -12: "ATTN_ERR_WORKSPACE", -13: "ATTN_ERR_STRIDE"}
 EXPORTS = ("attn_fwd", "attn_fwd_lse", "attn_fwd_fp8", "attn_fwd_fp8_lse", "attn_fwd_split", "attn_split_workspace", "attn_split_suggest",
            "attn_fwd_strided", "attn_bwd", "attn_bwd_workspace", "attn_bwd_fp8", "attn_bwd_fp8_workspace",
-           "attn_strerror")
+           "attn_bwd_fp8_dev", "attn_fp8_state_bytes", "attn_fp8_state_init", "attn_fp8_quantize", "attn_fp8_update",
+           "attn_fwd_fp8_dev", "attn_strerror")
 # causal argument: 0 none, 1 lower triangle (top-left), 2 bottom-right (Sq <= Skv)
 CAUSAL_CODE = {False: 0, True: 1, "top_left": 1, "bottom_right": 2, 0: 0, 1: 1, 2: 2}
 
@@ -64,6 +66,18 @@ def lib():
         L.attn_bwd_fp8.restype = i
         L.attn_bwd_fp8_workspace.argtypes = [i, i, i, i, i, i]
         L.attn_bwd_fp8_workspace.restype = ctypes.c_size_t
+        L.attn_bwd_fp8_dev.argtypes = [vp] * 9 + [i, i, i, i, i, i, f, i, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.attn_bwd_fp8_dev.restype = i
+        L.attn_fp8_state_bytes.argtypes = []
+        L.attn_fp8_state_bytes.restype = ctypes.c_size_t
+        L.attn_fp8_state_init.argtypes = [vp, i, i, vp]
+        L.attn_fp8_state_init.restype = i
+        L.attn_fp8_quantize.argtypes = [vp, i, vp, ctypes.c_int64, vp, vp]
+        L.attn_fp8_quantize.restype = i
+        L.attn_fp8_update.argtypes = [vp, i, vp]
+        L.attn_fp8_update.restype = i
+        L.attn_fwd_fp8_dev.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, vp, vp, vp]
+        L.attn_fwd_fp8_dev.restype = i
         L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, f, f, f, vp]
         L.attn_fwd_fp8.restype = i
         L.attn_fwd_split.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, ctypes.c_size_t, vp]
@@ -156,6 +170,37 @@ def attn_bwd_fp8(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, sc
 
 def attn_bwd_fp8_workspace(B, Hq, Hkv, Sq, Skv, D):
     return int(lib().attn_bwd_fp8_workspace(B, Hq, Hkv, Sq, Skv, D))
+
+
+def attn_bwd_fp8_dev(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, scale, causal, q_descale,
+                     k_descale, v_descale, do_descale, workspace, workspace_bytes, stream):
+    """Raw C call of the FP8 backward with device-side factor pointers, returns the status code."""
+    return lib().attn_bwd_fp8_dev(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, float(scale),
+                                  int(causal), q_descale, k_descale, v_descale, do_descale, workspace,
+                                  int(workspace_bytes), stream)
+
+
+def attn_fp8_state_bytes():
+    return int(lib().attn_fp8_state_bytes())
+
+
+def attn_fp8_state_init(states, n_states, fmt, stream):
+    return lib().attn_fp8_state_init(states, int(n_states), int(fmt), stream)
+
+
+def attn_fp8_quantize(x, x_dtype, codes, n, state, stream):
+    return lib().attn_fp8_quantize(x, int(x_dtype), codes, int(n), state, stream)
+
+
+def attn_fp8_update(states, n_states, stream):
+    return lib().attn_fp8_update(states, int(n_states), stream)
+
+
+def attn_fwd_fp8_dev(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, q_descale, k_descale, v_descale,
+                     stream):
+    """Raw C call of the E4M3 forward with device-side factor pointers, returns the status code."""
+    return lib().attn_fwd_fp8_dev(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, float(scale), int(causal), q_descale,
+                                  k_descale, v_descale, stream)
 
 
 def _check(st):
@@ -345,4 +390,99 @@ def bwd(q, k, v, out, dout, lse, *, causal=False, scale=None, dq=None, dk=None, 
     else:
         _check(attn_bwd(*ptrs, B, Hq, Hkv, Sq, Skv, D, scale, causal, DTYPE_CODE[q.dtype], workspace.data_ptr(),
                         workspace.numel(), stream))
+    return dq, dk, dv
+
+
+# ---- FP8 delayed scaling (state in device memory) -------------------------------------------
+
+FP8_FORMAT = {torch.float8_e4m3fn: ATTN_FP8_E4M3, torch.float8_e5m2: ATTN_FP8_E5M2}
+FP8_TORCH = {ATTN_FP8_E4M3: torch.float8_e4m3fn, ATTN_FP8_E5M2: torch.float8_e5m2}
+
+
+def fp8_states(n, fmt, device="cuda:0", stream=None):
+    """n delayed-scaling states (a uint8 device tensor of shape (n, FP8_STATE_BYTES)),
+    initialised for format ATTN_FP8_E4M3 or ATTN_FP8_E5M2."""
+    st = torch.empty((n, FP8_STATE_BYTES), dtype=torch.uint8, device=device)
+    if stream is None:
+        stream = torch.cuda.current_stream(st.device).cuda_stream
+    _check(attn_fp8_state_init(st.data_ptr(), n, fmt, stream))
+    return st
+
+
+def fp8_scale_inv_ptr(state):
+    """Device pointer to a state's scale_inv word (its dequantisation factor)."""
+    return state.data_ptr() + 4
+
+
+def fp8_quantize(x, state, fmt, *, out=None, stream=None):
+    """FP8 codes of x (float32 / bfloat16 / float16, contiguous) cast with the
+    state's current scale; records amax(|x|) in the state's history. ``fmt``
+    (ATTN_FP8_E4M3 / ATTN_FP8_E5M2) must be the state's format: it only picks
+    the torch dtype of the result (the kernel reads the format from the state)."""
+    if not x.is_contiguous() or not x.is_cuda:
+        raise ValueError("x must be a contiguous GPU tensor")
+    code = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}.get(x.dtype)
+    if code is None:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    if out is None:
+        out = torch.empty(x.shape, dtype=FP8_TORCH[fmt], device=x.device)
+    elif out.dtype != FP8_TORCH[fmt] or out.shape != x.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous FP8 tensor of x's shape in the state's format")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    _check(attn_fp8_quantize(x.data_ptr(), code, out.data_ptr(), x.numel(), state.data_ptr(), stream))
+    return out
+
+
+def fp8_update(states, stream=None):
+    """Scale update of every state in a (n, FP8_STATE_BYTES) tensor (or one state row)."""
+    n = 1 if states.dim() == 1 else states.shape[0]
+    if stream is None:
+        stream = torch.cuda.current_stream(states.device).cuda_stream
+    _check(attn_fp8_update(states.data_ptr(), n, stream))
+
+
+def fwd_fp8_dev(q, k, v, states, *, causal=False, scale=None, out=None, lse=None, with_lse=False, stream=None):
+    """The E4M3 forward with the q, k, v dequantisation factors read on the
+    device from three scaling states (rows of a state tensor). Returns
+    (out, lse or None)."""
+    _check_qkv(q, k, v)
+    if q.dtype != torch.float8_e4m3fn:
+        raise ValueError("fwd_fp8_dev takes float8_e4m3fn q, k, v")
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    causal = _causal_code(causal)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(attn_fwd_fp8_dev(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr() if lse is not None else None, B, Hq, Hkv, Sq, Skv, D, scale, causal,
+                            *(fp8_scale_inv_ptr(s) for s in states), stream))
+    return out, lse
+
+
+def bwd_fp8_dev(q, k, v, out, dout, lse, states, *, causal=False, scale=None, workspace=None, stream=None):
+    """The FP8 backward (E4M3 q, k, v; E5M2 dout) with the four factors read on
+    the device from scaling states (q, k, v, dout). Returns bf16 (dq, dk, dv)."""
+    _check_qkv(q, k, v)
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    causal = _causal_code(causal)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    dq = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    dk = torch.empty(k.shape, dtype=torch.bfloat16, device=q.device)
+    dv = torch.empty(v.shape, dtype=torch.bfloat16, device=q.device)
+    need = attn_bwd_fp8_workspace(B, Hq, Hkv, Sq, Skv, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(attn_bwd_fp8_dev(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Sq, Skv, D,
+                            scale, causal, *(fp8_scale_inv_ptr(s) for s in states), workspace.data_ptr(),
+                            workspace.numel(), stream))
     return dq, dk, dv

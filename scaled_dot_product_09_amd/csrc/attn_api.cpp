@@ -22,6 +22,9 @@ hipError_t launch_fwd_pp(const FwdParams& p, int D, int dtype, bool causal, hipS
 hipError_t launch_combine(const FwdParams& p, int D, bool is_bf16, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& bp, int D, bool is_bf16, bool causal, hipStream_t stream);
 hipError_t launch_widen_fp8(const void* in, void* out, int64_t n, bool e5m2, hipStream_t stream);
+hipError_t launch_fp8_state_init(void* states, int n_states, int fmt, hipStream_t stream);
+hipError_t launch_fp8_quantize(const void* x, int dtype, void* codes, int64_t n, void* state, hipStream_t stream);
+hipError_t launch_fp8_update(void* states, int n_states, hipStream_t stream);
 }
 
 namespace {
@@ -71,6 +74,7 @@ attn::FwdParams make_params(const void* q, const void* k, const void* v, void* o
     p.part_o = nullptr;
     p.part_ml = nullptr;
     p.lse = nullptr;
+    p.dsc_q = p.dsc_k = p.dsc_v = nullptr;
     p.q = q; p.k = k; p.v = v; p.out = out;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Sq = Sq; p.Skv = Skv;
     p.G = Hq / Hkv;
@@ -149,10 +153,10 @@ MfmaKernel mfma_kernel() {
 hipError_t launch_mfma(const void* q, const void* k, const void* v, void* out,
                        int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale_log2,
                        float out_mul, int dtype, int causal, const int64_t* strides, hipStream_t stream,
-                       float* lse = nullptr) {
-    // Head dimension 32, strided layouts and the log-sum-exp output exist
-    // only in the four- and eight-wave kernel.
-    const bool four_or_eight = D == 32 || strides || lse;
+                       float* lse = nullptr, const float* const* dsc = nullptr) {
+    // Head dimension 32, strided layouts, the log-sum-exp output and
+    // device-side FP8 factors exist only in the four- and eight-wave kernel.
+    const bool four_or_eight = D == 32 || strides || lse || dsc;
     const MfmaKernel kern = (four_or_eight && (mfma_kernel() == kPingPong || mfma_kernel() == kRows64))
                                 ? kFourWave : mfma_kernel();
     const int rpw = kern == kRows64 ? 64 : 32;
@@ -168,6 +172,11 @@ hipError_t launch_mfma(const void* q, const void* k, const void* v, void* out,
         set_dense_strides(p, D);
     }
     p.lse = lse;
+    if (dsc) {
+        p.dsc_q = dsc[0];
+        p.dsc_k = dsc[1];
+        p.dsc_v = dsc[2];
+    }
     const bool masked = causal != 0;
     switch (kern) {
         case kRows64: return attn::launch_fwd_rb2(p, D, dtype, masked, stream);
@@ -502,7 +511,8 @@ int bwd_validate(const void* q, const void* k, const void* v, const void* out, c
 // Enqueues the two backward kernels on 16-bit q, k, v, out, dout.
 int bwd_launch(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
                void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
-               bool is_bf16, const BwdScalars& sc, float* rows, hipStream_t stream) {
+               bool is_bf16, const BwdScalars& sc, float* rows, hipStream_t stream,
+               const float* const* dsc = nullptr, float raw_scale = 0.0f) {
     attn::BwdParams bp;
     bp.f = make_params(q, k, v, (void*)out, B, Hq, Hkv, Sq > 0 ? Sq : 1, Skv, sc.scale_log2, 1.0f,
                        causal, true, 32, 4, true);
@@ -524,6 +534,8 @@ int bwd_launch(const void* q, const void* k, const void* v, const void* out, con
     bp.dk_mul = sc.dk_mul;
     bp.dv_mul = sc.dv_mul;
     bp.n_kblocks = (Skv + 127) / 128;
+    for (int i = 0; i < 4; ++i) bp.dsc[i] = dsc ? dsc[i] : nullptr;
+    bp.scale = raw_scale;
     const hipError_t e = attn::launch_bwd(bp, D, is_bf16, causal != 0, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
@@ -584,6 +596,105 @@ extern "C" int attn_bwd_fp8(const void* q, const void* k, const void* v, const v
     if (e != hipSuccess) return ATTN_ERR_HIP;
     return bwd_launch(ws + L.q, ws + L.k, ws + L.v, out, ws + L.dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D,
                       causal, true, sc, (float*)(ws + L.rows), stream);
+}
+
+extern "C" int attn_bwd_fp8_dev(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                                const float* lse, void* dq, void* dk, void* dv,
+                                int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale, int causal,
+                                const float* q_descale, const float* k_descale, const float* v_descale,
+                                const float* do_descale, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+    bool noop;
+    const bool shape_ok = B >= 0 && Sq >= 0 && Skv >= 0 && Hq > 0 && Hkv > 0 && D > 0;
+    const size_t need = shape_ok ? attn_bwd_fp8_workspace(B, Hq, Hkv, Sq, Skv, D) : 0;
+    const int st = bwd_validate(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, scale, causal, 1,
+                                workspace, workspace_bytes, need, &noop);
+    if (st != ATTN_OK) return st;
+    if (D == 32) return ATTN_ERR_HEAD_DIM;
+    if (!q_descale || !k_descale || !v_descale || !do_descale) return ATTN_ERR_NULL;
+    if (((uintptr_t)q_descale | (uintptr_t)k_descale | (uintptr_t)v_descale | (uintptr_t)do_descale) & 3)
+        return ATTN_ERR_ALIGN;
+    if (noop) return ATTN_OK;
+    const Fp8BwdLayout L = fp8_bwd_layout(B, Hq, Hkv, Sq, Skv, D);
+    uint8_t* ws = (uint8_t*)workspace;
+    const int64_t nq = (int64_t)B * Sq * Hq * D, nk = (int64_t)B * Skv * Hkv * D;
+    hipError_t e = hipSuccess;
+    if (nq > 0) e = attn::launch_widen_fp8(q, ws + L.q, nq, false, stream);
+    if (e == hipSuccess && nk > 0) e = attn::launch_widen_fp8(k, ws + L.k, nk, false, stream);
+    if (e == hipSuccess && nk > 0) e = attn::launch_widen_fp8(v, ws + L.v, nk, false, stream);
+    if (e == hipSuccess && nq > 0) e = attn::launch_widen_fp8(dout, ws + L.dout, nq, true, stream);
+    if (e != hipSuccess) return ATTN_ERR_HIP;
+    const float* dsc[4] = {q_descale, k_descale, v_descale, do_descale};
+    const BwdScalars sc = {0.f, 1.f, 1.f, 1.f, 1.f, 1.f};   // formed on the device
+    return bwd_launch(ws + L.q, ws + L.k, ws + L.v, out, ws + L.dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D,
+                      causal, true, sc, (float*)(ws + L.rows), stream, dsc, scale);
+}
+
+// ---- FP8 delayed scaling --------------------------------------------------------------------
+
+extern "C" size_t attn_fp8_state_bytes(void) { return ATTN_FP8_STATE_BYTES; }
+
+extern "C" int attn_fp8_state_init(void* states, int n_states, int format, hipStream_t stream) {
+    if (!states) return ATTN_ERR_NULL;
+    if (n_states < 0) return ATTN_ERR_SHAPE;
+    if (format != ATTN_FP8_E4M3 && format != ATTN_FP8_E5M2) return ATTN_ERR_DTYPE;
+    if ((uintptr_t)states & 15) return ATTN_ERR_ALIGN;
+    if (n_states == 0) return ATTN_OK;
+    const hipError_t e = attn::launch_fp8_state_init(states, n_states, format == ATTN_FP8_E5M2 ? 1 : 0, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+extern "C" int attn_fp8_quantize(const void* x, int x_dtype, void* codes, int64_t n, void* state,
+                                 hipStream_t stream) {
+    if (!state) return ATTN_ERR_NULL;
+    if (n < 0 || n >= ((int64_t)1 << 40)) return ATTN_ERR_SHAPE;
+    if (n > 0 && (!x || !codes)) return ATTN_ERR_NULL;
+    int eb;
+    switch (x_dtype) {
+        case ATTN_F32: eb = 4; break;
+        case ATTN_BF16: case ATTN_F16: eb = 2; break;
+        default: return ATTN_ERR_DTYPE;
+    }
+    if (((uintptr_t)x | (uintptr_t)codes | (uintptr_t)state) & 15) return ATTN_ERR_ALIGN;
+    if (n == 0) return ATTN_OK;   // the amax of nothing (0) changes no history slot
+    if (ranges_overlap(codes, n, x, n * eb) || ranges_overlap(codes, n, state, ATTN_FP8_STATE_BYTES) ||
+        ranges_overlap(state, ATTN_FP8_STATE_BYTES, x, n * eb))
+        return ATTN_ERR_ALIAS;
+    const hipError_t e = attn::launch_fp8_quantize(x, x_dtype, codes, n, state, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+extern "C" int attn_fp8_update(void* states, int n_states, hipStream_t stream) {
+    if (!states) return ATTN_ERR_NULL;
+    if (n_states < 0) return ATTN_ERR_SHAPE;
+    if ((uintptr_t)states & 15) return ATTN_ERR_ALIGN;
+    if (n_states == 0) return ATTN_OK;
+    const hipError_t e = attn::launch_fp8_update(states, n_states, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+extern "C" int attn_fwd_fp8_dev(const void* q, const void* k, const void* v, void* out, float* lse,
+                                int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale, int causal,
+                                const float* q_descale, const float* k_descale, const float* v_descale,
+                                hipStream_t stream) {
+    bool noop;
+    const int st = validate(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, scale, causal, 1, 2, &noop);
+    if (st != ATTN_OK) return st;
+    if (!q_descale || !k_descale || !v_descale) return ATTN_ERR_NULL;
+    if (((uintptr_t)q_descale | (uintptr_t)k_descale | (uintptr_t)v_descale) & 3) return ATTN_ERR_ALIGN;
+    if (noop) return ATTN_OK;
+    if (lse) {
+        if ((uintptr_t)lse & 3) return ATTN_ERR_ALIGN;
+        const int64_t nl = (int64_t)B * Hq * Sq * 4;
+        const int64_t nq = (int64_t)B * Sq * Hq * D, nk = (int64_t)B * Skv * Hkv * D;
+        if (ranges_overlap(lse, nl, q, nq) || ranges_overlap(lse, nl, k, nk) || ranges_overlap(lse, nl, v, nk) ||
+            ranges_overlap(lse, nl, out, nq * 2))
+            return ATTN_ERR_ALIAS;
+    }
+    const float* dsc[3] = {q_descale, k_descale, v_descale};
+    const hipError_t e = launch_mfma(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, scale, 1.0f, ATTN_FP8_E4M3, causal,
+                                     nullptr, stream, lse, dsc);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 extern "C" const char* attn_strerror(int status) {

@@ -74,6 +74,27 @@ __device__ inline void mfma_agpr(f32x16& acc, frag a, frag b) {
         asm("s_nop 4\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
+struct BwdScalars {
+    float c2, dp_mul, delta_mul, dq_mul, dk_mul, dv_mul;
+};
+
+// The backward's scalar factors: from the parameters, or (FP8 with
+// device-side factors) formed from the bare scale and the q, k, v, dout
+// factors in device memory by the expressions the host uses.
+__device__ inline BwdScalars bwd_scalars(const BwdParams& bp) {
+    BwdScalars s = {bp.f.scale_log2, bp.dp_mul, bp.delta_mul, bp.dq_mul, bp.dk_mul, bp.dv_mul};
+    if (bp.dsc[0]) {
+        const float qd = *bp.dsc[0], kd = *bp.dsc[1], vd = *bp.dsc[2], dd = *bp.dsc[3];
+        s.c2 = ((bp.scale * qd) * kd) * kLog2eF32;
+        s.dp_mul = dd * vd;
+        s.delta_mul = dd;
+        s.dq_mul = bp.scale * kd;
+        s.dk_mul = bp.scale * qd;
+        s.dv_mul = dd;
+    }
+    return s;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -101,6 +122,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams bp) {
     const int h = lane >> 5, n = lane & 31;
 
     const WorkItem wi = map_workgroup(p, CAUSAL);
+    const BwdScalars sc = bwd_scalars(bp);
     const int HS = p.head_stride;
     const int slot = wave * 32 + n;
     const int hq = wi.hq0 + (slot / HS) % p.gpack;
@@ -134,15 +156,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams bp) {
             for (int e = 0; e < 4; ++e) dsum = dot2<T>(xg[e], xo[e], dsum);
         }
     }
-    const float delta = bp.delta_mul * xor32_sum(dsum);
-    const float dp_mul = bp.dp_mul;
+    const float delta = sc.delta_mul * xor32_sum(dsum);
+    const float dp_mul = sc.dp_mul;
     const size_t srow = ((size_t)wi.b * p.Hq + hq) * Sq + qrow;
     const float lse2 = row_ok ? bp.lse[srow] * kLog2eF : 0.f;
     if (row_ok && h == 0) {   // for the dK / dV kernel
         bp.delta[srow] = delta;
         bp.lse2[srow] = lse2;
     }
-    const float c2 = p.scale_log2;            // scale * log2(e), any sign
+    const float c2 = sc.c2;                   // scale * log2(e), any sign
     const int coff = p.causal_off;
 
     int n_tiles = (Skv + BN - 1) / BN;
@@ -295,15 +317,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams bp) {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // no copy may still be in flight when the workgroup ends
 
     if (row_ok) {
-        const float sc = bp.dq_mul;
+        const float dqm = sc.dq_mul;
         T* dst = (T*)bp.dq + roff;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int d0 = db * 32 + 8 * jj + 4 * h;
-                const uint32_t w0 = Tr::pack(dq[db][4 * jj] * sc, dq[db][4 * jj + 1] * sc);
-                const uint32_t w1 = Tr::pack(dq[db][4 * jj + 2] * sc, dq[db][4 * jj + 3] * sc);
+                const uint32_t w0 = Tr::pack(dq[db][4 * jj] * dqm, dq[db][4 * jj + 1] * dqm);
+                const uint32_t w1 = Tr::pack(dq[db][4 * jj + 2] * dqm, dq[db][4 * jj + 3] * dqm);
                 *(u32x2*)(dst + d0) = (u32x2){w0, w1};
             }
         }
@@ -370,8 +392,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams bp) {
     }
 
     const int coff = p.causal_off;
-    const float c2 = p.scale_log2;
-    const float dp_mul = bp.dp_mul;
+    const BwdScalars sc = bwd_scalars(bp);
+    const float c2 = sc.c2;
+    const float dp_mul = sc.dp_mul;
     const int n_qs = (Sq + BM - 1) / BM;
     // First query step holding a row that sees a key of this block.
     const int qs0 = CAUSAL ? min(n_qs, max(0, kblk * 128 - coff) / BM) : 0;
@@ -581,7 +604,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams bp) {
     }
 
     // Element i of the accumulators: key kw0 + 8 (i / 4) + 4h + i % 4, column 32 db + n.
-    const float sk_mul = bp.dk_mul, sv_mul = bp.dv_mul;
+    const float sk_mul = sc.dk_mul, sv_mul = sc.dv_mul;
     T* dkb = (T*)bp.dk + b * p.sk[0] + hkv * p.sk[2];
     T* dvb = (T*)bp.dv + b * p.sv[0] + hkv * p.sv[2];
 #pragma unroll

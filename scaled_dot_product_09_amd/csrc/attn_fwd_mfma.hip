@@ -76,6 +76,8 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
     const int n = lane & 31;              // query column inside the wave's 32 rows
 
     const WorkItem wi = map_workgroup(p, CAUSAL);
+    float sl2, out_mul;
+    fwd_scalars(p, sl2, out_mul);
     // The workgroup's 32 * NWAVES query slots cover gpack query heads (of one
     // KV head) times rows_per_wg rows, in runs of HS = head_stride rows of
     // one head: slot s is head hq0 + (s / HS) % gpack and row
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
     {
         const int row = qrow;
         const uint8_t* src = (const uint8_t*)(qbase + row * p.sq[1]);
-        const uint32_t flip = p.scale_log2 < 0.f ? Tr::SIGN_BITS : 0u;
+        const uint32_t flip = sl2 < 0.f ? Tr::SIGN_BITS : 0u;
         for (int ks = 0; ks < KSTEPS; ++ks) {
             u32x4 x[CH];
             for (int t = 0; t < CH; ++t) {
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
     float l_part = 0.f;        // this lane's share of the running denominator
     float neg_m = 0.f;         // exponent offset -m_run of the tile being weighted
 
-    const float c_log2 = fabsf(p.scale_log2);   // > 0: the host never passes 0
+    const float c_log2 = fabsf(sl2);   // > 0: never 0 (see fwd_scalars)
 
     // Per-lane constants of the V transpose read (see load_v).
     const int L16 = lane & 15;                 // lane inside its 16-lane group
@@ -501,7 +503,7 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
         }
         return;
     }
-    const float inv = p.out_mul / l;
+    const float inv = out_mul / l;
     // Row log-sum-exp: the weights are 2^(c s - m_run) with c = scale log2(e),
     // so sum_j e^(scale s_j) = 2^m_run l and its logarithm is (m_run + log2 l) ln 2.
     if (p.lse && qrow < Sq && h == 0)

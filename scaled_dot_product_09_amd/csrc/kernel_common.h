@@ -42,7 +42,30 @@ struct FwdParams {
     float* part_o;      // n_split > 1: unnormalised partial outputs [n_split][B][Sq][Hq][D]
     float* part_ml;     // n_split > 1: (running max, weight sum) pairs [n_split][B][Sq][Hq][2]
     float* lse;         // null, or the natural-log row log-sum-exp of the scaled scores, [B][Hq][Sq]
+    // FP8 with device-side dequantisation factors: when dsc_q is not null,
+    // scale_log2 holds the bare softmax scale and the kernel reads q, k, v
+    // factors from device memory: multiplier ((scale qd) kd) log2(e),
+    // out_mul = vd (the same expressions, in the same order, as the host
+    // computes for host-side factors).
+    const float* dsc_q;
+    const float* dsc_k;
+    const float* dsc_v;
 };
+
+constexpr float kLog2eF32 = 1.4426950408889634f;
+
+// The forward's score multiplier and output factor, from the parameters or
+// from device memory. A zero multiplier becomes 2^-100, as on the host (see
+// the C API): every weight is then exp2(0) = 1, the weights of scale 0.
+__device__ inline void fwd_scalars(const FwdParams& p, float& sl2, float& out_mul) {
+    sl2 = p.scale_log2;
+    out_mul = p.out_mul;
+    if (p.dsc_q) {
+        sl2 = ((p.scale_log2 * *p.dsc_q) * *p.dsc_k) * kLog2eF32;
+        out_mul = *p.dsc_v;
+        if (sl2 == 0.0f) sl2 = 0x1p-100f;
+    }
+}
 
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -64,6 +87,11 @@ struct BwdParams {
     //   dq = dq_mul (dS k), dk = dk_mul (dS^T q), dv = dv_mul (P^T dout).
     float dp_mul, delta_mul, dq_mul, dk_mul, dv_mul;
     int n_kblocks;      // key blocks of the dK / dV kernel, ceil(Skv / 128)
+    // FP8 with device-side factors (q, k, v, dout), or null: then the
+    // factors above are formed on the device from scale (the bare softmax
+    // scale) by the expressions the host uses.
+    const float* dsc[4];
+    float scale;
 };
 
 struct WorkItem {

@@ -153,6 +153,37 @@ def test_bwd_fp8_workspace_size():
     assert attn.attn_bwd_fp8_workspace(0, 8, 2, 64, 64, 128) == 0
 
 
+S_ = 0xE00000   # fake FP8 scaling state
+
+
+def test_fp8_scaling_rejected_before_launch():
+    assert attn.attn_fp8_state_bytes() == 16 + 4 * 1024
+    assert attn.attn_fp8_state_init(0, 1, attn.ATTN_FP8_E4M3, None) == -1
+    assert attn.attn_fp8_state_init(S_, -1, attn.ATTN_FP8_E4M3, None) == -2
+    assert attn.attn_fp8_state_init(S_, 1, attn.ATTN_BF16, None) == -5
+    assert attn.attn_fp8_state_init(S_ + 4, 1, attn.ATTN_FP8_E5M2, None) == -6
+    assert attn.attn_fp8_state_init(S_, 0, attn.ATTN_FP8_E5M2, None) == 0
+    q = lambda **kw: attn.attn_fp8_quantize(kw.get("x", Q), kw.get("dt", attn.ATTN_BF16), kw.get("c", K),
+                                           kw.get("n", 4096), kw.get("s", S_), None)
+    assert q(s=0) == -1 and q(x=0) == -1 and q(c=0) == -1 and q(n=-1) == -2
+    assert q(dt=attn.ATTN_FP8_E4M3) == -5 and q(x=Q + 2) == -6 and q(c=K + 8) == -6
+    assert q(c=Q + 1024) == -7 and q(s=K + 16) == -7
+    assert q(x=0, c=0, n=0) == 0                             # nothing to cast, no launch
+    assert attn.attn_fp8_update(0, 1, None) == -1 and attn.attn_fp8_update(S_, -2, None) == -2
+    assert attn.attn_fp8_update(S_ + 8, 1, None) == -6 and attn.attn_fp8_update(S_, 0, None) == 0
+
+
+def test_fp8_dev_entry_points_rejected_before_launch():
+    f = lambda **kw: attn.attn_fwd_fp8_dev(kw.get("q", Q), K, V, O, kw.get("lse", None), kw.get("B", 2), 8, 2, 64,
+                                           64, kw.get("D", 128), 0.125, 1, kw.get("qd", S_ + 4), S_ + 4, S_ + 4, None)
+    assert f(qd=0) == -1 and f(q=0) == -1 and f(D=32) == -4 and f(qd=S_ + 2) == -6 and f(lse=Q) == -7
+    assert f(B=0) == 0
+    b = lambda **kw: attn.attn_bwd_fp8_dev(Q, K, V, O, DO_, L_, DQ_, DK_, DV_, 2, 8, 2, 64, 64, kw.get("D", 128),
+                                           0.125, 1, kw.get("qd", S_ + 4), S_ + 4, S_ + 4, kw.get("dd", S_ + 4),
+                                           WB_, attn.attn_bwd_fp8_workspace(2, 8, 2, 64, 64, 128), None)
+    assert b(qd=0) == -1 and b(dd=0) == -1 and b(D=32) == -4 and b(dd=S_ + 1) == -6
+
+
 def test_bwd_workspace_size():
     assert attn.attn_bwd_workspace(2, 8, 64) == 2 * 2 * 8 * 64 * 4
     assert attn.attn_bwd_workspace(0, 8, 64) == 0
