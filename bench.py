@@ -125,6 +125,24 @@ def time_workload(w, steps, warmup, rotate=True, settle_s=SETTLE_S):
                  descales=desc if fp8 else None, stream=stream.cuda_stream,
                  n_split=n_split if ws is not None else None, workspace=ws)
 
+    if w.scaling == "delayed":
+        # One delayed-scaling FP8 step: cast bf16 q, k, v to E4M3 with each
+        # tensor's device-side state, the forward reading the three factors
+        # on the device, one update of the three states. No host read-back.
+        bf = [torch.from_numpy(x).to(torch.bfloat16).to(dev)
+              for x in workload.draw_normal(w.seed, [(w.B, w.Sq, w.Hq, w.D), (w.B, w.Skv, w.Hkv, w.D),
+                                                     (w.B, w.Skv, w.Hkv, w.D)])]
+        states = attn.fp8_states(3, attn.ATTN_FP8_E4M3)
+        codes = [torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=dev) for x in bf]
+        od = torch.empty(bf[0].shape, dtype=torch.bfloat16, device=dev)
+
+        def step(i):  # noqa: F811
+            for x, c, j in zip(bf, codes, range(3)):
+                attn.fp8_quantize(x, states[j], attn.ATTN_FP8_E4M3, out=c, stream=stream.cuda_stream)
+            attn.fwd_fp8_dev(*codes, [states[0], states[1], states[2]], causal=w.causal, scale=w.scale, out=od,
+                             stream=stream.cuda_stream)
+            attn.fp8_update(states, stream=stream.cuda_stream)
+
     if w.direction == "bwd":
         # Backward: the forward's out and lse are made once per input set,
         # outside the timed region; a step is one attn_bwd (attn_bwd_fp8 for

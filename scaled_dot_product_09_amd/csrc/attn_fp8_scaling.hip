@@ -10,14 +10,17 @@
 //
 //   * fp8_state_init_kernel: scale = scale_inv = 1, step 0, empty history.
 //   * fp8_quantize_kernel: codes = nearest-even, saturating FP8 of
-//     float32(x * scale) with the state's current scale (the one derived
+//     float32(x * scale) (hardware conversion after clamping to the largest
+//     finite value) with the state's current scale (the one derived
 //     from earlier steps), and amax(|x|) of this call folded into history
-//     slot (step mod 1024) with one atomic max per workgroup (on the bit
-//     patterns of non-negative floats, whose unsigned order is their order;
-//     NaN patterns sort above infinity, so a NaN propagates).
+//     slot (step mod 1024) with at most one atomic max per workgroup (on
+//     the bit patterns of non-negative floats, whose unsigned order is their
+//     order; NaN patterns sort above infinity, so a NaN propagates).
 //   * fp8_update_kernel: amax = max(history); if finite and positive,
 //     scale = fmax / amax and scale_inv = 1 / scale (binary32, correctly
 //     rounded divisions); step + 1; the next step's slot is cleared.
+
+#include <type_traits>
 
 #include "kernel_common.h"
 
@@ -39,38 +42,34 @@ constexpr int kHistory = 1024;
 
 __device__ inline float fmt_max(uint32_t fmt) { return fmt == 0 ? 448.0f : 57344.0f; }
 
-// Nearest-even, saturating FP8 code of y from the fields of binary32 y.
-// E4M3 (bias 7, 3 mantissa bits, largest finite 448, NaN S.1111.111) or
-// E5M2 (bias 15, 2 mantissa bits, largest finite 57344, NaN S.11111.10).
-__device__ inline uint32_t encode_fp8(float y, uint32_t fmt) {
-    const uint32_t bits = __builtin_bit_cast(uint32_t, y);
-    const uint32_t sign = (bits >> 24) & 0x80u;
-    const uint32_t mag = bits & 0x7FFFFFFFu;
+// Nearest-even, saturating FP8 codes of four binary32 values, packed in a
+// dword (value e in byte e). The hardware pair conversion rounds to nearest
+// even; values are first clamped to the format's largest finite magnitude
+// (448 for E4M3, 57344 for E5M2), which is saturation; a NaN input gets the
+// format's NaN code (E4M3 S.1111.111, E5M2 S.11111.10) with its sign.
+__device__ inline uint32_t encode4_fp8(const float (&y)[4], uint32_t fmt, bool may_have_nan = true) {
     const bool e4m3 = fmt == 0;
-    if (mag > 0x7F800000u) return sign | (e4m3 ? 0x7Fu : 0x7Eu);          // NaN
-    const uint32_t max_code = e4m3 ? 0x7Eu : 0x7Bu;
-    const int mbits = e4m3 ? 3 : 2;
-    const int bias = e4m3 ? 7 : 15;
-    const int emin = 1 - bias;                                             // exponent of the smallest normal
-    const float a = __builtin_bit_cast(float, mag);
-    uint32_t code;
-    if (a < __builtin_ldexpf(1.0f, emin)) {
-        // Subnormal (or zero): a / 2^(emin - mbits) rounded to an integer,
-        // nearest-even; 2^mbits (a carry into the smallest normal) is that code.
-        code = (uint32_t)__builtin_rintf(__builtin_ldexpf(a, mbits - emin));
-    } else if (mag >= 0x7F800000u) {
-        code = max_code;                                                   // infinity saturates
+    const float fmax = e4m3 ? 448.0f : 57344.0f;
+    float c[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c[e] = __builtin_fminf(__builtin_fmaxf(y[e], -fmax), fmax);
+    uint32_t r;
+    if (e4m3) {
+        r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+        r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], (int)r, true);
     } else {
-        const int e = (int)(mag >> 23) - 127;                              // a = 1.f * 2^e, a normal binary32
-        const uint32_t frac = mag & 0x7FFFFFu;
-        const int drop = 23 - mbits;
-        uint32_t m = frac >> drop;
-        const uint32_t rem = frac & ((1u << drop) - 1u), half = 1u << (drop - 1);
-        if (rem > half || (rem == half && (m & 1u))) ++m;                  // nearest, ties to even
-        code = ((uint32_t)(e + bias) << mbits) + m;                        // a carry moves into the exponent
-        if (code > max_code) code = max_code;
+        r = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c[0], c[1], 0, false);
+        r = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c[2], c[3], (int)r, true);
     }
-    return sign | code;
+    if (!may_have_nan) return r;
+    const uint32_t nan_code = e4m3 ? 0x7Fu : 0x7Eu;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t bits = __builtin_bit_cast(uint32_t, y[e]);
+        if ((bits & 0x7FFFFFFFu) > 0x7F800000u)
+            r = (r & ~(0xFFu << (8 * e))) | ((((bits >> 24) & 0x80u) | nan_code) << (8 * e));
+    }
+    return r;
 }
 
 __global__ __launch_bounds__(256) void fp8_state_init_kernel(Fp8State* states, uint32_t fmt) {
@@ -88,8 +87,28 @@ __global__ __launch_bounds__(256) void fp8_state_init_kernel(Fp8State* states, u
 template <typename T>
 __device__ inline float load_f32(const T* p) { return (float)*p; }
 
-// Each thread handles 8 consecutive elements per round, grid-stride over n8
-// rounds; the tail (n % 8) is done element by element by the last threads.
+// Eight consecutive elements (16-byte aligned) as float32, with 16-byte loads.
+template <typename T>
+__device__ inline void load8(const T* p, float (&v)[8]) {
+    if constexpr (std::is_same_v<T, float>) {
+        const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+        for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
+    } else {
+        const u32x4 r = *(const u32x4*)p;
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (std::is_same_v<T, __bf16>) {
+                v[2 * e] = __builtin_bit_cast(float, r[e] << 16);
+                v[2 * e + 1] = __builtin_bit_cast(float, r[e] & 0xFFFF0000u);
+            } else {
+                v[2 * e] = (float)__builtin_bit_cast(_Float16, (uint16_t)(r[e] & 0xFFFFu));
+                v[2 * e + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(r[e] >> 16));
+            }
+        }
+    }
+}
+
+// Threads handle groups of 8 consecutive elements, grid-stride over the n / 8
+// groups; the tail (n % 8) is done element by element.
 template <typename T>
 __global__ __launch_bounds__(256) void fp8_quantize_kernel(const T* __restrict__ x, uint8_t* __restrict__ codes,
                                                            int64_t n, Fp8State* st) {
@@ -104,22 +123,41 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(const T* __restrict__
     // with a NaN (pattern above infinity) taking precedence.
     uint32_t ab = 0;
     const int64_t n8 = n / 8;
-    for (int64_t i = gid; i < n8; i += nthreads) {
-        uint32_t w[2] = {0u, 0u};
+    // Four groups of 8 per thread and round, all loads issued before any
+    // arithmetic (enough bytes in flight to run at HBM speed).
+    constexpr int UN = 4;
+    for (int64_t i0 = gid; i0 < n8; i0 += UN * nthreads) {
+        float v[UN][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float v = load_f32(x + i * 8 + e);
-            const uint32_t vb = __builtin_bit_cast(uint32_t, v) & 0x7FFFFFFFu;
-            ab = vb > ab ? vb : ab;
-            w[e / 4] |= encode_fp8(v * scale, fmt) << (8 * (e % 4));
+        for (int u = 0; u < UN; ++u) {
+            const int64_t i = i0 + u * nthreads;
+            if (i < n8) load8(x + i * 8, v[u]);
         }
-        *(u32x2*)(codes + i * 8) = (u32x2){w[0], w[1]};
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+            const int64_t i = i0 + u * nthreads;
+            if (i >= n8) break;
+            float y0[4], y1[4];
+            uint32_t gb = 0;   // largest |v| pattern of the group
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t vb = __builtin_bit_cast(uint32_t, v[u][e]) & 0x7FFFFFFFu;
+                gb = vb > gb ? vb : gb;
+                (e < 4 ? y0 : y1)[e % 4] = v[u][e] * scale;
+            }
+            ab = gb > ab ? gb : ab;
+            // NaN codes need fixing only where a NaN is present (rare): a
+            // wave-uniform test keeps the common path short.
+            const bool nan_here = __builtin_amdgcn_ballot_w64(gb > 0x7F800000u) != 0;
+            *(u32x2*)(codes + i * 8) = (u32x2){encode4_fp8(y0, fmt, nan_here), encode4_fp8(y1, fmt, nan_here)};
+        }
     }
     for (int64_t i = n8 * 8 + gid; i < n; i += nthreads) {
         const float v = load_f32(x + i);
         const uint32_t vb = __builtin_bit_cast(uint32_t, v) & 0x7FFFFFFFu;
         ab = vb > ab ? vb : ab;
-        codes[i] = (uint8_t)encode_fp8(v * scale, fmt);
+        const float y[4] = {v * scale, 0.f, 0.f, 0.f};
+        codes[i] = (uint8_t)(encode4_fp8(y, fmt) & 0xFFu);
     }
     for (int off = 32; off > 0; off >>= 1) {
         const uint32_t o = (uint32_t)__shfl_xor((int)ab, off, 64);
@@ -133,7 +171,11 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(const T* __restrict__
             const uint32_t b = __builtin_bit_cast(uint32_t, red[w]);
             m = b > m ? b : m;
         }
-        atomicMax((unsigned int*)&st->history[slot], m);
+        // The slot only grows during a step, so a workgroup whose maximum
+        // does not exceed what the slot already holds has nothing to add
+        // (this keeps most workgroups off the one contended address).
+        unsigned int* slot_p = (unsigned int*)&st->history[slot];
+        if (m > __atomic_load_n(slot_p, __ATOMIC_RELAXED)) atomicMax(slot_p, m);
     }
 }
 
@@ -181,7 +223,7 @@ hipError_t launch_fp8_quantize(const void* x, int dtype, void* codes, int64_t n,
     // Enough workgroups to fill the GPU, each thread at least 8 elements a round.
     int64_t groups = (n / 8 + 255) / 256;
     if (groups < 1) groups = 1;
-    if (groups > 2048) groups = 2048;
+    if (groups > 1024) groups = 1024;
     const dim3 grid((unsigned)groups), block(256);
     if (dtype == 0)
         hipLaunchKernelGGL(fp8_quantize_kernel<float>, grid, block, 0, stream, (const float*)x, (uint8_t*)codes, n,

@@ -51,6 +51,9 @@ class Workload:
     n_split: object = None  # None: attn_fwd; "auto" or an int: the split-key entry point
     layout: str = "bshd"    # storage of q, k, v, out on the GPU: "bshd" (dense) or "bhsd" (transposed views)
     direction: str = "fwd"  # "fwd": the forward pass; "bwd": the backward pass (attn_bwd) of that forward
+    scaling: str = "amax"   # FP8 only: "amax" (codes cast with the tensor's own amax) or "delayed"
+                            # (a whole delayed-scaling step: bf16 -> E4M3 casts with device-side
+                            # scaling states, the forward reading its factors on the device, update)
 
     @property
     def scale(self):
@@ -104,6 +107,8 @@ WORKLOADS = {w.name: w for w in [
              "backward, MHA, head dim 64", direction="bwd"),
     Workload("e4m3_mha_b4_h16_s4096_d128_causal_bwd", "e4m3", 4, 16, 16, 4096, 4096, 128, True, 9000,
              "backward of the FP8 forward: E4M3 q, k, v, E5M2 dout, bf16 gradients", direction="bwd"),
+    Workload("e4m3_delayed_mha_b4_h16_s4096_d128_causal", "e4m3", 4, 16, 16, 4096, 4096, 128, True, 9000,
+             "FP8 forward step under delayed scaling (casts + attention + scale update)", scaling="delayed"),
 ]}
 
 HEADLINE = "bf16_gqa_b2_hq32_hkv8_s4096_d128_causal"
@@ -208,7 +213,8 @@ def workload_flops(w):
 
 def io_bytes(w):
     """Algorithmic HBM bytes of one call. Forward: Q, K, V read once, O
-    written once. Backward: Q, K, V, O, dO and the row log-sum-exp read once,
+    written once (a delayed-scaling step adds its casts: bf16 read, codes
+    written). Backward: Q, K, V, O, dO and the row log-sum-exp read once,
     dQ, dK, dV written once (and the per-row Delta written and read)."""
     e = ELEM_BYTES[w.dtype]
     o = ELEM_BYTES[w.out_dtype]
@@ -217,4 +223,6 @@ def io_bytes(w):
         rows = w.B * w.Hq * w.Sq
         g = 2   # gradients are 16-bit (bf16 for FP8 inputs)
         return nq * (e + o + e + g) + nk * (2 * e + 2 * g) + 3 * rows * 4
+    if w.scaling == "delayed":   # plus the casts: bf16 in, E4M3 codes out
+        return nq * (e + o) + 2 * nk * e + (nq + 2 * nk) * (2 + 1)
     return nq * (e + o) + 2 * nk * e
