@@ -36,27 +36,35 @@ N_BUFFER_SETS = 4   # rotating input sets, so one call's inputs are not cache-wa
 SETTLE_S = 0.25     # seconds of untimed steps after the warmup steps, before timing
 
 
-def kernel_source_hash():
+# The sources a workload's kernels are built and launched from: a committed
+# traffic figure stays valid while these are unchanged.
+KERNEL_SOURCES = {
+    "fwd": ["attn_fwd_mfma.hip", "attn_combine.hip", "mfma_common.h", "kernel_common.h", "attn_api.cpp"],
+    "bwd": ["attn_bwd.hip", "attn_fwd_mfma.hip", "mfma_common.h", "kernel_common.h", "attn_api.cpp"],
+}
+
+
+def kernel_source_hash(direction="fwd"):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "scaled_dot_product_09_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in KERNEL_SOURCES[direction]:
         h.update(f.encode())
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload_name):
-    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    counters, or None if there are none for this workload or the kernel
+def load_traffic(w):
+    """HBM bytes per call from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    counters, or None if there are none for this workload or its kernel
     sources changed since they were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(path)).get(workload_name)
+        rec = json.load(open(path)).get(w.name)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("kernel_hash") != kernel_source_hash():
+    if not rec or rec.get("kernel_hash") != kernel_source_hash(w.direction):
         return None
     return rec.get("traffic_bytes")
 
@@ -204,16 +212,20 @@ def result_line(w, t, steps, warmup, n_gpus, cpu=None, warm=None):
     peak = PEAK_TFLOPS[compute]
     nbytes = io_bytes(w)
     gbps = nbytes / (ms * 1e-3) / 1e9
-    # Below the ridge point (peak flop/s over peak HBM bytes/s) the kernel is
-    # bound by HBM, not by the matrix cores.
-    hbm_bound = flops / nbytes < peak * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    # Below the ridge point (peak flop/s over peak HBM bytes/s) the attention
+    # kernel is bound by HBM, not by the matrix cores. The attention's own
+    # bytes decide (a delayed-scaling step's casts are separate HBM-bound
+    # kernels beside the dominant attention kernel).
+    from dataclasses import replace
+    attn_bytes = io_bytes(replace(w, scaling="amax"))
+    hbm_bound = flops / attn_bytes < peak * 1e12 / (PEAK_HBM_GBPS * 1e9)
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(gbps / PEAK_HBM_GBPS, 4)}
     else:
         roof = {"bound": PEAK_KIND[compute], "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(tflops / peak, 4)}
-    roof.update({"traffic": load_traffic(w.name), "algorithmic_bytes": nbytes})
+    roof.update({"traffic": load_traffic(w), "algorithmic_bytes": nbytes})
     line = {
         "metric": METRIC if w.direction == "fwd" else METRIC_BWD, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": n_gpus,
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
