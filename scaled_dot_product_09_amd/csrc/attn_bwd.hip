@@ -37,8 +37,6 @@ namespace attn {
 
 namespace {
 
-constexpr float kLog2eF = 1.4426950408889634f;
-
 template <typename T>
 __device__ inline float dot2(uint32_t a, uint32_t b, float c) {
     if constexpr (std::is_same_v<T, __bf16>)
@@ -159,7 +157,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams bp) {
     const float delta = sc.delta_mul * xor32_sum(dsum);
     const float dp_mul = sc.dp_mul;
     const size_t srow = ((size_t)wi.b * p.Hq + hq) * Sq + qrow;
-    const float lse2 = row_ok ? bp.lse[srow] * kLog2eF : 0.f;
+    const float lse2 = row_ok ? bp.lse[srow] * kLog2eF32 : 0.f;
     if (row_ok && h == 0) {   // for the dK / dV kernel
         bp.delta[srow] = delta;
         bp.lse2[srow] = lse2;
@@ -227,9 +225,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams bp) {
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) { s[kb][i] = 0.f; dp[kb][i] = 0.f; }
-        // dS^T = P^T (dP^T - Delta), P^T = 2^(c2 s - lse2) on visible keys,
-        // rounded to the input type in pairs of consecutive keys; elements
-        // i0 .. i0 + cnt - 1 of block kb.
+        // dS^T = P^T (dp_mul dP^T - Delta), P^T = 2^(c2 s - lse2) on visible
+        // keys, rounded to the input type in pairs of consecutive keys;
+        // elements i0 .. i0 + cnt - 1 of block kb.
         uint32_t pw[NKB][8];
         // Key of element i of block kb: key0 + 8 (i / 4) + i % 4, visible iff
         // its offset 8 (i / 4) + i % 4 <= lim. Blocks where every element of

@@ -108,6 +108,10 @@ BWD_CASES = [
     W("bf16", 2, 4, 2, 64, 64, 128, False),
     W("f16", 1, 8, 2, 160, 160, 128, True),
     W("f16", 1, 4, 4, 97, 150, 64, "bottom_right"),
+    W("f16", 2, 4, 1, 65, 65, 32, True),            # f16 head dim 32, MQA
+    W("bf16", 1, 4, 2, 1, 700, 128, "bottom_right"),    # one decode query, keys in 6 blocks of 128 (ragged)
+    W("bf16", 1, 2, 2, 129, 383, 64, False),        # one row past a step, keys past three blocks
+    W("bf16", 3, 8, 4, 100, 100, 128, True),        # three batches, G = 2
 ]
 
 
