@@ -69,6 +69,31 @@ def test_quantize_and_update_follow_the_oracle(fmt, dtype):
         check_state(st, ref)
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_quantize_large_input_loops_and_tail(fmt, dtype):
+    """More elements than one pass of the cast's grid covers (256 workgroups x
+    1024 threads x 8 elements), a tail of n % 8 = 5 elements and NaN-free
+    data with a single large outlier late in the array: codes and history
+    slot bit-exact against the oracle."""
+    n = 256 * 1024 * 8 * 2 + 12349                      # 4,206,653: three trips, n % 8 = 5
+    print(f"case {fmt} {dtype} n={n}", flush=True)
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal(n).astype(np.float32) * 3.0
+    x[n - 3] = -700.0 if fmt == "e4m3" else -90000.0    # saturates; the amax sits in the tail
+    xt = torch.from_numpy(x).to(dtype)
+    ref = oracle.DelayedScalingState(fmt)
+    st = attn.fp8_states(1, FMT[fmt])[0]
+    for step in range(2):                                # scale 1, then fmax / amax
+        want = ref.quantize(xt.float().numpy())
+        got = attn.fp8_quantize(xt.to(DEV), st, FMT[fmt])
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().view(torch.uint8).numpy(), want), step
+        attn.fp8_update(st)
+        ref.update()
+        check_state(st, ref)
+
+
 def test_nan_amax_and_shared_step():
     """Two casts in one step combine their amaxes; a NaN input freezes the
     scale for as long as it stays in the history (as in the oracle)."""
