@@ -126,6 +126,34 @@ def test_backward_parity(w):
     check_grads(w, got, want)
 
 
+@pytest.mark.parametrize("dtype,D,causal", [("bf16", 128, True), ("f16", 64, False), ("bf16", 64, "bottom_right")])
+def test_backward_growing_row_maxima(dtype, D, causal):
+    """Keys drift along the sequence so that every row's scores rise by about
+    15 in exp2 terms per 64 keys, to about 2^140 at the last of 600 keys: the
+    weights are rebuilt from the forward's lse at scores whose plain
+    exponentials would overflow float32.
+
+    The rise comes mostly from queries with a large mean (2 per component)
+    and only a small drift of the keys (at most ~4-6 per component): dQ =
+    scale dS K inherits the error of Delta = rowsum(dO * out), formed from the
+    forward's rounded output, multiplied by the size of the keys, which no
+    kernel can avoid when keys share a large common offset."""
+    w = W(dtype, 1, 4, 2, 600, 600, D, causal, seed=33)
+    print(f"case {w.name} (drifting keys)", flush=True)
+    rng = np.random.default_rng(33)
+    slope = 0.081 / np.sqrt(D)            # 2 sqrt(D) slope log2(e) = 0.234 per key
+    qn = 2.0 + 0.5 * rng.standard_normal((1, 600, 4, D))
+    kn = 0.5 * rng.standard_normal((1, 600, 2, D)) + slope * np.arange(600)[None, :, None, None]
+    vn = rng.standard_normal((1, 600, 2, D))
+    td = workload.TORCH_DTYPE[dtype]
+    q, k, v = (torch.from_numpy(x.astype(np.float32)).to(td) for x in (qn, kn, vn))
+    g = workload.make_dout(w)
+    got = run_backward(w, q, k, v, g)
+    want = oracle.sdpa_backward(*(helpers.to_f64(x, w.dtype) for x in (q, k, v, g)), scale=w.scale,
+                                causal=w.causal)
+    check_grads(w, got, want)
+
+
 FP8_CASES = [
     W("e4m3", 1, 4, 2, 200, 200, 128, True),
     W("e4m3", 1, 4, 4, 130, 257, 64, False),
