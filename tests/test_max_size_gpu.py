@@ -87,3 +87,42 @@ def test_largest_kv_head(inputs, n_split):
     assert err <= 2e-2, err
     # The answer is essentially the needle's value row, unlike V's mean.
     assert float(np.max(np.abs(want[0, :, :, :] - v[0, J, 0, :].double().cpu().numpy()[None]))) < 1e-4
+
+
+def test_largest_query_tensor():
+    """q and out of 2^31 - 384 elements (16,777,213 query rows of one head,
+    D = 128) against 70 keys, top-left causal: query offsets run up to just
+    below 2^32 bytes. Sampled rows against the fp64 oracle (each needs only
+    its own query row and the 70 keys), among them the first and last rows
+    and rows on either side of the 2 GiB offset."""
+    from tests import helpers
+    print(f"case max-size query tensor, Sq={SKV}, Skv=70", flush=True)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(41)
+    q = torch.empty((1, SKV, 1, D), dtype=torch.bfloat16, device=DEV)
+    step = 1 << 20
+    for i0 in range(0, SKV, step):
+        n = min(step, SKV - i0)
+        q[0, i0:i0 + n, 0, :] = torch.randn((n, D), generator=gen, device=DEV).to(torch.bfloat16)
+    kv = torch.randn((2, 1, 70, 1, D), generator=gen, device=DEV).to(torch.bfloat16)
+    k, v = kv[0].contiguous(), kv[1].contiguous()
+    out = attn.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    half = (1 << 30) // D                        # the row starting at byte 2^31
+    rows = sorted({0, 1, 63, 69, 70, 71, half - 1, half, half + 1, SKV - 65, SKV - 2, SKV - 1,
+                   *np.random.default_rng(41).integers(0, SKV, 16).tolist()})
+    idx = torch.tensor(rows, device=DEV)
+    got = helpers.out_to_f64(out[0, idx, 0, :])
+    qs = q[0, idx, 0, :].cpu()
+    kc, vc = k.cpu(), v.cpu()
+    want = np.stack([oracle_row(qs[r], kc, vc, i) for r, i in enumerate(rows)])
+    err = helpers.max_abs_err(got, want)
+    print(f"  {len(rows)} rows, max-abs {err:.3e}", flush=True)
+    assert err <= 2e-2, err
+
+
+def oracle_row(qrow, k, v, i):
+    import oracle
+    from tests import helpers
+    return oracle.sdpa_one_row(helpers.to_f64(qrow, "bf16"), helpers.to_f64(k[0, :, 0], "bf16"),
+                               helpers.to_f64(v[0, :, 0], "bf16"), i=i, scale=1.0 / math.sqrt(D), causal=True)
