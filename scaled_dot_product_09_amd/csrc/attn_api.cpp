@@ -14,10 +14,10 @@
 #include "kernel_common.h"
 
 namespace attn {
-hipError_t launch_fwd_mfma(const FwdParams& p, int D, bool is_bf16, bool causal, int nwaves, hipStream_t stream);
+hipError_t launch_fwd_mfma(const FwdParams& p, int D, bool is_bf16, bool causal, int nwaves, int rb,
+                           hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int D, bool causal, hipStream_t stream);
-hipError_t launch_fwd_fp8(const FwdParams& p, int D, bool causal, int nwaves, hipStream_t stream);
-hipError_t launch_fwd_rb2(const FwdParams& p, int D, int dtype, bool causal, hipStream_t stream);
+hipError_t launch_fwd_fp8(const FwdParams& p, int D, bool causal, int nwaves, int rb, hipStream_t stream);
 hipError_t launch_fwd_pp(const FwdParams& p, int D, int dtype, bool causal, hipStream_t stream);
 hipError_t launch_combine(const FwdParams& p, int D, bool is_bf16, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& bp, int D, bool is_bf16, bool causal, hipStream_t stream);
@@ -135,10 +135,14 @@ float nonzero_multiplier(float c) { return c == 0.0f ? 0x1p-100f : c; }
 // Matrix-core kernel choice. Default: "w4", four independent waves per
 // workgroup (32 query rows each) and two workgroups per CU. Also built,
 // selectable with ATTN_KERNEL in the environment (the tests cover every one
-// on every shape): "pp", eight waves in two ping-pong groups of four, and
-// "rb2", 64 rows per wave, one wave per SIMD. Both measure slower on every
-// shape so far: on gfx950 a wave's matrix ops do not overlap another wave's
-// vector ops on the same SIMD, so the ping-pong split gains nothing.
+// on every shape): "w8", the same kernel with eight waves per workgroup;
+// "pp", eight waves in two ping-pong groups of four; and "rb2", the
+// four-wave kernel with two 32-row blocks per wave (64 query rows), every
+// K / V operand read from LDS shared by both blocks (half the LDS reads per
+// flop) at one wave per SIMD. All three measure slower on every shape so
+// far: on gfx950 a wave's matrix ops do not overlap another wave's vector
+// ops on the same SIMD, so the ping-pong split gains nothing, and the second
+// wave per SIMD hides more stall time than halving the LDS reads saves.
 enum MfmaKernel { kPingPong, kFourWave, kEightWave, kRows64 };
 
 MfmaKernel mfma_kernel() {
@@ -157,11 +161,13 @@ hipError_t launch_mfma(const void* q, const void* k, const void* v, void* out,
     // Head dimension 32, strided layouts, the log-sum-exp output and
     // device-side FP8 factors exist only in the four- and eight-wave kernel.
     const bool four_or_eight = D == 32 || strides || lse || dsc;
-    const MfmaKernel kern = (four_or_eight && (mfma_kernel() == kPingPong || mfma_kernel() == kRows64))
-                                ? kFourWave : mfma_kernel();
+    MfmaKernel kern = (four_or_eight && mfma_kernel() == kPingPong) ? kFourWave : mfma_kernel();
+    // Two row blocks per wave: 16-bit inputs with D >= 64 only.
+    if (kern == kRows64 && (D == 32 || dtype == ATTN_FP8_E4M3)) kern = kFourWave;
+    const int rb = kern == kRows64 ? 2 : 1;
     const int rpw = kern == kRows64 ? 64 : 32;
     const int waves = (kern == kPingPong || kern == kEightWave) ? 8 : 4;
-    const bool wide = kern == kFourWave || kern == kEightWave;
+    const bool wide = kern != kPingPong;
     attn::FwdParams p = make_params(q, k, v, out, B, Hq, Hkv, Sq, Skv, scale_log2, out_mul,
                                     causal, true, rpw, waves, wide);
     if (strides) {
@@ -179,11 +185,11 @@ hipError_t launch_mfma(const void* q, const void* k, const void* v, void* out,
     }
     const bool masked = causal != 0;
     switch (kern) {
-        case kRows64: return attn::launch_fwd_rb2(p, D, dtype, masked, stream);
         case kFourWave:
         case kEightWave:
-            return dtype == ATTN_FP8_E4M3 ? attn::launch_fwd_fp8(p, D, masked, waves, stream)
-                                          : attn::launch_fwd_mfma(p, D, dtype == ATTN_BF16, masked, waves, stream);
+        case kRows64:
+            return dtype == ATTN_FP8_E4M3 ? attn::launch_fwd_fp8(p, D, masked, waves, rb, stream)
+                                          : attn::launch_fwd_mfma(p, D, dtype == ATTN_BF16, masked, waves, rb, stream);
         default: return attn::launch_fwd_pp(p, D, dtype, masked, stream);
     }
 }
@@ -342,7 +348,7 @@ extern "C" int attn_fwd_split(const void* q, const void* k, const void* v, void*
     p.n_split = n_split;
     p.part_o = (float*)workspace;
     p.part_ml = (float*)workspace + (size_t)n_split * B * Sq * Hq * D;
-    hipError_t e = attn::launch_fwd_mfma(p, D, dtype == ATTN_BF16, causal != 0, 4, stream);
+    hipError_t e = attn::launch_fwd_mfma(p, D, dtype == ATTN_BF16, causal != 0, 4, 1, stream);
     if (e == hipSuccess) e = attn::launch_combine(p, D, dtype == ATTN_BF16, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }

@@ -45,8 +45,11 @@
 
 namespace attn {
 
-template <typename T, int D, int BN, bool CAUSAL, int NWAVES>
-__global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdParams p) {
+// RB = 32-row blocks per wave (1 or 2). With RB = 2 every K / V operand read
+// from LDS feeds the MFMAs of both blocks, which halves LDS reads per flop;
+// the doubled accumulators need the whole register file (one wave per SIMD).
+template <typename T, int D, int BN, bool CAUSAL, int NWAVES, int RB>
+__global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfma_kernel(FwdParams p) {
     using Tr = Traits<T>;
     using qk_frag = typename Tr::qk_frag;
     using pv_frag = typename Tr::pv_frag;
@@ -85,18 +88,21 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
     // 32 wave + n. With HS = 32 a wave holds 32 rows of one head; with
     // fewer rows than that per head (decode with GQA / MQA) a wave's 32 MFMA
     // columns hold rows of several heads instead of empty rows.
+    // With RB = 2, row block r of the wave owns slots 32 (2 wave + r) + n.
     const int HS = p.head_stride;
-    const int slot = wave * 32 + n;
-    const int hq = wi.hq0 + (slot / HS) % p.gpack;
-    const int qrow = wi.row_base + (slot / (HS * p.gpack)) * HS + slot % HS;
+    int hq[RB], qrow[RB];
+    for (int r = 0; r < RB; ++r) {
+        const int slot = (wave * RB + r) * 32 + n;
+        hq[r] = wi.hq0 + (slot / HS) % p.gpack;
+        qrow[r] = wi.row_base + (slot / (HS * p.gpack)) * HS + slot % HS;
+    }
     // No slot of this wave holds a query row (its first slot has its
     // smallest row): it only copies tiles and keeps the workgroup's barriers.
     const bool wave_idle =
-        __builtin_amdgcn_readfirstlane(wi.row_base + (wave * 32 / (HS * p.gpack)) * HS) >= p.Sq;
+        __builtin_amdgcn_readfirstlane(wi.row_base + (wave * RB * 32 / (HS * p.gpack)) * HS) >= p.Sq;
     const int Sq = p.Sq;
     int Skv = p.Skv;                                   // keys of this workgroup's range, from its start
 
-    const T* qbase = (const T*)p.q + wi.b * p.sq[0] + hq * p.sq[2];
     const uint8_t* kbase = (const uint8_t*)((const T*)p.k + wi.b * p.sk[0] + wi.hkv * p.sk[2]);
     const uint8_t* vbase = (const uint8_t*)((const T*)p.v + wi.b * p.sv[0] + wi.hkv * p.sv[2]);
     const size_t krow_b = (size_t)p.sk[1] * Tr::IN_BYTES;   // bytes between keys
@@ -108,9 +114,10 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
     // is exactly -(q.k) (negation is exact and the products are summed in
     // the same order), with the multiplier |c|, so the softmax below only
     // ever sees c >= 0 and masks with -inf.
-    qk_frag qf[KSTEPS];
-    {
-        const int row = qrow;
+    qk_frag qf[RB][KSTEPS];
+    for (int r = 0; r < RB; ++r) {
+        const int row = qrow[r];
+        const T* qbase = (const T*)p.q + wi.b * p.sq[0] + hq[r] * p.sq[2];
         const uint8_t* src = (const uint8_t*)(qbase + row * p.sq[1]);
         const uint32_t flip = sl2 < 0.f ? Tr::SIGN_BITS : 0u;
         for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -121,9 +128,9 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
                 x[t] ^= flip;
             }
             if constexpr (CH == 1) {
-                qf[ks] = __builtin_bit_cast(qk_frag, x[0]);
+                qf[r][ks] = __builtin_bit_cast(qk_frag, x[0]);
             } else {
-                qf[ks] = __builtin_bit_cast(qk_frag, (i32x8){(int)x[0][0], (int)x[0][1], (int)x[0][2], (int)x[0][3],
+                qf[r][ks] = __builtin_bit_cast(qk_frag, (i32x8){(int)x[0][0], (int)x[0][1], (int)x[0][2], (int)x[0][3],
                                                              (int)x[1][0], (int)x[1][1], (int)x[1][2], (int)x[1][3]});
             }
         }
@@ -152,13 +159,15 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
         Skv -= tb * BN;
         coff -= tb * BN;
         if (n_tiles == 0) {   // no keys in range: weight sum 0, max -inf, output 0
-            const int row = qrow;
-            if (row < Sq) {
-                const size_t r = (qrow_idx + row) * p.Hq + hq;
-                for (int db = 0; db < NDB; ++db)
-                    for (int jj = 0; jj < 4; ++jj)
-                        *(f32x4*)(p.part_o + r * D + db * 32 + 8 * jj + 4 * h) = (f32x4){0.f, 0.f, 0.f, 0.f};
-                if (h == 0) *(f32x2*)(p.part_ml + r * 2) = (f32x2){-INFINITY, 0.f};
+            for (int rb = 0; rb < RB; ++rb) {
+                const int row = qrow[rb];
+                if (row < Sq) {
+                    const size_t r = (qrow_idx + row) * p.Hq + hq[rb];
+                    for (int db = 0; db < NDB; ++db)
+                        for (int jj = 0; jj < 4; ++jj)
+                            *(f32x4*)(p.part_o + r * D + db * 32 + 8 * jj + 4 * h) = (f32x4){0.f, 0.f, 0.f, 0.f};
+                    if (h == 0) *(f32x2*)(p.part_ml + r * 2) = (f32x2){-INFINITY, 0.f};
+                }
             }
             return;
         }
@@ -220,12 +229,18 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
     };
 
     // ---- running softmax state (per lane: query n, partial over its keys) --
-    f32x16 oacc[NDB];
-    for (int db = 0; db < NDB; ++db)
-        for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-    float m_run = -INFINITY;   // running max of scale*log2(e)*score (same on both halves)
-    float l_part = 0.f;        // this lane's share of the running denominator
-    float neg_m = 0.f;         // exponent offset -m_run of the tile being weighted
+    f32x16 oacc[RB][NDB];
+    for (int r = 0; r < RB; ++r)
+        for (int db = 0; db < NDB; ++db)
+            for (int i = 0; i < 16; ++i) oacc[r][db][i] = 0.f;
+    float m_run[RB];    // running max of scale*log2(e)*score (same on both halves)
+    float l_part[RB];   // this lane's share of the running denominator
+    float neg_m[RB];    // exponent offset -m_run of the tile being weighted
+    for (int r = 0; r < RB; ++r) {
+        m_run[r] = -INFINITY;
+        l_part[r] = 0.f;
+        neg_m[r] = 0.f;
+    }
 
     const float c_log2 = fabsf(sl2);   // > 0: never 0 (see fwd_scalars)
 
@@ -280,16 +295,18 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
 
     // S^T = K Q^T for one tile (all 32-key blocks), K operands fetched one
     // k-step ahead.
-    auto qk_tile = [&](const uint8_t* kt, f32x16 (&s)[NKB]) {
-        for (int kb = 0; kb < NKB; ++kb)
-            for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+    auto qk_tile = [&](const uint8_t* kt, f32x16 (&s)[RB][NKB]) {
+        for (int r = 0; r < RB; ++r)
+            for (int kb = 0; kb < NKB; ++kb)
+                for (int i = 0; i < 16; ++i) s[r][kb][i] = 0.f;
         qk_frag cur[NKB], nxt[NKB];
         for (int kb = 0; kb < NKB; ++kb) cur[kb] = load_k(kt, kb, 0);
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
             if (ks + 1 < KSTEPS)
                 for (int kb = 0; kb < NKB; ++kb) nxt[kb] = load_k(kt, kb, ks + 1);
-            for (int kb = 0; kb < NKB; ++kb) s[kb] = Tr::qk(cur[kb], qf[ks], s[kb]);
+            for (int kb = 0; kb < NKB; ++kb)
+                for (int r = 0; r < RB; ++r) s[r][kb] = Tr::qk(cur[kb], qf[r][ks], s[r][kb]);
             if (ks + 1 < KSTEPS)
                 for (int kb = 0; kb < NKB; ++kb) cur[kb] = nxt[kb];
         }
@@ -300,21 +317,22 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
     // few instructions per 32-key block and is skipped (wave-uniformly)
     // wherever no key of the block is hidden from any row of the wave.
     const float masked = -INFINITY;
-    auto mask_tile = [&](f32x16 (&s)[NKB], int j) {
+    auto mask_tile = [&](f32x16 (&s)[NKB], int j, int r) {
         for (int kb = 0; kb < NKB; ++kb) {
-            const int kbase_h = j * BN + kb * 32 + 4 * h;       // key of element i: kbase_h + koff(i)
-            int lim = Skv - 1 - kbase_h;                         // last existing key offset
-            if (CAUSAL) lim = min(lim, qrow + coff - kbase_h);   // last visible key offset
+            const int kbase_h = j * BN + kb * 32 + 4 * h;          // key of element i: kbase_h + koff(i)
+            int lim = Skv - 1 - kbase_h;                            // last existing key offset
+            if (CAUSAL) lim = min(lim, qrow[r] + coff - kbase_h);   // last visible key offset
             if (__builtin_amdgcn_ballot_w64(lim < 27) != 0) {   // 27 = largest koff(i)
                 for (int i = 0; i < 16; ++i)
                     s[kb][i] = (8 * (i >> 2) + (i & 3) > lim) ? masked : s[kb][i];
             }
         }
     };
-    // Partial row max of scores 16 g .. 16 g + 15 (block g / 1),
-    // split into four pieces so it can ride along the PV MFMA groups.
-    auto max_piece = [&](const f32x16 (&s)[NKB], int piece, float m) -> float {
-        constexpr int PER = NKB * 16 / 4;                        // scores per piece
+    // Partial row max of one of NP equal pieces of a tile's scores, so it can
+    // ride along the PV MFMA groups (NP = 2 NKB of them) or be formed in
+    // four steps after the first tile's scores.
+    auto max_piece = [&](const f32x16 (&s)[NKB], int piece, float m, auto np_tag) -> float {
+        constexpr int PER = NKB * 16 / decltype(np_tag)::value;   // scores per piece
         const int base = piece * PER;
         for (int e = 0; e < PER; e += 2) {
             const int x = base + e;
@@ -325,18 +343,18 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
     // From this lane's raw max of a tile: the row max in the log2 domain, the
     // lazy rescale of O and l (only when the max grew by more than 8, i.e. a
     // factor 2^8), and the new exponent offset -m.
-    auto finish_max = [&](float mraw) -> float {
+    auto finish_max = [&](float mraw, int r) -> float {
         // c_log2 > 0, so a fully masked row gives -inf * c = -inf here.
         const float mt = xor32_max(mraw * c_log2);
-        const float mnew = fmaxf(m_run, mt);
-        if (__builtin_amdgcn_ballot_w64(mnew > m_run + 8.0f) != 0) {
-            const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);   // 0 on the first tile
+        const float mnew = fmaxf(m_run[r], mt);
+        if (__builtin_amdgcn_ballot_w64(mnew > m_run[r] + 8.0f) != 0) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run[r] - mnew);   // 0 on the first tile
             for (int db = 0; db < NDB; ++db)
-                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-            l_part *= alpha;
-            m_run = mnew;
+                for (int i = 0; i < 16; ++i) oacc[r][db][i] *= alpha;
+            l_part[r] *= alpha;
+            m_run[r] = mnew;
         }
-        return (m_run == -INFINITY) ? 0.f : -m_run;
+        return (m_run[r] == -INFINITY) ? 0.f : -m_run[r];
     };
 
     // One pipelined iteration over tile j. With HAS_NEXT (tile j+1 exists):
@@ -354,7 +372,7 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
     // access of the iteration with its buffer's scope, which is what lets
     // the compiler see that copies into kb_cur / vb_next never alias reads of
     // kb_next / vb_cur (otherwise it makes the reads wait for the copies).
-    auto iteration = [&](auto has_next_tag, int j, f32x16 (&s_cur)[NKB], f32x16 (&s_nxt)[NKB],
+    auto iteration = [&](auto has_next_tag, int j, f32x16 (&s_cur)[RB][NKB], f32x16 (&s_nxt)[RB][NKB],
                          uint8_t* __restrict__ kb_cur, uint8_t* __restrict__ kb_next,
                          uint8_t* __restrict__ vb_cur, uint8_t* __restrict__ vb_next) {
         constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
@@ -363,7 +381,7 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
             if (j + 2 < n_tiles) issue_k(j + 2, kb_cur);
             issue_v(j + 1, vb_next);
         }
-        uint32_t pw[NKB][8];
+        uint32_t pw[RB][NKB][8];
         pv_frag vf[2][NDB];     // V operands of two consecutive PV groups
         // Weights of tile j in two stages, so that no dependency chain sits
         // inside one k-step: stage 1 (scale, offset, exp2) of group g runs in
@@ -372,21 +390,21 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
         // added to the row sum in phase B, beside the PV products that use
         // them, where the vector unit has more room than in phase A
         // (measured: 1.7 % faster at head dim 64, 3.8 % at 32, same at 128).
-        float ex[NKB * 8][2];
-        auto weight_exp = [&](int pp) {
+        float ex[RB][NKB * 8][2];
+        auto weight_exp = [&](int r, int pp) {
             const int kb = pp / 8, i = pp % 8;
-            const float x0 = fmaf(s_cur[kb][2 * i], c_log2, neg_m);
-            const float x1 = fmaf(s_cur[kb][2 * i + 1], c_log2, neg_m);
-            ex[pp][0] = __builtin_amdgcn_exp2f(x0);
-            ex[pp][1] = __builtin_amdgcn_exp2f(x1);
+            const float x0 = fmaf(s_cur[r][kb][2 * i], c_log2, neg_m[r]);
+            const float x1 = fmaf(s_cur[r][kb][2 * i + 1], c_log2, neg_m[r]);
+            ex[r][pp][0] = __builtin_amdgcn_exp2f(x0);
+            ex[r][pp][1] = __builtin_amdgcn_exp2f(x1);
             // Keep the weights where they are computed (between the score
             // MFMAs) instead of letting the compiler sink them to their use.
-            asm volatile("" : "+v"(ex[pp][0]), "+v"(ex[pp][1]));
+            asm volatile("" : "+v"(ex[r][pp][0]), "+v"(ex[r][pp][1]));
         };
-        auto weight_pack = [&](int pp) {
+        auto weight_pack = [&](int r, int pp) {
             const int kb = pp / 8, i = pp % 8;
-            pw[kb][i] = Tr::pack(ex[pp][0], ex[pp][1]);
-            asm volatile("" : "+v"(pw[kb][i]));
+            pw[r][kb][i] = Tr::pack(ex[r][pp][0], ex[r][pp][1]);
+            asm volatile("" : "+v"(pw[r][kb][i]));
         };
         // ---- A ---------------------------------------------------------------
         // Phase A is the one that mixes score MFMAs with the softmax VALU
@@ -399,8 +417,9 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
             constexpr int PAIRS = NKB * 8;
             constexpr int PER_STEP = PAIRS / KSTEPS;
             static_assert(PER_STEP * KSTEPS == PAIRS, "weight pairs must split evenly over k-steps");
-            for (int kb = 0; kb < NKB; ++kb)
-                for (int i = 0; i < 16; ++i) s_nxt[kb][i] = 0.f;
+            for (int r = 0; r < RB; ++r)
+                for (int kb = 0; kb < NKB; ++kb)
+                    for (int i = 0; i < 16; ++i) s_nxt[r][kb][i] = 0.f;
             // K operands are fetched two k-steps ahead; the V operands of the
             // first PV group are fetched during the last k-step.
             qk_frag kf[3][NKB];
@@ -413,50 +432,63 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
                     for (int kb = 0; kb < NKB; ++kb) kf[(ks + 2) % 3][kb] = load_k(kb_next, kb, ks + 2);
                 if (ks + 1 == KSTEPS)
                     for (int db = 0; db < NDB; ++db) vf[0][db] = load_v(vb_cur, 0, 0, db);
-                for (int kb = 0; kb < NKB; ++kb) s_nxt[kb] = Tr::qk(kf[ks % 3][kb], qf[ks], s_nxt[kb]);
+                for (int kb = 0; kb < NKB; ++kb)
+                    for (int r = 0; r < RB; ++r) s_nxt[r][kb] = Tr::qk(kf[ks % 3][kb], qf[r][ks], s_nxt[r][kb]);
 #pragma unroll
-                for (int t = 0; t < PER_STEP; ++t) weight_exp(ks * PER_STEP + t);
+                for (int r = 0; r < RB; ++r)
+                    for (int t = 0; t < PER_STEP; ++t) weight_exp(r, ks * PER_STEP + t);
                 if (ks > 0) {
 #pragma unroll
-                    for (int t = 0; t < PER_STEP; ++t) weight_pack((ks - 1) * PER_STEP + t);
+                    for (int r = 0; r < RB; ++r)
+                        for (int t = 0; t < PER_STEP; ++t) weight_pack(r, (ks - 1) * PER_STEP + t);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
-            for (int t = 0; t < PER_STEP; ++t) weight_pack((KSTEPS - 1) * PER_STEP + t);
+            for (int r = 0; r < RB; ++r)
+                for (int t = 0; t < PER_STEP; ++t) weight_pack(r, (KSTEPS - 1) * PER_STEP + t);
             // ---- A' ------------------------------------------------------------
-            mask_tile(s_nxt, j + 1);
+            for (int r = 0; r < RB; ++r) mask_tile(s_nxt[r], j + 1, r);
         } else {
 #pragma unroll
-            for (int pp = 0; pp < NKB * 8; ++pp) weight_exp(pp);
+            for (int r = 0; r < RB; ++r)
+                for (int pp = 0; pp < NKB * 8; ++pp) weight_exp(r, pp);
 #pragma unroll
-            for (int pp = 0; pp < NKB * 8; ++pp) weight_pack(pp);
+            for (int r = 0; r < RB; ++r)
+                for (int pp = 0; pp < NKB * 8; ++pp) weight_pack(r, pp);
             for (int db = 0; db < NDB; ++db) vf[0][db] = load_v(vb_cur, 0, 0, db);
         }
         // ---- B -----------------------------------------------------------------
         __builtin_amdgcn_s_setprio(0);
-        float mraw = masked;
+        float mraw[RB];
+        for (int r = 0; r < RB; ++r) mraw[r] = masked;
 #pragma unroll
         for (int g = 0; g < NKB * 2; ++g) {
             const int kb = g / 2, s2 = g % 2;
-            const pv_frag pf = __builtin_bit_cast(pv_frag, (u32x4){pw[kb][4 * s2], pw[kb][4 * s2 + 1],
-                                                                   pw[kb][4 * s2 + 2], pw[kb][4 * s2 + 3]});
             // V operands of the next group are fetched while this group's MFMAs run.
             if (g + 1 < NKB * 2)
                 for (int db = 0; db < NDB; ++db) vf[(g + 1) & 1][db] = load_v(vb_cur, (g + 1) / 2, (g + 1) % 2, db);
-            for (int db = 0; db < NDB; ++db) oacc[db] = Tr::pv(vf[g & 1][db], pf, oacc[db]);
+            for (int r = 0; r < RB; ++r) {
+                const pv_frag pf = __builtin_bit_cast(pv_frag, (u32x4){pw[r][kb][4 * s2], pw[r][kb][4 * s2 + 1],
+                                                                       pw[r][kb][4 * s2 + 2], pw[r][kb][4 * s2 + 3]});
+                for (int db = 0; db < NDB; ++db) oacc[r][db] = Tr::pv(vf[g & 1][db], pf, oacc[r][db]);
+            }
             // Row sum over this group's rounded weights (left unpinned, so the
             // compiler places the dot products in the gaps between the MFMAs).
-            for (int t = 0; t < 4; ++t) l_part = Tr::sum2(pw[kb][4 * s2 + t], l_part);
-            if constexpr (HAS_NEXT) mraw = max_piece(s_nxt, g, mraw);
+            for (int r = 0; r < RB; ++r)
+                for (int t = 0; t < 4; ++t) l_part[r] = Tr::sum2(pw[r][kb][4 * s2 + t], l_part[r]);
+            if constexpr (HAS_NEXT)
+                for (int r = 0; r < RB; ++r)
+                    mraw[r] = max_piece(s_nxt[r], g, mraw[r], std::integral_constant<int, NKB * 2>{});
             __builtin_amdgcn_sched_barrier(0);
         }
         // ---- C -----------------------------------------------------------------
-        if constexpr (HAS_NEXT) neg_m = finish_max(mraw);
+        if constexpr (HAS_NEXT)
+            for (int r = 0; r < RB; ++r) neg_m[r] = finish_max(mraw[r], r);
         if constexpr (HAS_NEXT) finish_v(vb_next);
     };
 
-    f32x16 s0[NKB], s1[NKB];
+    f32x16 s0[RB][NKB], s1[RB][NKB];
     issue_k(0, kbuf0);
     issue_v(0, vbuf0);
     if (n_tiles > 1) issue_k(1, kbuf1);
@@ -464,11 +496,13 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
     dma_barrier();
     if (!wave_idle) {
         qk_tile(kbuf0, s0);
-        mask_tile(s0, 0);
-        float mraw = masked;
+        for (int r = 0; r < RB; ++r) {
+            mask_tile(s0[r], 0, r);
+            float mraw = masked;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) mraw = max_piece(s0, g, mraw);
-        neg_m = finish_max(mraw);
+            for (int g = 0; g < 4; ++g) mraw = max_piece(s0[r], g, mraw, std::integral_constant<int, 4>{});
+            neg_m[r] = finish_max(mraw, r);
+        }
     }
     if (wave_idle) {
         // Same copies and barriers as an iteration, no compute.
@@ -495,71 +529,88 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void fwd_mfma_kernel(FwdPa
     }
 
     // ---- epilogue: O = O^T / l, round once, store [b][row][hq][d] ----------
-    const float l = xor32_sum(l_part);
-    if (p.n_split > 1) {
-        // Partial result of this key range: O and l relative to 2^m_run.
-        if (qrow < Sq) {
-            const size_t r = (qrow_idx + qrow) * p.Hq + hq;
-            for (int db = 0; db < NDB; ++db)
-                for (int jj = 0; jj < 4; ++jj)
-                    *(f32x4*)(p.part_o + r * D + db * 32 + 8 * jj + 4 * h) =
-                        (f32x4){oacc[db][4 * jj], oacc[db][4 * jj + 1], oacc[db][4 * jj + 2], oacc[db][4 * jj + 3]};
-            if (h == 0) *(f32x2*)(p.part_ml + r * 2) = (f32x2){m_run, l};
+    for (int rb = 0; rb < RB; ++rb) {
+        const float l = xor32_sum(l_part[rb]);
+        const int row = qrow[rb];
+        if (p.n_split > 1) {
+            // Partial result of this key range: O and l relative to 2^m_run.
+            if (row < Sq) {
+                const size_t r = (qrow_idx + row) * p.Hq + hq[rb];
+                for (int db = 0; db < NDB; ++db)
+                    for (int jj = 0; jj < 4; ++jj)
+                        *(f32x4*)(p.part_o + r * D + db * 32 + 8 * jj + 4 * h) =
+                            (f32x4){oacc[rb][db][4 * jj], oacc[rb][db][4 * jj + 1], oacc[rb][db][4 * jj + 2],
+                                    oacc[rb][db][4 * jj + 3]};
+                if (h == 0) *(f32x2*)(p.part_ml + r * 2) = (f32x2){m_run[rb], l};
+            }
+            continue;
         }
-        return;
-    }
-    const float inv = out_mul / l;
-    // Row log-sum-exp: the weights are 2^(c s - m_run) with c = scale log2(e),
-    // so sum_j e^(scale s_j) = 2^m_run l and its logarithm is (m_run + log2 l) ln 2.
-    if (p.lse && qrow < Sq && h == 0)
-        p.lse[((size_t)wi.b * p.Hq + hq) * Sq + qrow] = (m_run + __builtin_amdgcn_logf(l)) * kLn2;
-    if (qrow < Sq) {
-        out_t* orow = (out_t*)p.out + wi.b * p.so[0] + qrow * p.so[1] + hq * p.so[2];
-        for (int db = 0; db < NDB; ++db) {
-            for (int jj = 0; jj < 4; ++jj) {
-                const int d0 = db * 32 + 8 * jj + 4 * h;
-                const uint32_t w0 = Tr::pack(oacc[db][4 * jj + 0] * inv, oacc[db][4 * jj + 1] * inv);
-                const uint32_t w1 = Tr::pack(oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv);
-                *(u32x2*)(orow + d0) = (u32x2){w0, w1};
+        const float inv = out_mul / l;
+        // Row log-sum-exp: the weights are 2^(c s - m_run) with c = scale log2(e),
+        // so sum_j e^(scale s_j) = 2^m_run l and its logarithm is (m_run + log2 l) ln 2.
+        if (p.lse && row < Sq && h == 0)
+            p.lse[((size_t)wi.b * p.Hq + hq[rb]) * Sq + row] = (m_run[rb] + __builtin_amdgcn_logf(l)) * kLn2;
+        if (row < Sq) {
+            out_t* orow = (out_t*)p.out + wi.b * p.so[0] + row * p.so[1] + hq[rb] * p.so[2];
+            for (int db = 0; db < NDB; ++db) {
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int d0 = db * 32 + 8 * jj + 4 * h;
+                    const uint32_t w0 = Tr::pack(oacc[rb][db][4 * jj + 0] * inv, oacc[rb][db][4 * jj + 1] * inv);
+                    const uint32_t w1 = Tr::pack(oacc[rb][db][4 * jj + 2] * inv, oacc[rb][db][4 * jj + 3] * inv);
+                    *(u32x2*)(orow + d0) = (u32x2){w0, w1};
+                }
             }
         }
     }
 }
 
+// nwaves = 8: eight waves of 32 rows; nwaves = 4: four waves of 32 rows
+// (rb = 1) or of 64 rows (rb = 2: 16-bit inputs, head dims 64 and 128, with
+// 32-key tiles so that both blocks' double-buffered scores fit the vector
+// registers; other cases run rb = 1).
 template <typename T, int D, int BN>
-static hipError_t launch_typed(const FwdParams& p, bool causal, int nwaves, hipStream_t stream) {
+static hipError_t launch_typed(const FwdParams& p, bool causal, int nwaves, int rb, hipStream_t stream) {
     const dim3 grid(p.n_units * p.n_row_blocks * p.n_split), block(64 * nwaves);
     if (nwaves == 8) {
         if (causal)
-            hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, true, 8>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, true, 8, 1>), grid, block, 0, stream, p);
         else
-            hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, false, 8>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, false, 8, 1>), grid, block, 0, stream, p);
+    } else if (rb == 2 && D >= 64 && sizeof(T) == 2) {
+        if constexpr (D >= 64 && sizeof(T) == 2) {
+            if (causal)
+                hipLaunchKernelGGL((fwd_mfma_kernel<T, D, 32, true, 4, 2>), grid, block, 0, stream, p);
+            else
+                hipLaunchKernelGGL((fwd_mfma_kernel<T, D, 32, false, 4, 2>), grid, block, 0, stream, p);
+        }
     } else {
         if (causal)
-            hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, true, 4>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, true, 4, 1>), grid, block, 0, stream, p);
         else
-            hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, false, 4>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, false, 4, 1>), grid, block, 0, stream, p);
     }
     return hipGetLastError();
 }
 
 // bf16 (is_bf16 = true) or f16 inputs, D = 32, 64 or 128; nwaves = 4 or 8
-// waves per workgroup.
-hipError_t launch_fwd_mfma(const FwdParams& p, int D, bool is_bf16, bool causal, int nwaves, hipStream_t stream) {
+// waves per workgroup; rb = 32-row blocks per wave (2 only with four waves
+// and D >= 64).
+hipError_t launch_fwd_mfma(const FwdParams& p, int D, bool is_bf16, bool causal, int nwaves, int rb,
+                           hipStream_t stream) {
     if (is_bf16) {
-        return D == 32 ? launch_typed<__bf16, 32, 64>(p, causal, nwaves, stream)
-             : D == 64 ? launch_typed<__bf16, 64, 64>(p, causal, nwaves, stream)
-                       : launch_typed<__bf16, 128, 64>(p, causal, nwaves, stream);
+        return D == 32 ? launch_typed<__bf16, 32, 64>(p, causal, nwaves, rb, stream)
+             : D == 64 ? launch_typed<__bf16, 64, 64>(p, causal, nwaves, rb, stream)
+                       : launch_typed<__bf16, 128, 64>(p, causal, nwaves, rb, stream);
     }
-    return D == 32 ? launch_typed<_Float16, 32, 64>(p, causal, nwaves, stream)
-         : D == 64 ? launch_typed<_Float16, 64, 64>(p, causal, nwaves, stream)
-                   : launch_typed<_Float16, 128, 64>(p, causal, nwaves, stream);
+    return D == 32 ? launch_typed<_Float16, 32, 64>(p, causal, nwaves, rb, stream)
+         : D == 64 ? launch_typed<_Float16, 64, 64>(p, causal, nwaves, rb, stream)
+                   : launch_typed<_Float16, 128, 64>(p, causal, nwaves, rb, stream);
 }
 
 // E4M3 inputs, bf16 output, D = 64 or 128 (one FP8 score MFMA spans 64 of D).
-hipError_t launch_fwd_fp8(const FwdParams& p, int D, bool causal, int nwaves, hipStream_t stream) {
-    return D == 64 ? launch_typed<fp8_t, 64, 64>(p, causal, nwaves, stream)
-                   : launch_typed<fp8_t, 128, 64>(p, causal, nwaves, stream);
+hipError_t launch_fwd_fp8(const FwdParams& p, int D, bool causal, int nwaves, int rb, hipStream_t stream) {
+    return D == 64 ? launch_typed<fp8_t, 64, 64>(p, causal, nwaves, rb, stream)
+                   : launch_typed<fp8_t, 128, 64>(p, causal, nwaves, rb, stream);
 }
 
 }  // namespace attn
