@@ -38,8 +38,9 @@
 //     so the result is unchanged, and weights up to 256 are harmless in
 //     bf16 / f16.
 //   * Causal: tiles wholly above the workgroup's diagonal are never loaded;
-//     32-key blocks wholly above a wave's diagonal skip their MFMAs; only
-//     blocks crossing the diagonal (or the end of the keys) are masked.
+//     from the first tile wholly above a wave's own rows on, that wave only
+//     copies tiles and keeps the barriers; only 32-key blocks crossing the
+//     diagonal (or the end of the keys) are masked.
 
 #include "mfma_common.h"
 
@@ -357,6 +358,11 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
         return (m_run[r] == -INFINITY) ? 0.f : -m_run[r];
     };
 
+    // Causal bf16 / f16: a wave stops computing after the last tile its own
+    // rows can see (see wave_tiles below). Not for E4M3, whose V copies go
+    // through registers: keeping them in the last-tile iteration would
+    // spill.
+    constexpr bool WAVE_SKIP = CAUSAL && Tr::V_DMA;
     // One pipelined iteration over tile j. With HAS_NEXT (tile j+1 exists):
     //   A: scores of tile j+1 (MFMA) interleaved with the weights of tile j
     //      (exp2(c s - m), packed, summed) — the offset -m of tile j is known;
@@ -377,9 +383,14 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
                          uint8_t* __restrict__ vb_cur, uint8_t* __restrict__ vb_next) {
         constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
         dma_barrier();
-        if constexpr (HAS_NEXT) {
-            if (j + 2 < n_tiles) issue_k(j + 2, kb_cur);
-            issue_v(j + 1, vb_next);
+        // The copies follow the workgroup's tiles, which (with WAVE_SKIP) may
+        // run past this wave's last computed tile. With HAS_NEXT, tile j + 1
+        // exists by construction (j + 1 < wave_tiles <= n_tiles).
+        if constexpr (HAS_NEXT || WAVE_SKIP) {
+            if (HAS_NEXT || j + 1 < n_tiles) {
+                if (j + 2 < n_tiles) issue_k(j + 2, kb_cur);
+                issue_v(j + 1, vb_next);
+            }
         }
         uint32_t pw[RB][NKB][8];
         pv_frag vf[2][NDB];     // V operands of two consecutive PV groups
@@ -504,27 +515,66 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
             neg_m[r] = finish_max(mraw, r);
         }
     }
-    if (wave_idle) {
-        // Same copies and barriers as an iteration, no compute.
-        for (int j = 0; j < n_tiles; ++j) {
+    if constexpr (!WAVE_SKIP) {
+        if (wave_idle) {
+            // Same copies and barriers as an iteration, no compute.
+            for (int j = 0; j < n_tiles; ++j) {
+                dma_barrier();
+                if (j + 1 < n_tiles) {
+                    if (j + 2 < n_tiles) issue_k(j + 2, (j & 1) ? kbuf1 : kbuf0);
+                    issue_v(j + 1, (j & 1) ? vbuf0 : vbuf1);
+                    finish_v((j & 1) ? vbuf0 : vbuf1);
+                }
+            }
+        } else {
+            int j = 0;
+            for (; j + 2 < n_tiles; j += 2) {
+                iteration(std::true_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
+                iteration(std::true_type{}, j + 1, s1, s0, kbuf1, kbuf0, vbuf1, vbuf0);
+            }
+            if (j + 1 < n_tiles) {
+                iteration(std::true_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
+                iteration(std::false_type{}, j + 1, s1, s0, kbuf1, kbuf0, vbuf1, vbuf0);
+            } else {
+                iteration(std::false_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
+            }
+        }
+    } else {
+        // The wave's own rows need tiles 0 .. wave_tiles - 1 only. Its
+        // highest row is that of its last slot (rows grow with the slot's run
+        // index, and the last slot ends a run); rows past Sq count as row
+        // Sq - 1 (their results are never stored). From tile wave_tiles on,
+        // every score of the wave is masked and every weight 0, so the wave
+        // only copies and keeps the barriers, leaving its SIMD to the other
+        // workgroup's wave. This happens where the waves of a workgroup hold
+        // different rows (several row blocks of one head).
+        const int s_last = 32 * RB * (wave + 1) - 1;
+        const int last_row = min(wi.row_base + (s_last / (HS * p.gpack)) * HS + s_last % HS, Sq - 1);
+        const int last_key = last_row + coff;   // from the start of this workgroup's key range
+        const int wave_tiles = __builtin_amdgcn_readfirstlane(last_key < 0 ? 0 : min(n_tiles, last_key / BN + 1));
+        int j = 0;
+        if (!wave_idle) {
+            for (; j + 2 < wave_tiles; j += 2) {
+                iteration(std::true_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
+                iteration(std::true_type{}, j + 1, s1, s0, kbuf1, kbuf0, vbuf1, vbuf0);
+            }
+            if (j + 1 < wave_tiles) {
+                iteration(std::true_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
+                iteration(std::false_type{}, j + 1, s1, s0, kbuf1, kbuf0, vbuf1, vbuf0);
+                j += 2;
+            } else if (j < wave_tiles) {
+                iteration(std::false_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
+                j += 1;
+            }
+        }
+        // Tiles j .. n_tiles - 1: the same copies and barriers, no compute.
+        for (; j < n_tiles; ++j) {
             dma_barrier();
             if (j + 1 < n_tiles) {
                 if (j + 2 < n_tiles) issue_k(j + 2, (j & 1) ? kbuf1 : kbuf0);
                 issue_v(j + 1, (j & 1) ? vbuf0 : vbuf1);
                 finish_v((j & 1) ? vbuf0 : vbuf1);
             }
-        }
-    } else {
-        int j = 0;
-        for (; j + 2 < n_tiles; j += 2) {
-            iteration(std::true_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
-            iteration(std::true_type{}, j + 1, s1, s0, kbuf1, kbuf0, vbuf1, vbuf0);
-        }
-        if (j + 1 < n_tiles) {
-            iteration(std::true_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
-            iteration(std::false_type{}, j + 1, s1, s0, kbuf1, kbuf0, vbuf1, vbuf0);
-        } else {
-            iteration(std::false_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
         }
     }
 
