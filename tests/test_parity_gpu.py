@@ -95,6 +95,38 @@ def test_parity_small(w, kernel):
     assert err <= TOL[w.dtype], err
 
 
+# Causal MHA and G = 2 (one head, or two, per workgroup, several 32-row blocks
+# of a head in one workgroup): the lower waves of a workgroup stop computing
+# after the last key tile their own rows can see and only copy tiles from there;
+# the last workgroup of a ragged Sq has waves without rows. Top-left and
+# bottom-right alignment, with and without split key ranges (whose ranges
+# start past some waves' last visible key).
+WAVE_STOP = [
+    W("bf16", 1, 2, 2, 192, 192, 128, True),              # last workgroup: two waves without rows
+    W("bf16", 2, 2, 2, 385, 385, 64, True),
+    W("f16", 1, 3, 3, 1000, 1000, 128, True),
+    W("bf16", 1, 2, 2, 300, 450, 128, "bottom_right"),
+    W("f16", 1, 4, 2, 250, 250, 64, True),                # G = 2: two row blocks per head
+    W("bf16", 1, 2, 2, 130, 130, 32, True),
+]
+
+
+@pytest.mark.parametrize("n_split", [None, 3])
+@pytest.mark.parametrize("w", WAVE_STOP, ids=lambda w: w.name)
+def test_causal_wave_stop(w, n_split):
+    print(f"case {w.name} n_split {n_split}", flush=True)
+    q, k, v, desc = workload.make_inputs(w)
+    ws = None
+    if n_split is not None:
+        ws = torch.empty(attn.attn_split_workspace(w.B, w.Hq, w.Sq, w.D, n_split), dtype=torch.uint8,
+                         device="cuda:0")
+    got = helpers.out_to_f64(helpers.gpu_run(w, q, k, v, desc, n_split=n_split, workspace=ws))
+    want = helpers.oracle_full(w, q, k, v, desc)
+    err = helpers.max_abs_err(got, want)
+    print(f"  max-abs {err:.3e}", flush=True)
+    assert err <= TOL[w.dtype], err
+
+
 def test_scale_zero_and_negative(kernel):
     w = W("bf16", 1, 4, 2, 130, 130, 128, True)
     q, k, v, desc = workload.make_inputs(w)
