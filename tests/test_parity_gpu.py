@@ -16,6 +16,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from scaled_dot_product_09_amd import attn, workload
 from scaled_dot_product_09_amd.workload import Workload
 from tests import helpers
@@ -220,6 +221,30 @@ def test_parity_full_size_sampled(name):
         g = np.arange(w.Hq) // (w.Hq // w.Hkv)
         v0 = v[:, 0][:, torch.from_numpy(g)]
         assert torch.equal(o[:, 0].cpu(), v0)
+
+
+def test_e4m3_every_value_code_widened_exactly(kernel):
+    """E4M3 V codes are widened to bf16 on their way to LDS. Every E4M3 value
+    is a bf16 value, so causal row 0 (key 0 only, weight exactly 1, V factor 1)
+    must return V[0] decoded bit for bit: here V[0] holds all 254 non-NaN codes
+    (the two NaN codes left out), the oracle's own decoder gives the expected
+    values."""
+    B, H, S, D = 1, 4, 70, 128
+    gen = torch.Generator().manual_seed(11)
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)   # 254 codes
+    v_bits = torch.randint(0, 256, (B, S, H, D), generator=gen, dtype=torch.uint8)
+    v_bits[v_bits.bitwise_and(0x7F) == 0x7F] = 0x38                       # no NaN anywhere (0x38 = 1.0)
+    row0 = np.resize(codes, H * D).reshape(H, D)                          # every code, some twice
+    v_bits[0, 0] = torch.from_numpy(row0)
+    qk_bits = torch.randint(0, 256, (2, B, S, H, D), generator=gen, dtype=torch.uint8)
+    qk_bits[qk_bits.bitwise_and(0x7F) == 0x7F] = 0x38
+    dev = torch.device("cuda:0")
+    q, k, v = (x.view(torch.float8_e4m3fn).to(dev) for x in (qk_bits[0], qk_bits[1], v_bits))
+    o = attn.fwd(q, k, v, causal=True, scale=D ** -0.5, descales=(0.05, 0.05, 1.0))
+    torch.cuda.synchronize()
+    got = helpers.out_to_f64(o[0, 0])
+    want = oracle.e4m3_bits_to_f64(row0)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5]
 
 
 def test_gqa_equals_repeated_mha_bitwise(kernel):
