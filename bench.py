@@ -99,9 +99,17 @@ def cpu_baseline(w, q, k, v, desc, budget_s):
         if elapsed >= budget_s:
             break
     flops = metric_flops(1, done, w.Sq, w.Skv, w.D, w.causal)
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), model)
+    except OSError:
+        pass
+    full = " (the oracle forms the whole matrix: twice the counted causal FLOPs)" if w.causal else ""
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} of {w.B * w.Hq} (batch, query head) pairs of the same workload, full "
-                      f"Sq x Skv each, fp64 numpy, {elapsed:.1f} s; host has {os.cpu_count()} CPUs"}
+                      f"Sq x Skv each{full}, fp64 numpy on {threads} BLAS threads, {elapsed:.1f} s; "
+                      f"host: {os.cpu_count()} CPUs, {model}"}
 
 
 def time_workload(w, steps, warmup, rotate=True, settle_s=SETTLE_S):
