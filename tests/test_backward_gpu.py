@@ -40,7 +40,7 @@ def grad_tol(ref):
     return 2e-2 * max(1.0, float(np.max(np.abs(ref))) if ref.size else 1.0)
 
 
-@pytest.fixture(params=["w4", "w8"])
+@pytest.fixture(params=["w4", "w8", "rb2"])
 def kernel(request, monkeypatch):
     monkeypatch.setenv("ATTN_KERNEL", request.param)
     return request.param
