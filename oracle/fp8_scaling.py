@@ -16,9 +16,12 @@ meaning):
   saturating at the format's largest finite value; and records amax(|x|) of
   this step in history slot (step mod 1024).
 * The update after the step sets amax = max(history) and, when amax is
-  finite and positive, scale = float32(fmax / amax) / 2^margin (margin 0:
-  fmax / amax, one binary32 division) and scale_inv = float32(1 / scale);
-  otherwise both stay. The step counter then advances and the slot the next
+  finite and positive and the quotient s = float32(fmax / amax) / 2^margin
+  (margin 0: fmax / amax, one binary32 division) is finite too, scale = s
+  and scale_inv = float32(1 / scale); otherwise both stay. (The quotient
+  overflows for amax below fmax / FLT_MAX, about 1.3e-36 for E4M3; the
+  codelab's recipe states no rule for it, and keeping the last finite scale
+  keeps scale_inv a usable, non-zero dequantisation factor.) The step counter then advances and the slot the next
   step writes is cleared, so the history always holds the last (up to) 1024
   recorded amaxes.
 
@@ -69,9 +72,11 @@ class DelayedScalingState:
         """New scale from the history's maximum; advance to the next step."""
         amax = np.float32(np.max(self.history))
         if np.isfinite(amax) and amax > 0:
-            s = np.float32(np.float32(FORMAT_MAX[self.fmt]) / amax)
-            s = np.float32(s / np.float32(2.0 ** self.margin))
-            self.scale = s
-            self.scale_inv = np.float32(np.float32(1.0) / s)
+            with np.errstate(over="ignore"):
+                s = np.float32(np.float32(FORMAT_MAX[self.fmt]) / amax)
+                s = np.float32(s / np.float32(2.0 ** self.margin))
+            if np.isfinite(s):
+                self.scale = s
+                self.scale_inv = np.float32(np.float32(1.0) / s)
         self.step += 1
         self.history[self.step % len(self.history)] = np.float32(0.0)

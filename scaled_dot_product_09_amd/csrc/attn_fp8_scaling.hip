@@ -17,8 +17,11 @@
 //     the bit patterns of non-negative floats, whose unsigned order is their
 //     order; NaN patterns sort above infinity, so a NaN propagates).
 //   * fp8_update_kernel: amax = max(history); if finite and positive,
-//     scale = fmax / amax and scale_inv = 1 / scale (binary32, correctly
-//     rounded divisions); step + 1; the next step's slot is cleared.
+//     s = fmax / amax (binary32, correctly rounded), and if s is finite too
+//     (it overflows for amax below fmax / FLT_MAX, about 1.3e-36 for E4M3)
+//     scale = s and scale_inv = 1 / scale; otherwise the scale stays; step
+//     + 1; the next step's slot is cleared. The scale is therefore always
+//     finite and positive, and x * scale is NaN only where x is.
 
 #include <type_traits>
 
@@ -124,16 +127,19 @@ __device__ inline uint32_t quantize_range(const T* __restrict__ x, uint8_t* __re
         load8(x + i * 8, v);
         float y0[4], y1[4];
         uint32_t gb = 0;   // largest |v| pattern of the group
+        bool y_nan = false;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const uint32_t vb = __builtin_bit_cast(uint32_t, v[e]) & 0x7FFFFFFFu;
             gb = vb > gb ? vb : gb;
-            (e < 4 ? y0 : y1)[e % 4] = v[e] * scale;
+            const float y = v[e] * scale;
+            y_nan |= y != y;
+            (e < 4 ? y0 : y1)[e % 4] = y;
         }
         ab = gb > ab ? gb : ab;
-        // NaN codes need fixing only where a NaN is present (rare): a
+        // NaN codes need fixing only where a product is NaN (rare): a
         // wave-uniform test keeps the common path short.
-        const bool nan_here = __builtin_amdgcn_ballot_w64(gb > 0x7F800000u) != 0;
+        const bool nan_here = __builtin_amdgcn_ballot_w64(y_nan) != 0;
         *(u32x2*)(codes + i * 8) = (u32x2){encode4_fp8<FMT>(y0, nan_here), encode4_fp8<FMT>(y1, nan_here)};
     }
     for (int64_t i = n8 * 8 + gid; i < n; i += nthreads) {
@@ -216,8 +222,10 @@ __global__ __launch_bounds__(256) void fp8_update_kernel(Fp8State* states) {
         if (mm > 0u && mm < 0x7F800000u) {
             const float amax = __builtin_bit_cast(float, mm);
             const float s = fmt_max(st->fmt) / amax;
-            st->scale = s;
-            st->scale_inv = 1.0f / s;
+            if (__builtin_bit_cast(uint32_t, s) < 0x7F800000u) {   // finite (s > 0 here)
+                st->scale = s;
+                st->scale_inv = 1.0f / s;
+            }
         }
         const uint32_t next = st->step + 1;
         st->step = next;

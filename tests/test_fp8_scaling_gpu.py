@@ -111,6 +111,26 @@ def test_nan_amax_and_shared_step():
         check_state(st, ref)
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_tiny_amax_keeps_a_finite_scale(fmt):
+    """A step whose amax is 1e-37 (fmax / amax overflows binary32) leaves the
+    scale finite; the next cast, of zeros among other values, gives the
+    oracle's codes (0 for zeros, no NaN codes) and the same state."""
+    ref = oracle.DelayedScalingState(fmt)
+    st = attn.fp8_states(1, FMT[fmt])[0]
+    z = np.zeros(64, np.float32)
+    for x in (np.concatenate([z, [1e-37, -1e-38]]).astype(np.float32),
+              np.concatenate([z, [1e-37, 2.0, -3.5, 0.25]]).astype(np.float32)):
+        want = ref.quantize(x)
+        got = attn.fp8_quantize(torch.from_numpy(x).to(DEV), st, FMT[fmt])
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().view(torch.uint8).numpy(), want)
+        attn.fp8_update(st)
+        ref.update()
+        check_state(st, ref)
+        assert np.isfinite(read_state(st)[0]) and read_state(st)[1] > 0
+
+
 def test_history_window_over_1100_steps():
     rng = np.random.default_rng(12)
     amaxes = np.exp(rng.normal(0, 1.5, 1100)).astype(np.float32)

@@ -74,6 +74,22 @@ def test_zero_inf_nan_amax_keep_the_scale():
                 assert st.scale == s0                      # non-finite maximum: unchanged
 
 
+def test_tiny_amax_keeps_a_finite_scale():
+    """amax = 1e-37: fmax / amax overflows binary32, so the update keeps the
+    last finite scale (here 1) and its non-zero inverse; the next cast of
+    zeros and tiny values gives ordinary codes (0 for zero), no NaN codes."""
+    for fmt, fmax in (("e4m3", 448.0), ("e5m2", 57344.0)):
+        st = oracle.DelayedScalingState(fmt)
+        st.quantize(np.array([1e-37, 0.0, -1e-38], np.float32))
+        st.update()
+        assert np.float32(fmax) / np.float32(1e-37) == np.inf    # the quotient does overflow
+        assert st.scale == np.float32(1.0) and st.scale_inv == np.float32(1.0)
+        codes = st.quantize(np.array([0.0, -0.0, 1e-37, 2.0], np.float32))
+        want = torch.from_numpy(np.array([0.0, -0.0, 1e-37, 2.0], np.float32)).to(
+            torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2).view(torch.uint8).numpy()
+        assert np.array_equal(codes, want), (codes, want)
+
+
 def test_codes_match_torch_casts():
     rng = np.random.default_rng(6)
     x = (rng.standard_normal(20000) * 30).astype(np.float32)
@@ -112,6 +128,16 @@ def _update_current_only(self):
     self.history[self.step % len(self.history)] = 0
 
 
+def _update_any_quotient(self):
+    amax = np.float32(np.max(self.history))
+    if np.isfinite(amax) and amax > 0:
+        with np.errstate(over="ignore", divide="ignore"):
+            self.scale = np.float32(np.float32(fs.FORMAT_MAX[self.fmt]) / amax)
+            self.scale_inv = np.float32(1.0) / self.scale
+    self.step += 1
+    self.history[self.step % len(self.history)] = 0
+
+
 def _quantize_with_amax_first(self, x):
     x = np.asarray(x, dtype=np.float32)
     amax = np.float32(np.max(np.abs(x)))
@@ -122,9 +148,10 @@ def _quantize_with_amax_first(self, x):
 
 PINS = [test_first_step_uses_unit_scale_and_saturates, test_scale_is_fmax_over_history_max_e5m2,
         test_window_is_the_last_1024_amaxes, test_delayed_scale_is_used_by_the_next_step,
-        test_zero_inf_nan_amax_keep_the_scale]
+        test_zero_inf_nan_amax_keep_the_scale, test_tiny_amax_keeps_a_finite_scale]
 MUTANTS = {"mean_not_max": ("update", _update_mean), "slot_never_cleared": ("update", _update_no_clear),
-           "no_history": ("update", _update_current_only), "current_scale": ("quantize", _quantize_with_amax_first)}
+           "no_history": ("update", _update_current_only), "current_scale": ("quantize", _quantize_with_amax_first),
+           "overflowing_scale_adopted": ("update", _update_any_quotient)}
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
