@@ -27,7 +27,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s and % of MFMA peak at S=4096 causal GQA bf16"
-METRIC_BWD = "attention bwd TFLOP/s (2.5x the forward's FLOPs: the five products of the gradients)"
 # MI355X published dense peaks (TFLOP/s) by arithmetic type of the products.
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "f32": 157.3}
 PEAK_KIND = {"bf16": "mfma", "f16": "mfma", "e4m3": "mfma", "f32": "alu"}
@@ -67,6 +66,35 @@ def load_traffic(w):
     if not rec or rec.get("kernel_hash") != kernel_source_hash(w.direction):
         return None
     return rec.get("traffic_bytes")
+
+
+def describe(w):
+    """The workload's shape in words, e.g. "bf16 GQA B=2 Hq=32 Hkv=8 S=4096 D=128 causal"."""
+    kind = "MHA" if w.Hq == w.Hkv else ("MQA" if w.Hkv == 1 else "GQA")
+    heads = f"H={w.Hq}" if w.Hq == w.Hkv else f"Hq={w.Hq} Hkv={w.Hkv}"
+    seq = f"S={w.Sq}" if w.Sq == w.Skv else f"Sq={w.Sq} Skv={w.Skv}"
+    mask = {False: "", True: " causal", "bottom_right": " bottom-right causal"}[w.causal]
+    extra = []
+    if w.layout != "bshd":
+        extra.append(f"{w.layout.upper()} storage, strided entry point")
+    if w.n_split is not None:
+        extra.append("split keys")
+    if w.scaling == "delayed":
+        extra.append("delayed-scaling step: casts + attention + update")
+    tail = f" ({', '.join(extra)})" if extra else ""
+    return f"{w.dtype} {kind} B={w.B} {heads} {seq} D={w.D}{mask}{tail}"
+
+
+def metric_name(w):
+    """The headline workload carries the headline metric; every other line
+    names its own workload."""
+    from scaled_dot_product_09_amd import workload
+    if w.name == workload.HEADLINE:
+        return METRIC
+    if w.direction == "bwd":
+        return (f"attention bwd TFLOP/s (2.5x the forward's FLOPs: the five products of the gradients), "
+                f"{describe(w)}")
+    return f"attention fwd TFLOP/s and % of peak, {describe(w)}"
 
 
 def cpu_baseline(w, q, k, v, desc, budget_s):
@@ -235,7 +263,7 @@ def result_line(w, t, steps, warmup, n_gpus, cpu=None, warm=None):
                 "frac": round(tflops / peak, 4)}
     roof.update({"traffic": load_traffic(w), "algorithmic_bytes": nbytes})
     line = {
-        "metric": METRIC if w.direction == "fwd" else METRIC_BWD, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": n_gpus,
+        "metric": metric_name(w), "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": n_gpus,
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq, "Skv": w.Skv,
@@ -267,6 +295,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--sweep-out", default=None, help="also time every named workload, JSONL to this file")
+    ap.add_argument("--sweep-cpu-budget", type=float, default=3.0,
+                    help="seconds of oracle time for each sweep line's cpu_baseline (0: none)")
     ap.add_argument("--settle-s", type=float, default=SETTLE_S,
                     help="seconds of untimed steps after the warmup steps (clock settle)")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
@@ -304,7 +334,11 @@ def main():
         with open(args.sweep_out, "w") as f:
             for n, wi in workload.WORKLOADS.items():
                 ti = time_workload(wi, args.steps, args.warmup, rotate=True, settle_s=args.settle_s)
-                f.write(json.dumps(result_line(wi, ti, args.steps, args.warmup, 1)) + "\n")
+                ci = None
+                if args.sweep_cpu_budget > 0 and wi.direction == "fwd" and wi.scaling == "amax":
+                    qi, ki, vi, di = ti["inputs"]
+                    ci = cpu_baseline(wi, qi, ki, vi, di, args.sweep_cpu_budget)
+                f.write(json.dumps(result_line(wi, ti, args.steps, args.warmup, 1, cpu=ci)) + "\n")
                 f.flush()
                 print(f"sweep {n}: {ti['ms_per_step']:.4f} ms", file=sys.stderr, flush=True)
 

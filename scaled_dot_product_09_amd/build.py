@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn.so")
-SOURCES = ["attn_api.cpp", "attn_fwd_mfma.hip", "attn_fwd_pp.hip", "attn_fwd_f32.hip", "attn_combine.hip", "attn_bwd.hip", "attn_fp8_scaling.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd_mfma.hip", "attn_fwd_f32.hip", "attn_combine.hip", "attn_bwd.hip", "attn_fp8_scaling.hip"]
 
 # -packed-fp32-ops keeps the compiler from forming packed fp32 VALU ops
 # (v_pk_fma_f32 and friends); every HIP source is built with it.
@@ -40,10 +40,7 @@ def hipcc():
 # that the vector ALU reads in ordinary VGPRs (MFMA "VGPR form"); the default
 # puts them in accumulation registers, and the copies back cost more than
 # the products (measured: +29 % on the head-dim-64 backward). The forward
-# source needs it for its 64-row-per-wave variant (otherwise the output
-# accumulators are copied between the two register files around every PV
-# phase: 689 -> 891 TFLOP/s); its other kernels compile to the same code
-# either way.
+# kernel's score accumulators are read by the vector ALU too.
 SOURCE_FLAGS = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                 "attn_fwd_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 

@@ -7,18 +7,14 @@
 
 #include <math.h>
 #include <stdint.h>
-#include <stdlib.h>
-#include <string.h>
 
 #include "../../include/attn.h"
 #include "kernel_common.h"
 
 namespace attn {
-hipError_t launch_fwd_mfma(const FwdParams& p, int D, bool is_bf16, bool causal, int nwaves, int rb,
-                           hipStream_t stream);
+hipError_t launch_fwd_mfma(const FwdParams& p, int D, bool is_bf16, bool causal, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int D, bool causal, hipStream_t stream);
-hipError_t launch_fwd_fp8(const FwdParams& p, int D, bool causal, int nwaves, int rb, hipStream_t stream);
-hipError_t launch_fwd_pp(const FwdParams& p, int D, int dtype, bool causal, hipStream_t stream);
+hipError_t launch_fwd_fp8(const FwdParams& p, int D, bool causal, hipStream_t stream);
 hipError_t launch_combine(const FwdParams& p, int D, bool is_bf16, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& bp, int D, bool is_bf16, bool causal, hipStream_t stream);
 hipError_t launch_widen_fp8(const void* in, void* out, int64_t n, bool e5m2, hipStream_t stream);
@@ -80,8 +76,8 @@ attn::FwdParams make_params(const void* q, const void* k, const void* v, void* o
     p.G = Hq / Hkv;
     // A workgroup of `waves` waves shares one KV head between gpack query
     // heads and covers rows_per_wave * waves / gpack rows of each. gpack is
-    // the largest of 4, 2, 1 dividing G. The four- and eight-wave kernels
-    // (wide_heads), whose MFMA columns may mix heads, double it while G
+    // the largest of 4, 2, 1 dividing G. The matrix-core kernel
+    // (wide_heads), whose MFMA columns may mix heads, doubles it while G
     // allows and the heads' Sq rows still fit the workgroup's slots
     // (gpack * Sq <= rows_per_wave * waves): with few query rows (decode
     // with GQA / MQA) the slots then hold rows of many heads instead of
@@ -93,7 +89,7 @@ attn::FwdParams make_params(const void* q, const void* k, const void* v, void* o
             p.gpack *= 2;
     }
     p.rows_per_wg = rows_per_wave * waves / p.gpack;
-    // Slot map of the four- and eight-wave kernels: runs of head_stride
+    // Slot map of the matrix-core kernel: runs of head_stride
     // consecutive rows of one head, heads interleaved between runs. 32 (one
     // head per wave, 32 rows) when there are that many rows; with fewer
     // rows, the smallest power of two >= Sq, so the rows of all gpack heads
@@ -132,44 +128,13 @@ const float kLog2e = 1.4426950408889634f;
 // -inf, which lets the kernels mask with a single select.
 float nonzero_multiplier(float c) { return c == 0.0f ? 0x1p-100f : c; }
 
-// Matrix-core kernel choice. Default: "w4", four independent waves per
-// workgroup (32 query rows each) and two workgroups per CU. Also built,
-// selectable with ATTN_KERNEL in the environment (the tests cover every one
-// on every shape): "w8", the same kernel with eight waves per workgroup;
-// "pp", eight waves in two ping-pong groups of four; and "rb2", the
-// four-wave kernel with two 32-row blocks per wave (64 query rows), every
-// K / V operand read from LDS shared by both blocks (half the LDS reads per
-// flop) at one wave per SIMD. All three measure slower on every shape so
-// far: on gfx950 a wave's matrix ops do not overlap another wave's vector
-// ops on the same SIMD, so the ping-pong split gains nothing, and the second
-// wave per SIMD hides more stall time than halving the LDS reads saves.
-enum MfmaKernel { kPingPong, kFourWave, kEightWave, kRows64 };
-
-MfmaKernel mfma_kernel() {
-    const char* e = getenv("ATTN_KERNEL");
-    if (e && strcmp(e, "pp") == 0) return kPingPong;
-    if (e && strcmp(e, "w8") == 0) return kEightWave;
-    if (e && strcmp(e, "rb2") == 0) return kRows64;
-    return kFourWave;
-}
-
 // strides: NULL (dense) or q, k, v, out element strides (batch, seq, head).
 hipError_t launch_mfma(const void* q, const void* k, const void* v, void* out,
                        int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale_log2,
                        float out_mul, int dtype, int causal, const int64_t* strides, hipStream_t stream,
                        float* lse = nullptr, const float* const* dsc = nullptr) {
-    // Head dimension 32, strided layouts, the log-sum-exp output and
-    // device-side FP8 factors exist only in the four- and eight-wave kernel.
-    const bool four_or_eight = D == 32 || strides || lse || dsc;
-    MfmaKernel kern = (four_or_eight && mfma_kernel() == kPingPong) ? kFourWave : mfma_kernel();
-    // Two row blocks per wave: 16-bit inputs with D >= 64 only.
-    if (kern == kRows64 && (D == 32 || dtype == ATTN_FP8_E4M3)) kern = kFourWave;
-    const int rb = kern == kRows64 ? 2 : 1;
-    const int rpw = kern == kRows64 ? 64 : 32;
-    const int waves = (kern == kPingPong || kern == kEightWave) ? 8 : 4;
-    const bool wide = kern != kPingPong;
     attn::FwdParams p = make_params(q, k, v, out, B, Hq, Hkv, Sq, Skv, scale_log2, out_mul,
-                                    causal, true, rpw, waves, wide);
+                                    causal, true, 32, 4, true);
     if (strides) {
         for (int i = 0; i < 3; ++i) {
             p.sq[i] = strides[i]; p.sk[i] = strides[3 + i]; p.sv[i] = strides[6 + i]; p.so[i] = strides[9 + i];
@@ -184,14 +149,8 @@ hipError_t launch_mfma(const void* q, const void* k, const void* v, void* out,
         p.dsc_v = dsc[2];
     }
     const bool masked = causal != 0;
-    switch (kern) {
-        case kFourWave:
-        case kEightWave:
-        case kRows64:
-            return dtype == ATTN_FP8_E4M3 ? attn::launch_fwd_fp8(p, D, masked, waves, rb, stream)
-                                          : attn::launch_fwd_mfma(p, D, dtype == ATTN_BF16, masked, waves, rb, stream);
-        default: return attn::launch_fwd_pp(p, D, dtype, masked, stream);
-    }
+    return dtype == ATTN_FP8_E4M3 ? attn::launch_fwd_fp8(p, D, masked, stream)
+                                  : attn::launch_fwd_mfma(p, D, dtype == ATTN_BF16, masked, stream);
 }
 
 // Workgroups of the four-wave kernel for a shape (the unit of the split
@@ -341,23 +300,35 @@ extern "C" int attn_fwd_split(const void* q, const void* k, const void* v, void*
     if (ranges_overlap(workspace, (int64_t)need, q, nq * 2) || ranges_overlap(workspace, (int64_t)need, k, nk * 2) ||
         ranges_overlap(workspace, (int64_t)need, v, nk * 2) || ranges_overlap(workspace, (int64_t)need, out, nq * 2))
         return ATTN_ERR_WORKSPACE;
-    // The split path always runs the four-wave kernel.
     attn::FwdParams p = make_params(q, k, v, out, B, Hq, Hkv, Sq, Skv, nonzero_multiplier(scale * kLog2e), 1.0f,
                                     causal, true, 32, 4, true);
     set_dense_strides(p, D);
     p.n_split = n_split;
     p.part_o = (float*)workspace;
     p.part_ml = (float*)workspace + (size_t)n_split * B * Sq * Hq * D;
-    hipError_t e = attn::launch_fwd_mfma(p, D, dtype == ATTN_BF16, causal != 0, 4, 1, stream);
+    hipError_t e = attn::launch_fwd_mfma(p, D, dtype == ATTN_BF16, causal != 0, stream);
     if (e == hipSuccess) e = attn::launch_combine(p, D, dtype == ATTN_BF16, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 namespace {
 
-// Largest element offset a (B, S, H, D) view with non-negative strides reaches, plus 1.
+// (n - 1) * stride for n >= 1 and a non-negative stride, or -1 when the
+// product does not fit in int64.
+int64_t span(int64_t stride, int n) {
+    int64_t r;
+    return __builtin_mul_overflow((int64_t)(n - 1), stride, &r) ? -1 : r;
+}
+
+// Largest element offset a (B, S, H, D) view with non-negative strides
+// reaches, plus 1; -1 when it does not fit in int64.
 int64_t extent(const int64_t* st, int B, int S, int H, int D) {
-    return (int64_t)(B - 1) * st[0] + (int64_t)(S - 1) * st[1] + (int64_t)(H - 1) * st[2] + D;
+    const int64_t a = span(st[0], B), b = span(st[1], S), c = span(st[2], H);
+    if (a < 0 || b < 0 || c < 0) return -1;
+    int64_t r;
+    if (__builtin_add_overflow(a, b, &r) || __builtin_add_overflow(r, c, &r) || __builtin_add_overflow(r, (int64_t)D, &r))
+        return -1;
+    return r;
 }
 
 // No two (b, i, h, d) of a view share an element: sorted by stride, every
@@ -370,11 +341,11 @@ bool injective(const int64_t* st, int B, int S, int H, int D) {
             int64_t t = s[b]; s[b] = s[b - 1]; s[b - 1] = t;
             t = n[b]; n[b] = n[b - 1]; n[b - 1] = t;
         }
-    int64_t span = 1;   // elements covered by the faster axes, as a stride unit
+    int64_t covered = 1;   // elements covered by the faster axes, as a stride unit
     for (int a = 0; a < 4; ++a) {
         if (n[a] == 1) continue;
-        if (s[a] < span) return false;
-        span = s[a] * n[a];
+        if (s[a] < covered) return false;
+        if (__builtin_mul_overflow(s[a], n[a], &covered)) return false;
     }
     return true;
 }
@@ -408,13 +379,20 @@ extern "C" int attn_fwd_strided(const void* q, const void* k, const void* v, voi
             if ((st[i] * eb) % 16 != 0) return ATTN_ERR_ALIGN;
         }
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15) return ATTN_ERR_ALIGN;
+    // Every product of a stride and an axis length must fit in int64 (a
+    // stride is at most 2^40, an axis below 2^31: the product can reach
+    // 2^71), and so must each view's extent in bytes.
+    const int64_t xq = extent(q_strides, B, Sq, Hq, D), xk = extent(k_strides, B, Skv, Hkv, D);
+    const int64_t xv = extent(v_strides, B, Skv, Hkv, D), xo = extent(out_strides, B, Sq, Hq, D);
+    const int64_t kmax = ((int64_t)1 << 62) / eb;
+    if (xq < 0 || xk < 0 || xv < 0 || xo < 0 || xq > kmax || xk > kmax || xv > kmax || xo > kmax)
+        return ATTN_ERR_STRIDE;
     if (!injective(out_strides, B, Sq, Hq, D)) return ATTN_ERR_STRIDE;
     // A key tile's byte offsets inside one head must fit in 32 bits.
-    if (((int64_t)(Skv - 1) * k_strides[1] + D) * eb >= ((int64_t)1 << 32) ||
-        ((int64_t)(Skv - 1) * v_strides[1] + D) * eb >= ((int64_t)1 << 32))
+    const int64_t kspan = span(k_strides[1], Skv), vspan = span(v_strides[1], Skv);
+    if ((kspan + D) * eb >= ((int64_t)1 << 32) || (vspan + D) * eb >= ((int64_t)1 << 32))
         return ATTN_ERR_SHAPE;
-    const int64_t eq = extent(q_strides, B, Sq, Hq, D) * eb, ek = extent(k_strides, B, Skv, Hkv, D) * eb;
-    const int64_t ev = extent(v_strides, B, Skv, Hkv, D) * eb, eo = extent(out_strides, B, Sq, Hq, D) * eb;
+    const int64_t eq = xq * eb, ek = xk * eb, ev = xv * eb, eo = xo * eb;
     if (ranges_overlap(out, eo, q, eq) || ranges_overlap(out, eo, k, ek) || ranges_overlap(out, eo, v, ev))
         return ATTN_ERR_ALIAS;
     int64_t strides[12];

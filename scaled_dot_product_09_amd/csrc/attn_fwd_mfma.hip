@@ -238,11 +238,15 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
         for (int db = 0; db < NDB; ++db)
             for (int i = 0; i < 16; ++i) oacc[r][db][i] = 0.f;
     float m_run[RB];    // running max of scale*log2(e)*score (same on both halves)
-    float l_part[RB];   // this lane's share of the running denominator
+    // This lane's share of the running denominator, as NLSUM partial sums
+    // (the row-sum dot products of a tile form NLSUM independent chains
+    // instead of one).
+    constexpr int NLSUM = 4;
+    float l_part[RB][NLSUM];
     float neg_m[RB];    // exponent offset -m_run of the tile being weighted
     for (int r = 0; r < RB; ++r) {
         m_run[r] = -INFINITY;
-        l_part[r] = 0.f;
+        for (int t = 0; t < NLSUM; ++t) l_part[r][t] = 0.f;
         neg_m[r] = 0.f;
     }
 
@@ -355,7 +359,7 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
             const float alpha = __builtin_amdgcn_exp2f(m_run[r] - mnew);   // 0 on the first tile
             for (int db = 0; db < NDB; ++db)
                 for (int i = 0; i < 16; ++i) oacc[r][db][i] *= alpha;
-            l_part[r] *= alpha;
+            for (int t = 0; t < NLSUM; ++t) l_part[r][t] *= alpha;
             m_run[r] = mnew;
         }
         return (m_run[r] == -INFINITY) ? 0.f : -m_run[r];
@@ -427,10 +431,16 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
         // MFMA-only phase B), which keeps both the matrix core and the VALU
         // fed. Measured: +2 % (D=128) and +6 % (D=64) over equal priority.
         __builtin_amdgcn_s_setprio(1);
+        // With BAL, the exponentials of the last PV group's four weight pairs
+        // move from phase A into the first two PV groups of phase B (the last
+        // group is the first to need them), which evens out the vector work
+        // per matrix product between the two phases (measured: E4M3 S=4096
+        // +2 %, head dim 32 +5 %, MQA S=1024 +1.4 %, GQA S=4096 and head dim
+        // 64 within 1 %).
+        constexpr int PAIRS = NKB * 8;
+        constexpr bool BAL = NKB >= 2 && RB == 1;
+        constexpr int PA = BAL ? PAIRS - 4 : PAIRS;   // pairs weighted in phase A
         if constexpr (HAS_NEXT) {
-            constexpr int PAIRS = NKB * 8;
-            constexpr int PER_STEP = PAIRS / KSTEPS;
-            static_assert(PER_STEP * KSTEPS == PAIRS, "weight pairs must split evenly over k-steps");
             for (int r = 0; r < RB; ++r)
                 for (int kb = 0; kb < NKB; ++kb)
                     for (int i = 0; i < 16; ++i) s_nxt[r][kb][i] = 0.f;
@@ -450,17 +460,17 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
                     for (int r = 0; r < RB; ++r) s_nxt[r][kb] = Tr::qk(kf[ks % 3][kb], qf[r][ks], s_nxt[r][kb]);
 #pragma unroll
                 for (int r = 0; r < RB; ++r)
-                    for (int t = 0; t < PER_STEP; ++t) weight_exp(r, ks * PER_STEP + t);
+                    for (int pp = ks * PA / KSTEPS; pp < (ks + 1) * PA / KSTEPS; ++pp) weight_exp(r, pp);
                 if (ks > 0) {
 #pragma unroll
                     for (int r = 0; r < RB; ++r)
-                        for (int t = 0; t < PER_STEP; ++t) weight_pack(r, (ks - 1) * PER_STEP + t);
+                        for (int pp = (ks - 1) * PA / KSTEPS; pp < ks * PA / KSTEPS; ++pp) weight_pack(r, pp);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int r = 0; r < RB; ++r)
-                for (int t = 0; t < PER_STEP; ++t) weight_pack(r, (KSTEPS - 1) * PER_STEP + t);
+                for (int pp = (KSTEPS - 1) * PA / KSTEPS; pp < PA; ++pp) weight_pack(r, pp);
             // ---- A' ------------------------------------------------------------
             for (int r = 0; r < RB; ++r) mask_tile(s_nxt[r], j + 1, r);
         } else {
@@ -487,13 +497,35 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
                                                                        pw[r][kb][4 * s2 + 2], pw[r][kb][4 * s2 + 3]});
                 for (int db = 0; db < NDB; ++db) oacc[r][db] = Tr::pv(vf[g & 1][db], pf, oacc[r][db]);
             }
+            if constexpr (BAL && HAS_NEXT) {
+                if (g < 2)
+                    for (int r = 0; r < RB; ++r)
+                        for (int pp = PA + 2 * g; pp < PA + 2 * g + 2; ++pp) weight_exp(r, pp);
+                if (g == 1 || g == 2)
+                    for (int r = 0; r < RB; ++r)
+                        for (int pp = PA + 2 * (g - 1); pp < PA + 2 * g; ++pp) weight_pack(r, pp);
+            }
             // Row sum over this group's rounded weights (left unpinned, so the
             // compiler places the dot products in the gaps between the MFMAs).
             for (int r = 0; r < RB; ++r)
-                for (int t = 0; t < 4; ++t) l_part[r] = Tr::sum2(pw[r][kb][4 * s2 + t], l_part[r]);
-            if constexpr (HAS_NEXT)
-                for (int r = 0; r < RB; ++r)
-                    mraw[r] = max_piece(s_nxt[r], g, mraw[r], std::integral_constant<int, NKB * 2>{});
+                for (int t = 0; t < 4; ++t)
+                    l_part[r][t % NLSUM] = Tr::sum2(pw[r][kb][4 * s2 + t], l_part[r][t % NLSUM]);
+            if constexpr (HAS_NEXT) {
+                constexpr auto np = std::integral_constant<int, NKB * 2>{};
+                for (int r = 0; r < RB; ++r) {
+                    if (BAL) {
+                        // The row max of tile j + 1 goes to the last two
+                        // groups (the first two carry the moved exponentials).
+                        if (g >= NKB * 2 - 2) {
+                            const int p0 = (g - (NKB * 2 - 2)) * NKB;
+                            for (int pc = p0; pc < p0 + NKB; ++pc)
+                                mraw[r] = max_piece(s_nxt[r], pc, mraw[r], np);
+                        }
+                    } else {
+                        mraw[r] = max_piece(s_nxt[r], g, mraw[r], np);
+                    }
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
         // ---- C -----------------------------------------------------------------
@@ -583,7 +615,9 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
 
     // ---- epilogue: O = O^T / l, round once, store [b][row][hq][d] ----------
     for (int rb = 0; rb < RB; ++rb) {
-        const float l = xor32_sum(l_part[rb]);
+        float lsum = l_part[rb][0];
+        for (int t = 1; t < NLSUM; ++t) lsum += l_part[rb][t];
+        const float l = xor32_sum(lsum);
         const int row = qrow[rb];
         if (p.n_split > 1) {
             // Partial result of this key range: O and l relative to 2^m_run.
@@ -617,53 +651,33 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
     }
 }
 
-// nwaves = 8: eight waves of 32 rows; nwaves = 4: four waves of 32 rows
-// (rb = 1) or of 64 rows (rb = 2: 16-bit inputs, head dims 64 and 128, with
-// 32-key tiles so that both blocks' double-buffered scores fit the vector
-// registers; other cases run rb = 1).
 template <typename T, int D, int BN>
-static hipError_t launch_typed(const FwdParams& p, bool causal, int nwaves, int rb, hipStream_t stream) {
-    const dim3 grid(p.n_units * p.n_row_blocks * p.n_split), block(64 * nwaves);
-    if (nwaves == 8) {
-        if (causal)
-            hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, true, 8, 1>), grid, block, 0, stream, p);
-        else
-            hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, false, 8, 1>), grid, block, 0, stream, p);
-    } else if (rb == 2 && D >= 64 && sizeof(T) == 2) {
-        if constexpr (D >= 64 && sizeof(T) == 2) {
-            if (causal)
-                hipLaunchKernelGGL((fwd_mfma_kernel<T, D, 32, true, 4, 2>), grid, block, 0, stream, p);
-            else
-                hipLaunchKernelGGL((fwd_mfma_kernel<T, D, 32, false, 4, 2>), grid, block, 0, stream, p);
-        }
-    } else {
-        if (causal)
-            hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, true, 4, 1>), grid, block, 0, stream, p);
-        else
-            hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, false, 4, 1>), grid, block, 0, stream, p);
-    }
+static hipError_t launch_typed(const FwdParams& p, bool causal, hipStream_t stream) {
+    const dim3 grid(p.n_units * p.n_row_blocks * p.n_split), block(64 * 4);
+    if (causal)
+        hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, true, 4, 1>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, false, 4, 1>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 
-// bf16 (is_bf16 = true) or f16 inputs, D = 32, 64 or 128; nwaves = 4 or 8
-// waves per workgroup; rb = 32-row blocks per wave (2 only with four waves
-// and D >= 64).
-hipError_t launch_fwd_mfma(const FwdParams& p, int D, bool is_bf16, bool causal, int nwaves, int rb,
-                           hipStream_t stream) {
+// bf16 (is_bf16 = true) or f16 inputs, D = 32, 64 or 128.
+hipError_t launch_fwd_mfma(const FwdParams& p, int D, bool is_bf16, bool causal, hipStream_t stream) {
     if (is_bf16) {
-        return D == 32 ? launch_typed<__bf16, 32, 64>(p, causal, nwaves, rb, stream)
-             : D == 64 ? launch_typed<__bf16, 64, 64>(p, causal, nwaves, rb, stream)
-                       : launch_typed<__bf16, 128, 64>(p, causal, nwaves, rb, stream);
+        return D == 32 ? launch_typed<__bf16, 32, 64>(p, causal, stream)
+             : D == 64 ? launch_typed<__bf16, 64, 64>(p, causal, stream)
+                       : launch_typed<__bf16, 128, 64>(p, causal, stream);
     }
-    return D == 32 ? launch_typed<_Float16, 32, 64>(p, causal, nwaves, rb, stream)
-         : D == 64 ? launch_typed<_Float16, 64, 64>(p, causal, nwaves, rb, stream)
-                   : launch_typed<_Float16, 128, 64>(p, causal, nwaves, rb, stream);
+    return D == 32 ? launch_typed<_Float16, 32, 64>(p, causal, stream)
+         : D == 64 ? launch_typed<_Float16, 64, 64>(p, causal, stream)
+                   : launch_typed<_Float16, 128, 64>(p, causal, stream);
 }
 
 // E4M3 inputs, bf16 output, D = 64 or 128 (one FP8 score MFMA spans 64 of D).
-hipError_t launch_fwd_fp8(const FwdParams& p, int D, bool causal, int nwaves, int rb, hipStream_t stream) {
-    return D == 64 ? launch_typed<fp8_t, 64, 64>(p, causal, nwaves, rb, stream)
-                   : launch_typed<fp8_t, 128, 64>(p, causal, nwaves, rb, stream);
+hipError_t launch_fwd_fp8(const FwdParams& p, int D, bool causal, hipStream_t stream) {
+    return D == 64 ? launch_typed<fp8_t, 64, 64>(p, causal, stream)
+                   : launch_typed<fp8_t, 128, 64>(p, causal, stream);
 }
 
 }  // namespace attn
+

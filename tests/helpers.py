@@ -82,5 +82,44 @@ def oracle_rows(w, q, k, v, desc, rows, *, scale=None, causal=None):
     return np.stack(res)
 
 
+def oracle_sdpa_threaded(qf, kf, vf, *, scale, causal, workers=16):
+    """``oracle.sdpa`` on float64 (B, S, H, D) arrays, one (batch, query
+    head) at a time in a pool of ``workers`` threads (numpy's matrix products
+    and element-wise passes release the GIL; BLAS itself is held to one
+    thread per task). Each task is a plain ``oracle.sdpa`` call on one query
+    head and its KV head, so the result is the oracle's own, element for
+    element."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    B, Sq, Hq, D = qf.shape
+    Hkv = kf.shape[2]
+    out = np.empty((B, Sq, Hq, vf.shape[3]), dtype=np.float64)
+
+    def task(bh):
+        b, hq = bh
+        g = oracle.kv_head_of(hq, Hq, Hkv)
+        out[b:b + 1, :, hq:hq + 1] = oracle.sdpa(qf[b:b + 1, :, hq:hq + 1], kf[b:b + 1, :, g:g + 1],
+                                                 vf[b:b + 1, :, g:g + 1], scale=scale, causal=causal)
+
+    with threadpool_limits(1):
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(task, [(b, h) for b in range(B) for h in range(Hq)]))
+    return out
+
+
+def oracle_full_threaded(w, q, k, v, desc, *, workers=16):
+    """The oracle over the whole output of a workload's input codes (decoded
+    by the oracle's codecs), computed by :func:`oracle_sdpa_threaded`."""
+    qf, kf, vf = to_f64(q, w.dtype, desc[0]), to_f64(k, w.dtype, desc[1]), to_f64(v, w.dtype, desc[2])
+    return oracle_sdpa_threaded(qf, kf, vf, scale=w.scale, causal=w.causal, workers=workers)
+
+
+def where_max_err(got, want):
+    """(max-abs error, its (b, i, h, d) index, exact value there)."""
+    d = np.abs(got - want)
+    idx = np.unravel_index(int(np.argmax(d)), d.shape)
+    return float(d[idx]), tuple(int(i) for i in idx), float(want[idx])
+
+
 def max_abs_err(got, want):
     return float(np.max(np.abs(got - want))) if got.size else 0.0

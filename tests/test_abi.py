@@ -244,6 +244,9 @@ def call_strided(q=Q, k=K, v=V, o=O, B=2, Hq=8, Hkv=2, Sq=64, Skv=64, D=128, qs=
     (dict(os_=(8192, 1024, 0)), -13), (dict(os_=(8192, 64, 128)), -13),   # heads or rows collide
     (dict(o=Q + 1024), -7), (dict(o=K), -7),
     (dict(Skv=1 << 20, ks=(0, 1 << 14, 128)), -2),                        # one head spans >= 4 GiB
+    (dict(Skv=(1 << 24) + 1, ks=(0, 1 << 40, 128)), -13),                 # (Skv - 1) * stride = 2^64
+    (dict(Sq=(1 << 24) + 1, os_=(0, 1 << 40, 128)), -13),
+    (dict(B=1 << 24, vs=(1 << 40, 256, 128)), -13),                        # (B - 1) * stride > 2^63
 ])
 def test_strided_rejected_before_launch(kw, status):
     assert call_strided(**kw) == status

@@ -8,12 +8,23 @@ a training step would.
 
 Bounds. lse: 1e-5 for float32 inputs; 2e-2 for bf16 / f16 (the forward sums
 weights rounded to the input type: relative error of the row sum below
-2^-8, so |d lse| < 4e-3). Gradients (bf16 / f16): max-abs error at most
-2e-2 * max(1, max |exact|) per tensor: P and dS enter the products rounded
-to the input type (relative 2^-9 each), Delta uses the rounded forward
-output, and each gradient is rounded once (relative 2^-9); 2e-2 is the
-forward's bf16 bound, taken relative to the tensor's own scale where that
-exceeds 1.
+2^-8, so |d lse| < 4e-3). Gradients (bf16 / f16), per tensor: max-abs error
+at most 2^-7 max |exact| + 2^-9, plus, for dq, the error it inherits from
+Delta (below). Rounding model: each gradient element is rounded once to the
+output type (at most 2^-9 of its size), and the weights P and the score
+gradients dS enter the products rounded to the input type (2^-9 relative
+each), errors that grow with the gradient's own scale and, summed over many
+keys or rows with mixed signs, stay within a small multiple of that rounding
+at the largest element (measured: 1.6 to 1.8 times 2^-9 of max |exact| on
+dq, dk and dv); 2^-7 = 4 times 2^-9 leaves about twice the measured error
+as headroom, and 2^-9 is an absolute floor for tensors whose exact values
+are all tiny. Delta_i = rowsum(dO_i * O_i) is formed from the forward's
+output rounded to the input type, an error of about 2^-9 sqrt(sum_d
+(dO_id O_id)^2) (independent roundings of the D terms; three times that is
+taken), and dq_i = scale sum_j P_ij (dP_ij - Delta_i) k_j carries it times
+scale (P K)_i, the weighted mean of the keys: small for zero-mean keys,
+large when the keys share an offset (the drifting-keys stress input). The
+oracle gives O and P K (attention with the keys as values) exactly.
 """
 
 import numpy as np
@@ -37,13 +48,7 @@ def W(dtype, B, Hq, Hkv, Sq, Skv, D, causal, seed=5):
 
 
 def grad_tol(ref):
-    return 2e-2 * max(1.0, float(np.max(np.abs(ref))) if ref.size else 1.0)
-
-
-@pytest.fixture(params=["w4", "w8", "rb2"])
-def kernel(request, monkeypatch):
-    monkeypatch.setenv("ATTN_KERNEL", request.param)
-    return request.param
+    return 2.0 ** -7 * (float(np.max(np.abs(ref))) if ref.size else 0.0) + 2.0 ** -9
 
 
 LSE_CASES = [
@@ -61,8 +66,8 @@ LSE_CASES = [
 
 
 @pytest.mark.parametrize("w", LSE_CASES, ids=lambda w: w.name)
-def test_lse_parity(w, kernel):
-    print(f"case {w.name} kernel {kernel}", flush=True)
+def test_lse_parity(w):
+    print(f"case {w.name}", flush=True)
     q, k, v, desc = workload.make_inputs(w)
     dev = torch.device("cuda:0")
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
@@ -88,12 +93,25 @@ def run_backward(w, q, k, v, g, *, scale=None):
     return dq, dk, dv
 
 
-def check_grads(w, got, want):
+def delta_term(f64_inputs, scale, causal):
+    """The bound on dq's error inherited from Delta (see the module
+    docstring): max over rows of scale * 3 * 2^-9 * sqrt(sum_d (dO O)^2)
+    * max_d |(P K)_id|, from the oracle's exact O and P K."""
+    qf, kf, vf, gf = f64_inputs
+    o = helpers.oracle_sdpa_threaded(qf, kf, vf, scale=scale, causal=causal)
+    pk = helpers.oracle_sdpa_threaded(qf, kf, kf, scale=scale, causal=causal)
+    e = 3 * 2.0 ** -9 * np.sqrt(np.sum((gf * o) ** 2, axis=-1))
+    return float(np.max(abs(scale) * e * np.max(np.abs(pk), axis=-1))) if e.size else 0.0
+
+
+def check_grads(w, got, want, f64_inputs, scale=None):
+    scale = w.scale if scale is None else scale
+    extra = {"dq": delta_term(f64_inputs, scale, w.causal), "dk": 0.0, "dv": 0.0}
     for name, a, b in zip(("dq", "dk", "dv"), got, want):
         a = helpers.out_to_f64(a)
-        err, tol = helpers.max_abs_err(a, b), grad_tol(b)
-        print(f"  {name} max-abs {err:.3e} (max |exact| {np.max(np.abs(b)) if b.size else 0:.3f}, bound {tol:.3e})",
-              flush=True)
+        err, tol = helpers.max_abs_err(a, b), grad_tol(b) + extra[name]
+        print(f"  {name} max-abs {err:.3e} (max |exact| {np.max(np.abs(b)) if b.size else 0:.3f}, bound {tol:.3e}"
+              f"{f', Delta term {extra[name]:.3e}' if extra[name] else ''})", flush=True)
         assert err <= tol, (name, err, tol)
 
 
@@ -121,9 +139,9 @@ def test_backward_parity(w):
     q, k, v, _ = workload.make_inputs(w)
     g = workload.make_dout(w)
     got = run_backward(w, q, k, v, g)
-    want = oracle.sdpa_backward(*(helpers.to_f64(x, w.dtype) for x in (q, k, v, g)), scale=w.scale,
-                                causal=w.causal)
-    check_grads(w, got, want)
+    f64 = tuple(helpers.to_f64(x, w.dtype) for x in (q, k, v, g))
+    want = oracle.sdpa_backward(*f64, scale=w.scale, causal=w.causal)
+    check_grads(w, got, want, f64)
 
 
 @pytest.mark.parametrize("dtype,D,causal", [("bf16", 128, True), ("f16", 64, False), ("bf16", 64, "bottom_right")])
@@ -149,9 +167,9 @@ def test_backward_growing_row_maxima(dtype, D, causal):
     q, k, v = (torch.from_numpy(x.astype(np.float32)).to(td) for x in (qn, kn, vn))
     g = workload.make_dout(w)
     got = run_backward(w, q, k, v, g)
-    want = oracle.sdpa_backward(*(helpers.to_f64(x, w.dtype) for x in (q, k, v, g)), scale=w.scale,
-                                causal=w.causal)
-    check_grads(w, got, want)
+    f64 = tuple(helpers.to_f64(x, w.dtype) for x in (q, k, v, g))
+    want = oracle.sdpa_backward(*f64, scale=w.scale, causal=w.causal)
+    check_grads(w, got, want, f64)
 
 
 FP8_CASES = [
@@ -175,10 +193,10 @@ def test_backward_fp8_parity(w):
     out, lse = attn.fwd_lse(qd, kd, vd, causal=w.causal, scale=w.scale, descales=desc)
     got = attn.bwd(qd, kd, vd, out, gd, lse, causal=w.causal, scale=w.scale, descales=(*desc, gdesc))
     torch.cuda.synchronize()
-    want = oracle.sdpa_backward(helpers.to_f64(q, "e4m3", desc[0]), helpers.to_f64(k, "e4m3", desc[1]),
-                                helpers.to_f64(v, "e4m3", desc[2]), helpers.to_f64(g, "e5m2", gdesc),
-                                scale=w.scale, causal=w.causal)
-    check_grads(w, got, want)
+    f64 = (helpers.to_f64(q, "e4m3", desc[0]), helpers.to_f64(k, "e4m3", desc[1]),
+           helpers.to_f64(v, "e4m3", desc[2]), helpers.to_f64(g, "e5m2", gdesc))
+    want = oracle.sdpa_backward(*f64, scale=w.scale, causal=w.causal)
+    check_grads(w, got, want, f64)
 
 
 def test_backward_negative_and_zero_scale():
@@ -188,9 +206,9 @@ def test_backward_negative_and_zero_scale():
     for scale in (-0.2, 0.0):
         print(f"scale {scale}", flush=True)
         got = run_backward(w, q, k, v, g, scale=scale)
-        want = oracle.sdpa_backward(*(helpers.to_f64(x, w.dtype) for x in (q, k, v, g)), scale=scale,
-                                    causal=w.causal)
-        check_grads(w, got, want)
+        f64 = tuple(helpers.to_f64(x, w.dtype) for x in (q, k, v, g))
+        want = oracle.sdpa_backward(*f64, scale=scale, causal=w.causal)
+        check_grads(w, got, want, f64, scale=scale)
 
 
 def test_backward_no_query_rows_zeroes_dk_dv():
@@ -217,25 +235,36 @@ def test_backward_is_deterministic():
 
 
 def test_backward_full_size_headline():
-    """Causal GQA, B=2, Hq=32, Hkv=8, S=4096, D=128, bf16: every gradient of
-    one (batch, KV head) group against the oracle (its four query heads
-    and the shared K/V head), and two sums that hold exactly for every
-    group: the key gradients of a KV head sum to zero over the keys, and its
-    value gradients sum to the group's dout summed over the rows."""
+    """Causal GQA, B=2, Hq=32, Hkv=8, S=4096, D=128, bf16: every gradient
+    element of all 16 (batch, KV head) groups (each group's four query heads
+    and its shared K/V head) against the oracle, computed group by group in a
+    thread pool; and two sums that hold exactly for every group: the key
+    gradients of a KV head sum to zero over the keys, and its value gradients
+    sum to the group's dout summed over the rows."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
     w = workload.WORKLOADS["bf16_gqa_b2_hq32_hkv8_s4096_d128_causal_bwd"]
     print(f"case {w.name}", flush=True)
     q, k, v, _ = workload.make_inputs(w)
     g = workload.make_dout(w)
     dq, dk, dv = run_backward(w, q, k, v, g)
     G = w.Hq // w.Hkv
-    b, hkv = 1, 5
-    hs = slice(hkv * G, (hkv + 1) * G)
-    want = oracle.sdpa_backward(helpers.to_f64(q[b:b + 1, :, hs], "bf16"),
-                                helpers.to_f64(k[b:b + 1, :, hkv:hkv + 1], "bf16"),
-                                helpers.to_f64(v[b:b + 1, :, hkv:hkv + 1], "bf16"),
-                                helpers.to_f64(g[b:b + 1, :, hs], "bf16"), scale=w.scale, causal=True)
-    got = (dq[b:b + 1, :, hs], dk[b:b + 1, :, hkv:hkv + 1], dv[b:b + 1, :, hkv:hkv + 1])
-    check_grads(w, got, want)
+    qf, kf, vf, gf = (helpers.to_f64(x, "bf16") for x in (q, k, v, g))
+    want = [np.empty(qf.shape), np.empty(kf.shape), np.empty(vf.shape)]
+
+    def group(bg):
+        b, hkv = bg
+        hs = slice(hkv * G, (hkv + 1) * G)
+        r = oracle.sdpa_backward(qf[b:b + 1, :, hs], kf[b:b + 1, :, hkv:hkv + 1], vf[b:b + 1, :, hkv:hkv + 1],
+                                 gf[b:b + 1, :, hs], scale=w.scale, causal=True)
+        want[0][b:b + 1, :, hs] = r[0]
+        want[1][b:b + 1, :, hkv:hkv + 1] = r[1]
+        want[2][b:b + 1, :, hkv:hkv + 1] = r[2]
+
+    with threadpool_limits(1):
+        with ThreadPoolExecutor(max_workers=16) as ex:
+            list(ex.map(group, [(b, h) for b in range(w.B) for h in range(w.Hkv)]))
+    check_grads(w, (dq, dk, dv), want, (qf, kf, vf, gf))
     # Sums over keys (float64 of the rounded gradients) for every (batch, KV head).
     dk64 = dk.double().sum(dim=1).cpu().numpy()
     dv64 = dv.double().sum(dim=1).cpu().numpy()

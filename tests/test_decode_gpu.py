@@ -30,13 +30,6 @@ def W(dtype, B, Hq, Hkv, Sq, Skv, D, causal, seed=11):
                     causal, seed)
 
 
-@pytest.fixture(params=["w4", "w8", "pp", "rb2"])
-def kernel(request, monkeypatch):
-    """Every matrix-core kernel applies the bottom-right mask."""
-    monkeypatch.setenv("ATTN_KERNEL", request.param)
-    return request.param
-
-
 BOTTOM_RIGHT = [
     W("bf16", 2, 8, 2, 1, 1000, 128, "bottom_right"),
     W("bf16", 1, 4, 4, 7, 300, 64, "bottom_right"),
@@ -50,8 +43,8 @@ BOTTOM_RIGHT = [
 
 
 @pytest.mark.parametrize("w", BOTTOM_RIGHT, ids=lambda w: w.name)
-def test_bottom_right_parity(w, kernel):
-    print(f"case {w.name} kernel {kernel}", flush=True)
+def test_bottom_right_parity(w):
+    print(f"case {w.name}", flush=True)
     q, k, v, desc = workload.make_inputs(w)
     got = helpers.out_to_f64(helpers.gpu_run(w, q, k, v, desc))
     want = helpers.oracle_full(w, q, k, v, desc)

@@ -42,17 +42,9 @@ def _check(dtype, q, k, v, out, causal, scale=None):
     return o
 
 
-@pytest.fixture(params=["w4", "rb2"])
-def kernel(request, monkeypatch):
-    """The default four-wave kernel, or two 32-row blocks per wave (bf16 / f16
-    with D >= 64; other calls run the default)."""
-    monkeypatch.setenv("ATTN_KERNEL", request.param)
-    return request.param
-
-
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("D", [32, 64, 128])
-def test_bhsd_storage(dtype, D, kernel):
+def test_bhsd_storage(dtype, D):
     """(B, H, S, D) tensors handed over as their (B, S, H, D) transposes."""
     B, Hq, Hkv, S = 2, 8, 2, 300
     dev = "cuda:0"
@@ -65,7 +57,7 @@ def test_bhsd_storage(dtype, D, kernel):
     assert o.data_ptr() == out.data_ptr()
 
 
-def test_packed_qkv_and_padding(kernel):
+def test_packed_qkv_and_padding():
     """Slices of one (B, S, Hq + 2 Hkv, D) buffer, and rows padded to D + 8."""
     B, S, Hq, Hkv, D = 2, 257, 8, 2, 128
     dev = "cuda:0"
@@ -76,7 +68,7 @@ def test_packed_qkv_and_padding(kernel):
     _check("bf16", pad[..., :D], k, v, None, False)
 
 
-def test_kv_broadcast_over_batch(kernel):
+def test_kv_broadcast_over_batch():
     """One K/V sequence shared by every batch entry (batch stride 0), bottom-right causal."""
     B, Sq, Skv, Hq, Hkv, D = 4, 17, 600, 8, 2, 64
     dev = "cuda:0"
@@ -88,7 +80,7 @@ def test_kv_broadcast_over_batch(kernel):
     _check("bf16", q, k, v, None, "bottom_right")
 
 
-def test_strided_matches_dense_bitwise(kernel):
+def test_strided_matches_dense_bitwise():
     """A transposed view gives exactly the result of the same values stored densely."""
     B, Hq, Hkv, S, D = 1, 4, 4, 200, 128
     dev = "cuda:0"

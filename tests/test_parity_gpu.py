@@ -74,19 +74,9 @@ SMALL = [
 ]
 
 
-@pytest.fixture(params=["w4", "w8", "pp", "rb2"])
-def kernel(request, monkeypatch):
-    """Force one of the matrix-core kernels: "w4" (four independent waves,
-    two workgroups per CU, the default), "w8" (eight independent waves, one
-    workgroup per CU), "pp" (eight waves in two ping-pong groups) or "rb2"
-    (64 query rows per wave)."""
-    monkeypatch.setenv("ATTN_KERNEL", request.param)
-    return request.param
-
-
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
-def test_parity_small(w, kernel):
-    print(f"case {w.name} kernel {kernel}", flush=True)
+def test_parity_small(w):
+    print(f"case {w.name}", flush=True)
     q, k, v, desc = workload.make_inputs(w)
     got = helpers.out_to_f64(helpers.gpu_run(w, q, k, v, desc))
     want = helpers.oracle_full(w, q, k, v, desc)
@@ -128,7 +118,7 @@ def test_causal_wave_stop(w, n_split):
     assert err <= TOL[w.dtype], err
 
 
-def test_scale_zero_and_negative(kernel):
+def test_scale_zero_and_negative():
     w = W("bf16", 1, 4, 2, 130, 130, 128, True)
     q, k, v, desc = workload.make_inputs(w)
     for scale in (0.0, -0.2):
@@ -139,14 +129,14 @@ def test_scale_zero_and_negative(kernel):
 
 @pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("f16", 128), ("f32", 64)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_growing_row_maxima(kernel, dtype, D, causal):
+def test_growing_row_maxima(dtype, D, causal):
     """Keys drift along the sequence so that every row's scores rise by about
     15 in exp2 terms per 64-key tile, to about 2^160 at the last key: the
     running maximum (and with it the rescale of the partial output and
     denominator) moves many times per row, and weights taken without the
     running offset would overflow float32."""
     w = W(dtype, 1, 4, 2, 700, 700, D, causal, seed=31)
-    print(f"case {w.name} kernel {kernel}", flush=True)
+    print(f"case {w.name}", flush=True)
     rng = np.random.default_rng(31)
     slope = 0.324 / np.sqrt(D)            # 0.5 sqrt(D) slope log2(e) = 0.234 per key
     qn = 0.5 + 0.5 * rng.standard_normal((1, 700, 4, D))
@@ -204,6 +194,23 @@ FULL = [n for n, w in workload.WORKLOADS.items()
 
 
 @pytest.mark.parametrize("name", FULL)
+def test_parity_full_output(name):
+    """Every element of a named workload's output at its full size, in the
+    launch configuration the benchmark times, against the fp64 oracle."""
+    w = workload.WORKLOADS[name]
+    print(f"case {name} (full size, whole output)", flush=True)
+    q, k, v, desc = workload.make_inputs(w)
+    o = helpers.gpu_run(w, q, k, v, desc, n_split=w.n_split)
+    got = helpers.out_to_f64(o)
+    want = helpers.oracle_full_threaded(w, q, k, v, desc)
+    err, at, exact = helpers.where_max_err(got, want)
+    print(f"  FULL {name}: {got.size} elements, max-abs {err:.3e} at (b, i, h, d) = {at}, exact {exact:+.4f}",
+          flush=True)
+    assert np.all(np.isfinite(got))
+    assert err <= TOL[w.dtype], err
+
+
+@pytest.mark.parametrize("name", FULL)
 def test_parity_full_size_sampled(name):
     w = workload.WORKLOADS[name]
     print(f"case {name} (full size, sampled rows)", flush=True)
@@ -223,7 +230,7 @@ def test_parity_full_size_sampled(name):
         assert torch.equal(o[:, 0].cpu(), v0)
 
 
-def test_e4m3_every_value_code_widened_exactly(kernel):
+def test_e4m3_every_value_code_widened_exactly():
     """E4M3 V codes are widened to bf16 on their way to LDS. Every E4M3 value
     is a bf16 value, so causal row 0 (key 0 only, weight exactly 1, V factor 1)
     must return V[0] decoded bit for bit: here V[0] holds all 254 non-NaN codes
@@ -247,7 +254,7 @@ def test_e4m3_every_value_code_widened_exactly(kernel):
     assert np.array_equal(got, want), np.argwhere(got != want)[:5]
 
 
-def test_gqa_equals_repeated_mha_bitwise(kernel):
+def test_gqa_equals_repeated_mha_bitwise():
     w = W("bf16", 2, 8, 2, 260, 260, 128, True)
     q, k, v, desc = workload.make_inputs(w)
     a = helpers.gpu_run(w, q, k, v, desc)
@@ -256,7 +263,7 @@ def test_gqa_equals_repeated_mha_bitwise(kernel):
     assert torch.equal(a, b)
 
 
-def test_deterministic_and_canaries(kernel):
+def test_deterministic_and_canaries():
     w = workload.WORKLOADS["bf16_gqa_b2_hq32_hkv8_s4096_d128_causal"]
     q, k, v, desc = workload.make_inputs(w, shapes=[(1, 700, 8, 128), (1, 700, 2, 128), (1, 700, 2, 128)])
     n, pad = q.numel(), 4096
@@ -270,7 +277,7 @@ def test_deterministic_and_canaries(kernel):
     assert not torch.isnan(out).any()
 
 
-def test_constant_v_gives_constant_output(kernel):
+def test_constant_v_gives_constant_output():
     w = W("bf16", 1, 4, 2, 200, 200, 128, True)
     q, k, _, desc = workload.make_inputs(w)
     row = torch.randn(128, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
