@@ -90,8 +90,10 @@ enum attn_status {
     ATTN_ERR_SPLIT = -11,     /* n_split outside 1 .. ATTN_MAX_SPLIT            */
     ATTN_ERR_WORKSPACE = -12, /* workspace NULL, misaligned, too small, or
                                  overlapping an input or an output              */
-    ATTN_ERR_STRIDE = -13     /* a stride is negative or above 2^40, or out's
+    ATTN_ERR_STRIDE = -13,    /* a stride is negative or above 2^40, or out's
                                  strides map two elements to one address        */
+    ATTN_ERR_SCRATCH = -14    /* attn_fwd_split_noalloc: the call needs more
+                                 than ATTN_NOALLOC_SCRATCH_BYTES of scratch     */
 };
 
 /* Largest number of key ranges attn_fwd_split accepts. */
@@ -203,6 +205,31 @@ int attn_fwd_split(const void* q, const void* k, const void* v, void* out,
  * n_split * B * Sq * Hq * (D + 2) * 4 (float32 partial outputs, maxima and
  * weight sums); 0 for n_split <= 1 or an empty problem. */
 size_t attn_split_workspace(int B, int Hq, int Sq, int D, int n_split);
+
+/* Bytes of the device array that attn_fwd_split_noalloc uses in place of a
+ * workspace (32 MiB per GPU the library runs on). */
+#define ATTN_NOALLOC_SCRATCH_BYTES (32 << 20)
+
+/*
+ * attn_fwd_split_noalloc — attn_fwd_split for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc. It takes no workspace: the key ranges'
+ * partial results go to a file-scope device array of
+ * ATTN_NOALLOC_SCRATCH_BYTES, which each GPU holds from the library's first
+ * use on it until the process ends. The call allocates and frees nothing.
+ *
+ * Arguments as attn_fwd_split without workspace and workspace_bytes; the
+ * device is the current one (the stream must belong to it). The result
+ * equals attn_fwd_split's bit for bit (same kernels). Errors as
+ * attn_fwd_split, plus ATTN_ERR_SCRATCH when attn_split_workspace(B, Hq, Sq,
+ * D, n_split) exceeds ATTN_NOALLOC_SCRATCH_BYTES (checked before anything
+ * else, on the host), and ATTN_ERR_HIP if the array's address cannot be
+ * obtained. All calls on one GPU share its array: calls that overlap in time
+ * on one GPU (e.g. on two streams) race and must be ordered by the caller.
+ */
+int attn_fwd_split_noalloc(const void* q, const void* k, const void* v, void* out,
+                           int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                           float scale, int causal, int dtype, int n_split, hipStream_t stream);
 
 /* attn_split_suggest — a key-range count for attn_fwd_split that fills the
  * GPU for this shape (1 when attn_fwd alone already does). Arguments as

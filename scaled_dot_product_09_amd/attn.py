@@ -8,7 +8,7 @@ no fallback: if the library is missing or a call is rejected, an exception is
 raised.
 
 The names follow include/attn.h: ``attn_fwd``, ``attn_fwd_lse``, ``attn_fwd_fp8``,
-``attn_fwd_split``, ``attn_split_workspace``, ``attn_split_suggest``,
+``attn_fwd_split``, ``attn_fwd_split_noalloc``, ``attn_split_workspace``, ``attn_split_suggest``,
 ``attn_fwd_strided``, ``attn_bwd``, ``attn_bwd_workspace``, ``attn_fwd_fp8_lse``,
 ``attn_bwd_fp8``, ``attn_bwd_fp8_workspace``, ``attn_strerror``; :func:`fwd`, :func:`fwd_lse` and :func:`bwd` are the
 tensor-level convenience wrappers.
@@ -31,8 +31,9 @@ DTYPE_CODE = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16, torch.float16:
 STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_GROUP",
           -4: "ATTN_ERR_HEAD_DIM", -5: "ATTN_ERR_DTYPE", -6: "ATTN_ERR_ALIGN", -7: "ATTN_ERR_ALIAS",
           -8: "ATTN_ERR_SCALE", -9: "ATTN_ERR_HIP", -10: "ATTN_ERR_CAUSAL", -11: "ATTN_ERR_SPLIT",
-          -12: "ATTN_ERR_WORKSPACE", -13: "ATTN_ERR_STRIDE"}
-EXPORTS = ("attn_fwd", "attn_fwd_lse", "attn_fwd_fp8", "attn_fwd_fp8_lse", "attn_fwd_split", "attn_split_workspace", "attn_split_suggest",
+          -12: "ATTN_ERR_WORKSPACE", -13: "ATTN_ERR_STRIDE", -14: "ATTN_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 32 << 20   # ATTN_NOALLOC_SCRATCH_BYTES of include/attn.h
+EXPORTS = ("attn_fwd", "attn_fwd_lse", "attn_fwd_fp8", "attn_fwd_fp8_lse", "attn_fwd_split", "attn_fwd_split_noalloc", "attn_split_workspace", "attn_split_suggest",
            "attn_fwd_strided", "attn_bwd", "attn_bwd_workspace", "attn_bwd_fp8", "attn_bwd_fp8_workspace",
            "attn_bwd_fp8_dev", "attn_fp8_state_bytes", "attn_fp8_state_init", "attn_fp8_quantize", "attn_fp8_update",
            "attn_fwd_fp8_dev", "attn_strerror")
@@ -82,6 +83,8 @@ def lib():
         L.attn_fwd_fp8.restype = i
         L.attn_fwd_split.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, ctypes.c_size_t, vp]
         L.attn_fwd_split.restype = i
+        L.attn_fwd_split_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp]
+        L.attn_fwd_split_noalloc.restype = i
         L.attn_split_workspace.argtypes = [i, i, i, i, i]
         L.attn_split_workspace.restype = ctypes.c_size_t
         L.attn_split_suggest.argtypes = [i, i, i, i, i, i, i]
@@ -124,6 +127,12 @@ def attn_fwd_split(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype, n
     """Raw C call of the split-key entry point, returns the status code."""
     return lib().attn_fwd_split(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, float(scale), int(causal), int(dtype),
                                 int(n_split), workspace, int(workspace_bytes), stream)
+
+
+def attn_fwd_split_noalloc(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype, n_split, stream):
+    """Raw C call of the allocation-free split-key entry point, returns the status code."""
+    return lib().attn_fwd_split_noalloc(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, float(scale), int(causal),
+                                        int(dtype), int(n_split), stream)
 
 
 def attn_split_workspace(B, Hq, Sq, D, n_split):

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn.so")
-SOURCES = ["attn_api.cpp", "attn_fwd_mfma.hip", "attn_fwd_f32.hip", "attn_combine.hip", "attn_bwd.hip", "attn_fp8_scaling.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd_mfma.hip", "attn_fwd_f32.hip", "attn_combine.hip", "attn_bwd.hip", "attn_fp8_scaling.hip", "attn_noalloc.hip"]
 
 # -packed-fp32-ops keeps the compiler from forming packed fp32 VALU ops
 # (v_pk_fma_f32 and friends); every HIP source is built with it.

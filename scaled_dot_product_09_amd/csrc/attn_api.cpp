@@ -696,6 +696,7 @@ extern "C" const char* attn_strerror(int status) {
         case ATTN_ERR_CAUSAL: return "causal must be 0, 1 or 2 (2, bottom-right alignment, needs Sq <= Skv)";
         case ATTN_ERR_SPLIT: return "n_split must be between 1 and ATTN_MAX_SPLIT";
         case ATTN_ERR_STRIDE: return "a stride is negative or too large, or out's strides make two elements share memory";
+        case ATTN_ERR_SCRATCH: return "the call needs more scratch than attn_fwd_split_noalloc holds (ATTN_NOALLOC_SCRATCH_BYTES); use attn_fwd_split with a workspace";
         case ATTN_ERR_WORKSPACE: return "workspace is NULL, not 16-byte aligned, smaller than the size function returns (attn_split_workspace / attn_bwd_workspace), or overlaps an input or an output";
         default: return "unknown status";
     }

@@ -279,3 +279,10 @@ def test_python_wrapper_rejects_host_tensors():
     x = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         attn.fwd(x, x, x)
+
+
+def test_noalloc_rejects_oversized_calls_on_the_host():
+    """attn_fwd_split_noalloc checks its scratch need before any HIP call:
+    8 ranges x 64 x 64 x 32 x (128 + 2) x 4 bytes = 545 MB > 32 MiB."""
+    assert attn.attn_fwd_split_noalloc(Q, K, V, O, 64, 32, 8, 64, 4096, 128, 0.1, 0, attn.ATTN_BF16, 8, None) == -14
+    assert attn.attn_split_workspace(64, 32, 64, 128, 8) > attn.NOALLOC_SCRATCH_BYTES

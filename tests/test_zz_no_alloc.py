@@ -1,0 +1,70 @@
+"""The allocation-free split-key forward (attn_fwd_split_noalloc) against
+attn_fwd_split with a caller workspace, through the C ABI.
+
+Both run the same kernels on the same inputs, so the outputs must be equal
+bit for bit; each is also checked against the fp64 oracle (2e-2, the bf16 /
+f16 bound). Two calls in a row, the second on a smaller input, show that the
+shared device array is reused correctly; a call needing more than the
+array's size is rejected before any launch.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from scaled_dot_product_09_amd import attn, workload
+from scaled_dot_product_09_amd.workload import Workload
+from tests import helpers
+from tests.helpers import TOL
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def run_both(w, n_split):
+    q, k, v, desc = workload.make_inputs(w)
+    qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+    causal = attn.CAUSAL_CODE[w.causal]
+    code = attn.DTYPE_CODE[q.dtype]
+    stream = torch.cuda.current_stream(DEV).cuda_stream
+    need = attn.attn_split_workspace(w.B, w.Hq, w.Sq, w.D, n_split)
+    assert 0 < need <= attn.NOALLOC_SCRATCH_BYTES
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    o_ref = torch.full(q.shape, float("nan"), dtype=q.dtype, device=DEV)
+    o_na = torch.full(q.shape, float("nan"), dtype=q.dtype, device=DEV)
+    args = (w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D, w.scale, causal, code, n_split)
+    st = attn.attn_fwd_split(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o_ref.data_ptr(), *args, ws.data_ptr(),
+                             need, stream)
+    assert st == 0, st
+    st = attn.attn_fwd_split_noalloc(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o_na.data_ptr(), *args, stream)
+    assert st == 0, st
+    torch.cuda.synchronize()
+    return (q, k, v, desc), o_ref, o_na
+
+
+CASES = [
+    # a decode shape near the array's size (8 ranges x 32 x 4 x 32 x 130 x 4 bytes = 17 MB), then smaller ones
+    (Workload("mqa_decode", "bf16", 32, 32, 1, 4, 8192, 128, "bottom_right", 21), 8),
+    (Workload("gqa_small", "bf16", 2, 8, 2, 3, 1000, 128, "bottom_right", 22), 3),
+    (Workload("mha_f16_d64", "f16", 1, 4, 4, 70, 700, 64, True, 23), 2),
+]
+
+
+def test_noalloc_equals_split_on_consecutive_calls():
+    for w, n_split in CASES:
+        print(f"case {w.name} n_split {n_split}", flush=True)
+        inputs, o_ref, o_na = run_both(w, n_split)
+        assert torch.equal(o_na, o_ref)
+        err = helpers.max_abs_err(helpers.out_to_f64(o_na), helpers.oracle_full(w, *inputs))
+        print(f"  equal to attn_fwd_split; max-abs vs oracle {err:.3e}", flush=True)
+        assert err <= TOL[w.dtype], err
+
+
+def test_noalloc_rejects_calls_beyond_the_array():
+    x = torch.zeros(16, dtype=torch.bfloat16, device=DEV)
+    p = x.data_ptr()
+    # 8 ranges x 64 x 64 x 32 x 130 x 4 bytes = 545 MB > 32 MiB
+    st = attn.attn_fwd_split_noalloc(p, p, p, p, 64, 32, 8, 64, 4096, 128, 0.1, 0, attn.ATTN_BF16, 8,
+                                     torch.cuda.current_stream(DEV).cuda_stream)
+    assert st == -14
