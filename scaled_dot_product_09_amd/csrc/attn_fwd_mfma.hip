@@ -49,7 +49,14 @@ namespace attn {
 // RB = 32-row blocks per wave (1 or 2). With RB = 2 every K / V operand read
 // from LDS feeds the MFMAs of both blocks, which halves LDS reads per flop;
 // the doubled accumulators need the whole register file (one wave per SIMD).
-template <typename T, int D, int BN, bool CAUSAL, int NWAVES, int RB>
+// KS = key halves per workgroup (1 or 2). With KS = 2 the workgroup has
+// twice the waves: waves w and w + NWAVES / 2 own the same query slots and
+// take alternate key tiles (even and odd). Each LDS stage then holds KS
+// tiles side by side (a step of KS * BN keys, copied by all waves); half h
+// computes on the tile at rows h * BN of it. At the end the two partial
+// softmax states (running max, weight sum, unnormalised output) of a slot
+// are merged through LDS. For grids too small to give every SIMD two waves.
+template <typename T, int D, int BN, bool CAUSAL, int NWAVES, int RB, int KS = 1>
 __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfma_kernel(FwdParams p) {
     using Tr = Traits<T>;
     using qk_frag = typename Tr::qk_frag;
@@ -63,7 +70,9 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
     constexpr int KSTEPS = D / Tr::QK_K;              // k-steps of the score product
     constexpr int NKB = BN / 32;                      // 32-key blocks per tile
     constexpr int NDB = D / 32;                       // 32-wide column blocks of O
-    constexpr int KTILE = BN * KROWB, VTILE = BN * VROWB;
+    constexpr int KTILE = KS * BN * KROWB, VTILE = KS * BN * VROWB;   // one stage: KS tiles
+    constexpr int NWQ = NWAVES / KS;                  // waves holding distinct query slots
+    static_assert(KS == 1 || RB == 1, "the key halves merge one row block per wave");
 
     // Four separate LDS objects (not one array cut in four), so the compiler
     // can prove that a copy landing in one buffer never aliases reads of
@@ -75,7 +84,9 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
 
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = KS == 1 ? wave_all : wave_all % NWQ;   // which query slots
+    const int half = KS == 1 ? 0 : wave_all / NWQ;          // which key half
     const int h = lane >> 5;              // which half of the wave
     const int n = lane & 31;              // query column inside the wave's 32 rows
 
@@ -143,6 +154,12 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
         n_tiles = min(n_tiles, last_row / BN + 1);
     }
     n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
+    // With KS = 2, half h takes the tiles h, h + 2, h + 4, ...: its local tile
+    // j is tile gt(j) = 2 j + h of the workgroup's range; n_tiles becomes the
+    // half's own count, nt_max the larger of the two halves' counts (both
+    // halves run nt_max barrier steps).
+    auto gt = [&](int j) { return KS == 1 ? j : KS * j + half; };
+    auto local_count = [&](int n_glob) { return KS == 1 ? n_glob : max(0, (n_glob - half + KS - 1) / KS); };
 
     // Split keys (n_split > 1): this workgroup takes tiles [tb, te) of the
     // n_tiles it would otherwise loop over, and writes an unnormalised partial
@@ -173,6 +190,9 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
             return;
         }
     }
+    const int nt_glob = n_tiles;
+    const int nt_max = KS == 1 ? nt_glob : (nt_glob + KS - 1) / KS;
+    n_tiles = local_count(nt_glob);
 
     // ---- tile staging ------------------------------------------------------
     // LDS: two K tiles and two V tiles. The loop below is software-pipelined
@@ -187,27 +207,28 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
     // FP8: V is widened to bf16 in registers (exact) and written to LDS by
     // the threads; 8 values (one 16-byte chunk) per thread and step.
     constexpr int NTHR = 64 * NWAVES;
-    constexpr int V_ST = Tr::V_DMA ? 1 : (BN * D / 8) / NTHR;
+    constexpr int V_ST = Tr::V_DMA ? 1 : (KS * BN * D / 8) / NTHR;
     u32x2 vstage[V_ST];
     // The copies are split over all waves, or over the first four when a
     // tile has fewer 1 KiB pieces than there are waves.
-    constexpr int NWK = (BN * KROWB / 1024) % NWAVES == 0 ? NWAVES : 4;
-    constexpr int NWV = (BN * VROWB / 1024) % NWAVES == 0 ? NWAVES : 4;
-    TileDma<KROWB, BN, NWK> kdma;
-    TileDma<VROWB, BN, NWV> vdma;
-    kdma.init(kbase, (uint32_t)krow_b, wave % NWK, lane, kSwzK);
-    if constexpr (Tr::V_DMA) vdma.init(vbase, (uint32_t)vrow_b, wave % NWV, lane, kSwzV);
+    // j is a stage (a step of KS tiles); every wave of the workgroup copies.
+    constexpr int NWK = (KS * BN * KROWB / 1024) % NWAVES == 0 ? NWAVES : 4;
+    constexpr int NWV = (KS * BN * VROWB / 1024) % NWAVES == 0 ? NWAVES : 4;
+    TileDma<KROWB, KS * BN, NWK> kdma;
+    TileDma<VROWB, KS * BN, NWV> vdma;
+    kdma.init(kbase, (uint32_t)krow_b, wave_all % NWK, lane, kSwzK);
+    if constexpr (Tr::V_DMA) vdma.init(vbase, (uint32_t)vrow_b, wave_all % NWV, lane, kSwzV);
     auto issue_k = [&](int j, uint8_t* kt) {
-        if (NWK == NWAVES || wave < NWK) kdma.issue(j * BN, Skv, kt, wave);
+        if (NWK == NWAVES || wave_all < NWK) kdma.issue(j * KS * BN, Skv, kt, wave_all);
     };
     auto issue_v = [&](int j, uint8_t* vt) {
         if constexpr (Tr::V_DMA) {
-            if (NWV == NWAVES || wave < NWV) vdma.issue(j * BN, Skv, vt, wave);
+            if (NWV == NWAVES || wave_all < NWV) vdma.issue(j * KS * BN, Skv, vt, wave_all);
         } else {
             for (int u = 0; u < V_ST; ++u) {
                 const int id = u * NTHR + tid;
                 const int r = id / (D / 8), c = id % (D / 8);
-                const int key = min(j * BN + r, Skv - 1);
+                const int key = min(j * KS * BN + r, Skv - 1);
                 vstage[u] = *(const u32x2*)(vbase + key * vrow_b + c * 8);
             }
         }
@@ -241,7 +262,7 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
     // This lane's share of the running denominator, as NLSUM partial sums
     // (the row-sum dot products of a tile form NLSUM independent chains
     // instead of one).
-    constexpr int NLSUM = 4;
+    constexpr int NLSUM = 2;
     float l_part[RB][NLSUM];
     float neg_m[RB];    // exponent offset -m_run of the tile being weighted
     for (int r = 0; r < RB; ++r) {
@@ -267,12 +288,16 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
     // flips bits of the chunk index above those of (h, t), so the offset is
     // k_lane_base ^ (ks * 32 * CH) plus t * 16 (t ^ mask bit, folded below).
     const int k_sw = k_swz<NCK>(n);
-    const uint32_t k_lane_base0 = n * KROWB + ((((h * CH) ^ k_sw)) << 4);
-    const uint32_t k_lane_base1 = n * KROWB + ((((h * CH + (CH - 1)) ^ k_sw)) << 4);
+    // With KS = 2 half h reads the tile at rows h * BN of each stage: a
+    // multiple of the swizzle periods, and a power of two above every bit the
+    // k-step XOR below touches.
+    const uint32_t k_half = (uint32_t)(half * BN * KROWB), v_half = (uint32_t)(half * BN * VROWB);
+    const uint32_t k_lane_base0 = k_half + n * KROWB + ((((h * CH) ^ k_sw)) << 4);
+    const uint32_t k_lane_base1 = k_half + n * KROWB + ((((h * CH + (CH - 1)) ^ k_sw)) << 4);
     int v_lane_off[NDB];
     for (int db = 0; db < NDB; ++db) {
         const int cb = db * 64 + v_col_b;
-        v_lane_off[db] = v_row_in * VROWB + ((((cb >> 4) ^ v_swz<NCV>(v_row_in)) << 4) | (cb & 15));
+        v_lane_off[db] = v_half + v_row_in * VROWB + ((((cb >> 4) ^ v_swz<NCV>(v_row_in)) << 4) | (cb & 15));
     }
 
     // Operand fetches from the LDS tiles (lane-base + compile-time offsets).
@@ -327,7 +352,7 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
     const float masked = -INFINITY;
     auto mask_tile = [&](f32x16 (&s)[NKB], int j, int r) {
         for (int kb = 0; kb < NKB; ++kb) {
-            const int kbase_h = j * BN + kb * 32 + 4 * h;          // key of element i: kbase_h + koff(i)
+            const int kbase_h = gt(j) * BN + kb * 32 + 4 * h;      // key of element i: kbase_h + koff(i)
             int lim = Skv - 1 - kbase_h;                            // last existing key offset
             if (CAUSAL) lim = min(lim, qrow[r] + coff - kbase_h);   // last visible key offset
             if (__builtin_amdgcn_ballot_w64(lim < 27) != 0) {   // 27 = largest koff(i)
@@ -390,12 +415,13 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
                          uint8_t* __restrict__ vb_cur, uint8_t* __restrict__ vb_next) {
         constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
         dma_barrier();
-        // The copies follow the workgroup's tiles, which (with WAVE_SKIP) may
-        // run past this wave's last computed tile. With HAS_NEXT, tile j + 1
-        // exists by construction (j + 1 < wave_tiles <= n_tiles).
-        if constexpr (HAS_NEXT || WAVE_SKIP) {
-            if (HAS_NEXT || j + 1 < n_tiles) {
-                if (j + 2 < n_tiles) issue_k(j + 2, kb_cur);
+        // The copies follow the workgroup's stages, which (with WAVE_SKIP, or
+        // for the key half with one tile fewer) may run past this wave's last
+        // computed tile. With HAS_NEXT, stage j + 1 exists by construction
+        // (j + 1 < wave_tiles <= n_tiles <= nt_max).
+        if constexpr (HAS_NEXT || WAVE_SKIP || KS == 2) {
+            if (HAS_NEXT || j + 1 < nt_max) {
+                if (j + 2 < nt_max) issue_k(j + 2, kb_cur);
                 issue_v(j + 1, vb_next);
             }
         }
@@ -531,16 +557,19 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
         // ---- C -----------------------------------------------------------------
         if constexpr (HAS_NEXT)
             for (int r = 0; r < RB; ++r) neg_m[r] = finish_max(mraw[r], r);
-        if constexpr (HAS_NEXT) finish_v(vb_next);
+        if constexpr (HAS_NEXT || KS == 2)
+            if (HAS_NEXT || j + 1 < nt_max) finish_v(vb_next);
     };
 
     f32x16 s0[RB][NKB], s1[RB][NKB];
+    // Every wave copies its share of each stage, also a key half without
+    // tiles of its own (KS = 2 with a single tile).
     issue_k(0, kbuf0);
     issue_v(0, vbuf0);
-    if (n_tiles > 1) issue_k(1, kbuf1);
+    if (nt_max > 1) issue_k(1, kbuf1);
     finish_v(vbuf0);
     dma_barrier();
-    if (!wave_idle) {
+    if (!wave_idle && n_tiles > 0) {
         qk_tile(kbuf0, s0);
         for (int r = 0; r < RB; ++r) {
             mask_tile(s0[r], 0, r);
@@ -551,12 +580,12 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
         }
     }
     if constexpr (!WAVE_SKIP) {
-        if (wave_idle) {
+        if (wave_idle || n_tiles == 0) {
             // Same copies and barriers as an iteration, no compute.
-            for (int j = 0; j < n_tiles; ++j) {
+            for (int j = 0; j < nt_max; ++j) {
                 dma_barrier();
-                if (j + 1 < n_tiles) {
-                    if (j + 2 < n_tiles) issue_k(j + 2, (j & 1) ? kbuf1 : kbuf0);
+                if (j + 1 < nt_max) {
+                    if (j + 2 < nt_max) issue_k(j + 2, (j & 1) ? kbuf1 : kbuf0);
                     issue_v(j + 1, (j & 1) ? vbuf0 : vbuf1);
                     finish_v((j & 1) ? vbuf0 : vbuf1);
                 }
@@ -573,6 +602,9 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
             } else {
                 iteration(std::false_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
             }
+            // The other key half's last stage, if it has one tile more (no
+            // copies left). The branch above already ran nt_max steps.
+            for (j = n_tiles; j < nt_max; ++j) dma_barrier();
         }
     } else {
         // The wave's own rows need tiles 0 .. wave_tiles - 1 only. Its
@@ -586,7 +618,8 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
         const int s_last = 32 * RB * (wave + 1) - 1;
         const int last_row = min(wi.row_base + (s_last / (HS * p.gpack)) * HS + s_last % HS, Sq - 1);
         const int last_key = last_row + coff;   // from the start of this workgroup's key range
-        const int wave_tiles = __builtin_amdgcn_readfirstlane(last_key < 0 ? 0 : min(n_tiles, last_key / BN + 1));
+        const int wave_tiles =
+            __builtin_amdgcn_readfirstlane(local_count(last_key < 0 ? 0 : min(nt_glob, last_key / BN + 1)));
         int j = 0;
         if (!wave_idle) {
             for (; j + 2 < wave_tiles; j += 2) {
@@ -602,15 +635,52 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
                 j += 1;
             }
         }
-        // Tiles j .. n_tiles - 1: the same copies and barriers, no compute.
-        for (; j < n_tiles; ++j) {
+        // Tiles j .. n_tiles - 1: the same copies and barriers, no compute
+        // (and, with KS = 2, the other key half's last step).
+        for (; j < nt_max; ++j) {
             dma_barrier();
-            if (j + 1 < n_tiles) {
-                if (j + 2 < n_tiles) issue_k(j + 2, (j & 1) ? kbuf1 : kbuf0);
+            if (j + 1 < nt_max) {
+                if (j + 2 < nt_max) issue_k(j + 2, (j & 1) ? kbuf1 : kbuf0);
                 issue_v(j + 1, (j & 1) ? vbuf0 : vbuf1);
                 finish_v((j & 1) ? vbuf0 : vbuf1);
             }
         }
+    }
+
+    if constexpr (KS == 2) {
+        // Merge the key halves: half 1 publishes each lane's running max,
+        // weight sum and unnormalised output in LDS (the tile buffers are free
+        // once every wave has passed this barrier); half 0 rescales both to
+        // the larger maximum and adds. Slot wave w's outputs (64 lanes x D/2
+        // floats = 128 D bytes) go to the V buffers (each holds two), the
+        // (max, sum) pairs to the first K buffer.
+        __syncthreads();
+        float lsum = l_part[0][0];
+        for (int t = 1; t < NLSUM; ++t) lsum += l_part[0][t];
+        float* xo = (float*)((wave < 2 ? lds_v0 : lds_v1) + (wave & 1) * 128 * D);
+        float* xml = (float*)lds_k0 + wave * 128;
+        if (half == 1) {
+            for (int db = 0; db < NDB; ++db)
+                for (int q4 = 0; q4 < 4; ++q4)
+                    *(f32x4*)(xo + ((db * 4 + q4) * 64 + lane) * 4) =
+                        (f32x4){oacc[0][db][4 * q4], oacc[0][db][4 * q4 + 1], oacc[0][db][4 * q4 + 2],
+                                oacc[0][db][4 * q4 + 3]};
+            *(f32x2*)(xml + lane * 2) = (f32x2){m_run[0], lsum};
+        }
+        __syncthreads();
+        if (half == 1) return;
+        const f32x2 ml1 = *(const f32x2*)(xml + lane * 2);
+        const float m = fmaxf(m_run[0], ml1[0]);
+        const float a0 = m_run[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[0] - m);
+        const float a1 = ml1[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml1[0] - m);
+        for (int db = 0; db < NDB; ++db)
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 o1 = *(const f32x4*)(xo + ((db * 4 + q4) * 64 + lane) * 4);
+                for (int e = 0; e < 4; ++e) oacc[0][db][4 * q4 + e] = a0 * oacc[0][db][4 * q4 + e] + a1 * o1[e];
+            }
+        l_part[0][0] = a0 * lsum + a1 * ml1[1];
+        for (int t = 1; t < NLSUM; ++t) l_part[0][t] = 0.f;
+        m_run[0] = m;
     }
 
     // ---- epilogue: O = O^T / l, round once, store [b][row][hq][d] ----------
@@ -651,13 +721,28 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
     }
 }
 
+// MI355X has 256 compute units; the four-wave kernel runs two workgroups
+// per CU. A launch with fewer than 1.5 workgroups per CU leaves SIMDs with a
+// single wave (nothing hides its stalls) or none; then, if a row block has
+// at least 8 key tiles, the key halves (KS = 2: eight waves per workgroup,
+// one workgroup per CU, two waves per SIMD) halve each wave's chain of tiles.
+constexpr int kComputeUnits = 256;
+
 template <typename T, int D, int BN>
 static hipError_t launch_typed(const FwdParams& p, bool causal, hipStream_t stream) {
-    const dim3 grid(p.n_units * p.n_row_blocks * p.n_split), block(64 * 4);
-    if (causal)
+    const int wgs = p.n_units * p.n_row_blocks * p.n_split;
+    const bool halves = p.n_split == 1 && wgs * 2 < kComputeUnits * 3 && (p.Skv + BN - 1) / BN >= 8;
+    const dim3 grid(wgs), block(64 * (halves ? 8 : 4));
+    if (halves) {
+        if (causal)
+            hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, true, 8, 1, 2>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, false, 8, 1, 2>), grid, block, 0, stream, p);
+    } else if (causal) {
         hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, true, 4, 1>), grid, block, 0, stream, p);
-    else
+    } else {
         hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, false, 4, 1>), grid, block, 0, stream, p);
+    }
     return hipGetLastError();
 }
 

@@ -71,6 +71,20 @@ SMALL = [
     W("e4m3", 1, 2, 1, 70, 70, 128, True),
     W("e4m3", 2, 8, 2, 192, 192, 128, True),
     W("f16", 2, 2, 1, 256, 256, 64, False),
+    # Grids of fewer than 384 workgroups with at least 8 key tiles run with two
+    # key halves per workgroup (waves w and w + 4 take alternate tiles and merge
+    # at the end): odd and even tile counts, a half without tiles of its own
+    # (top-left causal, 10 rows against 1000 keys: one tile in all), rows of
+    # several heads per wave (decode shapes), E4M3, f16 head dim 32, no mask.
+    W("bf16", 1, 4, 4, 545, 545, 128, True),       # 9 tiles
+    W("bf16", 1, 8, 2, 600, 600, 64, True),
+    W("bf16", 1, 4, 2, 10, 1000, 128, True),        # one tile: half 1 idle
+    W("bf16", 1, 4, 2, 70, 1000, 64, True),         # two tiles
+    W("bf16", 2, 8, 2, 5, 1000, 128, "bottom_right"),
+    W("bf16", 1, 2, 1, 100, 900, 128, False),
+    W("f16", 1, 4, 4, 600, 600, 32, True),
+    W("e4m3", 1, 4, 2, 600, 600, 128, True),
+    W("e4m3", 1, 2, 2, 100, 1000, 64, False),
 ]
 
 
@@ -99,6 +113,7 @@ WAVE_STOP = [
     W("bf16", 1, 2, 2, 300, 450, 128, "bottom_right"),
     W("f16", 1, 4, 2, 250, 250, 64, True),                # G = 2: two row blocks per head
     W("bf16", 1, 2, 2, 130, 130, 32, True),
+    W("bf16", 1, 2, 2, 700, 700, 128, True),              # key halves with per-wave stops
 ]
 
 
