@@ -402,18 +402,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams bp) {
     // Copies of one step: the Q and dO tiles (all four waves), the rows'
     // lse log2(e) (wave 0) and Delta (wave 1), each lane of those one row
     // (rows past the end repeat the last row; they are masked).
-    // Step t of a head covers rows [step_row(t), + BM): from the last query
-    // step down to the block's first, so that all key blocks of a KV head,
-    // which run side by side on one XCD, read the same Q / dO tiles at about
-    // the same time and share them through its L2 (the causal diagonal step
+    // Step t covers rows [step_row(t), + BM) of query head t % G: the query
+    // steps run from the last one down to the block's first, and the G heads
+    // of the group take turns within each, so that all key blocks of a KV
+    // head, which run side by side on one XCD, read the same (head, rows)
+    // tile of Q and dO at about the same time and share it through its L2,
+    // whatever the number of steps each block sees (the causal diagonal step
     // comes last).
-    auto step_row = [&](int t) { return (n_qs - 1 - t % per_head) * BM; };
+    auto step_row = [&](int t) { return (n_qs - 1 - t / G) * BM; };
     TileDma<ROWB, BM, 4> qdma, gdma;
     constexpr int NV = 2 * TileDma<ROWB, BM, 4>::PER_WAVE;   // tile copy instructions per wave and step
     static_assert(NV + 1 < 16, "the wait below encodes the count in four bits");
     const uint32_t qrow_b = (uint32_t)(p.sq[1] * 2);
     auto issue_step = [&](int t, uint8_t* qd, uint8_t* gd, float* sd) __attribute__((always_inline)) {
-        const int g = t / per_head, r0 = step_row(t);
+        const int g = t % G, r0 = step_row(t);
         const int hq = hkv * G + g;
         const size_t hoff = (size_t)b * p.sq[0] + (size_t)hq * p.sq[2];
         qdma.init((const uint8_t*)((const T*)p.q + hoff), qrow_b, wave, lane, kSwzKV);
