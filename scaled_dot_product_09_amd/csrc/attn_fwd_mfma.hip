@@ -684,6 +684,46 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
     }
 
     // ---- epilogue: O = O^T / l, round once, store [b][row][hq][d] ----------
+    // With D = 128 and a wave holding 32 consecutive rows of one head (HS =
+    // 32), the rounded tile goes through LDS first: each lane holds 4 consecutive
+    // values of one row per store, so storing from the accumulator layout
+    // takes 4 D / 32 instructions that each touch 32 rows at 16 bytes; read
+    // back row by row, the same bytes leave in 16-byte pieces of whole rows
+    // (D / 32 instructions, each 1 KiB of complete rows), a quarter of the
+    // instructions and an eighth of the memory requests. The wave's slice of
+    // the V buffers (32 rows of D 16-bit values) is free once every wave has
+    // passed the barrier below; chunks are XOR-swizzled by row as in K tiles.
+    if constexpr (KS == 1 && RB == 1 && D == 128) {
+        if (p.n_split == 1 && HS == 32) {
+            float lsum = l_part[0][0];
+            for (int t = 1; t < NLSUM; ++t) lsum += l_part[0][t];
+            const float l = xor32_sum(lsum);
+            const float inv = out_mul / l;
+            const int row = qrow[0];
+            if (p.lse && row < Sq && h == 0)
+                p.lse[((size_t)wi.b * p.Hq + hq[0]) * Sq + row] = (m_run[0] + __builtin_amdgcn_logf(l)) * kLn2;
+            __syncthreads();
+            uint8_t* const ost = (wave < 2 ? lds_v0 : lds_v1) + (wave & 1) * 32 * VROWB;
+            const int osw_n = k_swz<NCV>(n);
+            for (int db = 0; db < NDB; ++db)
+                for (int jj = 0; jj < 4; ++jj) {
+                    const uint32_t w0 = Tr::pack(oacc[0][db][4 * jj + 0] * inv, oacc[0][db][4 * jj + 1] * inv);
+                    const uint32_t w1 = Tr::pack(oacc[0][db][4 * jj + 2] * inv, oacc[0][db][4 * jj + 3] * inv);
+                    *(u32x2*)(ost + n * VROWB + (((db * 4 + jj) ^ osw_n) << 4) + h * 8) = (u32x2){w0, w1};
+                }
+            constexpr int RPI = 1024 / VROWB;   // rows per 1 KiB read / store
+            const int row0 = __builtin_amdgcn_readfirstlane(qrow[0] - n);   // the wave's first row
+            const int hw = __builtin_amdgcn_readfirstlane(hq[0]);
+            const int cc = lane % NCV;
+            out_t* const obase = (out_t*)p.out + wi.b * p.so[0] + hw * p.so[2] + cc * 8;
+            for (int it = 0; it < 32 / RPI; ++it) {
+                const int r = it * RPI + lane / NCV;
+                const u32x4 v = *(const u32x4*)(ost + r * VROWB + ((cc ^ k_swz<NCV>(r)) << 4));
+                if (row0 + r < Sq) *(u32x4*)(obase + (size_t)(row0 + r) * p.so[1]) = v;
+            }
+            return;
+        }
+    }
     for (int rb = 0; rb < RB; ++rb) {
         float lsum = l_part[rb][0];
         for (int t = 1; t < NLSUM; ++t) lsum += l_part[rb][t];
