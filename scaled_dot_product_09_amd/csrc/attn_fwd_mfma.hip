@@ -647,6 +647,7 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
         }
     }
 
+    uint8_t* ost_half = nullptr;   // KS = 2: this wave's region of the merge exchange (consumed below)
     if constexpr (KS == 2) {
         // Merge the key halves: half 1 publishes each lane's running max,
         // weight sum and unnormalised output in LDS (the tile buffers are free
@@ -681,6 +682,7 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
         l_part[0][0] = a0 * lsum + a1 * ml1[1];
         for (int t = 1; t < NLSUM; ++t) l_part[0][t] = 0.f;
         m_run[0] = m;
+        ost_half = (uint8_t*)xo;
     }
 
     // ---- epilogue: O = O^T / l, round once, store [b][row][hq][d] ----------
@@ -693,7 +695,10 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
     // instructions and an eighth of the memory requests. The wave's slice of
     // the V buffers (32 rows of D 16-bit values) is free once every wave has
     // passed the barrier below; chunks are XOR-swizzled by row as in K tiles.
-    if constexpr (KS == 1 && RB == 1 && D == 128) {
+    // With the key halves (KS = 2) only half 0 is left, and each of its waves
+    // stages the tile in its own region of the merge exchange, which it has
+    // just read.
+    if constexpr (RB == 1 && D == 128) {
         if (p.n_split == 1 && HS == 32) {
             float lsum = l_part[0][0];
             for (int t = 1; t < NLSUM; ++t) lsum += l_part[0][t];
@@ -702,8 +707,8 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
             const int row = qrow[0];
             if (p.lse && row < Sq && h == 0)
                 p.lse[((size_t)wi.b * p.Hq + hq[0]) * Sq + row] = (m_run[0] + __builtin_amdgcn_logf(l)) * kLn2;
-            __syncthreads();
-            uint8_t* const ost = (wave < 2 ? lds_v0 : lds_v1) + (wave & 1) * 32 * VROWB;
+            if constexpr (KS == 1) __syncthreads();
+            uint8_t* const ost = KS == 1 ? (wave < 2 ? lds_v0 : lds_v1) + (wave & 1) * 32 * VROWB : ost_half;
             const int osw_n = k_swz<NCV>(n);
             for (int db = 0; db < NDB; ++db)
                 for (int jj = 0; jj < 4; ++jj) {
