@@ -140,6 +140,48 @@ def cpu_baseline(w, q, k, v, desc, budget_s):
                       f"host: {os.cpu_count()} CPUs, {model}"}
 
 
+def cpu_baseline_bwd(w, q, k, v, desc, budget_s):
+    """Time the fp64 backward oracle (as it stands) on whole (batch, KV-head
+    group) units of a backward workload (the group's query heads with their
+    KV head, the workload's own dout) until ``budget_s`` seconds of CPU work
+    have accumulated; scale to TFLOP/s with the metric's backward FLOP count
+    of the heads done."""
+    import oracle
+    from tests.helpers import to_f64
+    from scaled_dot_product_09_amd.workload import bwd_metric_flops, make_dout
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    g = make_dout(w)
+    gdt, gdesc = ("e5m2", g[1]) if w.dtype == "e4m3" else (w.dtype, 1.0)
+    g = g[0] if w.dtype == "e4m3" else g
+    G = w.Hq // w.Hkv
+    done, elapsed = 0, 0.0
+    for b in range(w.B):
+        for hk in range(w.Hkv):
+            hs = slice(hk * G, (hk + 1) * G)
+            qh = to_f64(q[b:b + 1, :, hs], w.dtype, desc[0])
+            kh = to_f64(k[b:b + 1, :, hk:hk + 1], w.dtype, desc[1])
+            vh = to_f64(v[b:b + 1, :, hk:hk + 1], w.dtype, desc[2])
+            gh = to_f64(g[b:b + 1, :, hs], gdt, gdesc)
+            t0 = time.perf_counter()
+            oracle.sdpa_backward(qh, kh, vh, gh, scale=w.scale, causal=w.causal)
+            elapsed += time.perf_counter() - t0
+            done += G
+            if elapsed >= budget_s:
+                break
+        if elapsed >= budget_s:
+            break
+    flops = bwd_metric_flops(1, done, w.Sq, w.Skv, w.D, w.causal)
+    full = " (the oracle forms the whole matrices: twice the counted causal FLOPs)" if w.causal else ""
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {w.B * w.Hq} (batch, query head) pairs of the same workload, whole KV-head "
+                      f"groups, full Sq x Skv each{full}, fp64 numpy backward on {threads} BLAS threads, "
+                      f"{elapsed:.1f} s; host: {os.cpu_count()} CPUs"}
+
+
 def time_workload(w, steps, warmup, rotate=True, settle_s=SETTLE_S):
     import torch
     from scaled_dot_product_09_amd import attn, workload
@@ -325,9 +367,9 @@ def main():
     t = time_workload(w, args.steps, args.warmup, rotate=True, settle_s=args.settle_s)
     warm = time_workload(w, args.steps, args.warmup, rotate=False, settle_s=args.settle_s)
     cpu = None
-    if not args.no_cpu:
+    if not args.no_cpu and w.scaling == "amax":
         q, k, v, desc = t["inputs"]
-        cpu = cpu_baseline(w, q, k, v, desc, args.cpu_budget)
+        cpu = (cpu_baseline if w.direction == "fwd" else cpu_baseline_bwd)(w, q, k, v, desc, args.cpu_budget)
     line = result_line(w, t, args.steps, args.warmup, 1, cpu=cpu, warm=warm)
 
     if args.sweep_out:
@@ -335,9 +377,12 @@ def main():
             for n, wi in workload.WORKLOADS.items():
                 ti = time_workload(wi, args.steps, args.warmup, rotate=True, settle_s=args.settle_s)
                 ci = None
-                if args.sweep_cpu_budget > 0 and wi.direction == "fwd" and wi.scaling == "amax":
+                if args.sweep_cpu_budget > 0 and wi.scaling == "amax":
                     qi, ki, vi, di = ti["inputs"]
-                    ci = cpu_baseline(wi, qi, ki, vi, di, args.sweep_cpu_budget)
+                    if wi.direction == "fwd":
+                        ci = cpu_baseline(wi, qi, ki, vi, di, args.sweep_cpu_budget)
+                    else:
+                        ci = cpu_baseline_bwd(wi, qi, ki, vi, di, args.sweep_cpu_budget)
                 f.write(json.dumps(result_line(wi, ti, args.steps, args.warmup, 1, cpu=ci)) + "\n")
                 f.flush()
                 print(f"sweep {n}: {ti['ms_per_step']:.4f} ms", file=sys.stderr, flush=True)
