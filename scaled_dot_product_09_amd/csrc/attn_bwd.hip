@@ -121,12 +121,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams bp) {
 
     const WorkItem wi = map_workgroup(p, CAUSAL);
     const BwdScalars sc = bwd_scalars(bp);
-    const int HS = p.head_stride;
     const int slot = wave * 32 + n;
-    const int hq = wi.hq0 + (slot / HS) % p.gpack;
-    const int qrow = wi.row_base + (slot / (HS * p.gpack)) * HS + slot % HS;
-    const bool wave_idle =
-        __builtin_amdgcn_readfirstlane(wi.row_base + (wave * 32 / (HS * p.gpack)) * HS) >= p.Sq;
+    const int hq = wi.hq0 + slot_head(p, slot);
+    const int qrow = wi.row_base + slot_row(p, slot);
+    const bool wave_idle = __builtin_amdgcn_readfirstlane(wi.row_base + slot_row(p, wave * 32)) >= p.Sq;
     const int Sq = p.Sq, Skv = p.Skv;
     const bool row_ok = qrow < Sq;
 
@@ -663,7 +661,9 @@ hipError_t launch_widen_fp8(const void* in, void* out, int64_t n, bool e5m2, hip
 }
 
 template <typename T, int D>
-static hipError_t launch_bwd_typed(const BwdParams& bp, bool causal, hipStream_t stream) {
+static hipError_t launch_bwd_typed(const BwdParams& bp0, bool causal, hipStream_t stream) {
+    BwdParams bp = bp0;
+    set_divisors(bp.f);
     const FwdParams& p = bp.f;
     const unsigned gq = (unsigned)(p.n_units * p.n_row_blocks);
     const unsigned gk = (unsigned)(p.B * p.Hkv * bp.n_kblocks);

@@ -105,13 +105,12 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
     int hq[RB], qrow[RB];
     for (int r = 0; r < RB; ++r) {
         const int slot = (wave * RB + r) * 32 + n;
-        hq[r] = wi.hq0 + (slot / HS) % p.gpack;
-        qrow[r] = wi.row_base + (slot / (HS * p.gpack)) * HS + slot % HS;
+        hq[r] = wi.hq0 + slot_head(p, slot);
+        qrow[r] = wi.row_base + slot_row(p, slot);
     }
     // No slot of this wave holds a query row (its first slot has its
     // smallest row): it only copies tiles and keeps the workgroup's barriers.
-    const bool wave_idle =
-        __builtin_amdgcn_readfirstlane(wi.row_base + (wave * RB * 32 / (HS * p.gpack)) * HS) >= p.Sq;
+    const bool wave_idle = __builtin_amdgcn_readfirstlane(wi.row_base + slot_row(p, wave * RB * 32)) >= p.Sq;
     const int Sq = p.Sq;
     int Skv = p.Skv;                                   // keys of this workgroup's range, from its start
 
@@ -369,7 +368,7 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
         const int base = piece * PER;
         for (int e = 0; e < PER; e += 2) {
             const int x = base + e;
-            m = fmaxf(m, fmaxf(s[x / 16][x % 16], s[x / 16][(x + 1) % 16]));
+            m = fmaxf(fmaxf(m, s[x / 16][x % 16]), s[x / 16][(x + 1) % 16]);
         }
         return m;
     };
@@ -616,7 +615,7 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
         // workgroup's wave. This happens where the waves of a workgroup hold
         // different rows (several row blocks of one head).
         const int s_last = 32 * RB * (wave + 1) - 1;
-        const int last_row = min(wi.row_base + (s_last / (HS * p.gpack)) * HS + s_last % HS, Sq - 1);
+        const int last_row = min(wi.row_base + slot_row(p, s_last), Sq - 1);
         const int last_key = last_row + coff;   // from the start of this workgroup's key range
         const int wave_tiles =
             __builtin_amdgcn_readfirstlane(local_count(last_key < 0 ? 0 : min(nt_glob, last_key / BN + 1)));
@@ -774,7 +773,9 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
 constexpr int kComputeUnits = 256;
 
 template <typename T, int D, int BN>
-static hipError_t launch_typed(const FwdParams& p, bool causal, hipStream_t stream) {
+static hipError_t launch_typed(const FwdParams& p0, bool causal, hipStream_t stream) {
+    FwdParams p = p0;
+    set_divisors(p);
     const int wgs = p.n_units * p.n_row_blocks * p.n_split;
     const bool halves = p.n_split == 1 && wgs * 2 < kComputeUnits * 3 && (p.Skv + BN - 1) / BN >= 8;
     const dim3 grid(wgs), block(64 * (halves ? 8 : 4));

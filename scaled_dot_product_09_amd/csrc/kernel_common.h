@@ -18,6 +18,31 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
+// Division by a divisor fixed at launch, for dividends in [0, 2^31): with
+// l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1 (< 2^32),
+// n / d = (umulhi(n, m) + n) >> l (the round-up multiplier method of
+// Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994; exact for 31-bit dividends because m d - 2^(32+l)
+// is at most d <= 2^l). The sum stays below 2^32 for n < 2^31. Replaces a
+// ~40-instruction integer division by a multiply, an add and a shift.
+struct FastDiv {
+    uint32_t m;
+    int l;
+};
+
+inline FastDiv make_fastdiv(int d) {   // host side, d >= 1
+    FastDiv f;
+    f.l = 0;
+    while ((1ll << f.l) < (long long)d) ++f.l;
+    f.m = (uint32_t)(((((uint64_t)1 << f.l) - (uint64_t)d) << 32) / (uint64_t)d + 1);
+    return f;
+}
+
+__device__ inline int fdiv(int n, FastDiv f) {
+    const uint32_t hi = (uint32_t)(((uint64_t)(uint32_t)n * f.m) >> 32);
+    return (int)((hi + (uint32_t)n) >> f.l);
+}
+
 // Everything a forward kernel needs, passed by value as one kernel argument.
 struct FwdParams {
     const void* q;      // (B, Sq, Hq, D), element strides sq
@@ -50,7 +75,38 @@ struct FwdParams {
     const float* dsc_q;
     const float* dsc_k;
     const float* dsc_v;
+    // Divisors of the workgroup map (set by set_divisors before a launch):
+    // n_units / 8, n_units, n_split, G / gpack, Hkv; and log2 of head_stride
+    // and gpack (both powers of two).
+    FastDiv div_per, div_units, div_split, div_groups, div_hkv;
+    int hs_log2, gpack_log2;
 };
+
+// Fills the divisor fields from the shape fields (host side; call after the
+// last change to n_units, n_split, G, gpack, Hkv or head_stride).
+inline void set_divisors(FwdParams& p) {
+    const int per = p.n_units >> 3;
+    p.div_per = make_fastdiv(per > 0 ? per : 1);
+    p.div_units = make_fastdiv(p.n_units > 0 ? p.n_units : 1);
+    p.div_split = make_fastdiv(p.n_split > 0 ? p.n_split : 1);
+    const int groups = p.gpack > 0 ? p.G / p.gpack : 1;
+    p.div_groups = make_fastdiv(groups > 0 ? groups : 1);
+    p.div_hkv = make_fastdiv(p.Hkv > 0 ? p.Hkv : 1);
+    p.hs_log2 = 0;
+    while ((1 << p.hs_log2) < p.head_stride) ++p.hs_log2;
+    p.gpack_log2 = 0;
+    while ((1 << p.gpack_log2) < p.gpack) ++p.gpack_log2;
+}
+
+// Query slot s of a matrix-core workgroup: head offset (s / HS) % gpack and
+// row offset (s / (HS gpack)) HS + s % HS from the workgroup's first head and
+// row (see the slot map of the kernels; HS = head_stride).
+__device__ inline int slot_head(const FwdParams& p, int s) {
+    return (s >> p.hs_log2) & ((1 << p.gpack_log2) - 1);
+}
+__device__ inline int slot_row(const FwdParams& p, int s) {
+    return ((s >> (p.hs_log2 + p.gpack_log2)) << p.hs_log2) + (s & ((1 << p.hs_log2) - 1));
+}
 
 constexpr float kLog2eF32 = 1.4426950408889634f;
 
@@ -114,21 +170,21 @@ __device__ inline WorkItem map_workgroup(const FwdParams& p, bool causal) {
         const int per = p.n_units >> 3;
         const int xcd = pid & 7;
         const int slot = pid >> 3;
-        rank = slot / per;
+        rank = fdiv(slot, p.div_per);
         unit = xcd * per + (slot - rank * per);
     } else {
-        rank = pid / p.n_units;
+        rank = fdiv(pid, p.div_units);
         unit = pid - rank * p.n_units;
     }
-    const int rb_rank = rank / p.n_split;
+    const int rb_rank = fdiv(rank, p.div_split);
     const int split = rank - rb_rank * p.n_split;
     const int rb = causal ? (p.n_row_blocks - 1 - rb_rank) : rb_rank;
     const int groups = p.G / p.gpack;
-    const int hgrp = unit % groups;
-    const int t = unit / groups;
+    const int t = fdiv(unit, p.div_groups);
+    const int hgrp = unit - t * groups;
     WorkItem w;
-    w.hkv = t % p.Hkv;
-    w.b = t / p.Hkv;
+    w.b = fdiv(t, p.div_hkv);
+    w.hkv = t - w.b * p.Hkv;
     w.hq0 = w.hkv * p.G + hgrp * p.gpack;
     w.row_base = rb * p.rows_per_wg;
     w.split = split;
