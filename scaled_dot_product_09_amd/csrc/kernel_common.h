@@ -76,17 +76,24 @@ struct FwdParams {
     const float* dsc_k;
     const float* dsc_v;
     // Divisors of the workgroup map (set by set_divisors before a launch):
-    // n_units / 8, n_units, n_split, G / gpack, Hkv; and log2 of head_stride
-    // and gpack (both powers of two).
-    FastDiv div_per, div_units, div_split, div_groups, div_hkv;
+    // n_row_blocks * n_split, n_units, n_split, G / gpack, Hkv; and log2 of
+    // head_stride and gpack (both powers of two).
+    FastDiv div_ranks, div_per, div_units, div_split, div_groups, div_hkv;
     int hs_log2, gpack_log2;
+    int unit_major;     // with xcd_remap: an XCD runs its units one after another (see map_workgroup)
 };
 
 // Fills the divisor fields from the shape fields (host side; call after the
 // last change to n_units, n_split, G, gpack, Hkv or head_stride).
 inline void set_divisors(FwdParams& p) {
+    const int ranks = p.n_row_blocks * p.n_split;
+    p.div_ranks = make_fastdiv(ranks > 0 ? ranks : 1);
     const int per = p.n_units >> 3;
     p.div_per = make_fastdiv(per > 0 ? per : 1);
+    // A unit's row blocks fill an XCD's 64 workgroup slots (32 CUs, two
+    // each) on their own: its longest ones then start while at least a
+    // unit's worth of work remains, and the causal tail stays short.
+    p.unit_major = ranks >= 64;
     p.div_units = make_fastdiv(p.n_units > 0 ? p.n_units : 1);
     p.div_split = make_fastdiv(p.n_split > 0 ? p.n_split : 1);
     const int groups = p.gpack > 0 ? p.G / p.gpack : 1;
@@ -160,9 +167,13 @@ struct WorkItem {
 // to XCD i % 8 (MI355X has 8 XCDs, each with its own L2). When the units
 // split evenly over the XCDs, XCD x gets a contiguous range of units, so
 // every workgroup that reads a given KV head runs on the same XCD and shares
-// its L2. Within an XCD, row blocks go out in order of decreasing causal work
-// (the last row block first) so the short ones fill the tail of the launch;
-// the key ranges of one row block are neighbours.
+// its L2. Row blocks go out in order of decreasing causal work (the last row
+// block first) so the short ones fill the tail of the launch; the key ranges
+// of one row block are neighbours. With many row blocks per unit
+// (unit_major) the XCD runs its units one after another, all row blocks of
+// one before the next, so that about one unit's K and V are live in its L2
+// at a time; otherwise it interleaves them (every unit's longest row block
+// first).
 __device__ inline WorkItem map_workgroup(const FwdParams& p, bool causal) {
     const int pid = (int)__builtin_amdgcn_workgroup_id_x();
     int rank, unit;
@@ -170,8 +181,15 @@ __device__ inline WorkItem map_workgroup(const FwdParams& p, bool causal) {
         const int per = p.n_units >> 3;
         const int xcd = pid & 7;
         const int slot = pid >> 3;
-        rank = fdiv(slot, p.div_per);
-        unit = xcd * per + (slot - rank * per);
+        int ul;
+        if (p.unit_major) {
+            ul = fdiv(slot, p.div_ranks);
+            rank = slot - ul * (p.n_row_blocks * p.n_split);
+        } else {
+            rank = fdiv(slot, p.div_per);
+            ul = slot - rank * per;
+        }
+        unit = xcd * per + ul;
     } else {
         rank = fdiv(pid, p.div_units);
         unit = pid - rank * p.n_units;

@@ -56,6 +56,12 @@ SMALL = [
     W("bf16", 1, 8, 2, 600, 64, 128, True),       # one key tile
     W("bf16", 1, 4, 1, 700, 700, 128, True),      # G = 4, odd tile count
     W("bf16", 1, 8, 8, 1100, 1100, 128, False),   # G = 1: eight row blocks per workgroup
+    # Workgroup-map divisors that are not powers of two: 45 (batch, KV head,
+    # head group) units, Hkv = 5, G = 3; 24 units spread over the 8 XCDs
+    # (3 each); 15 units with Hkv = 3
+    W("bf16", 3, 15, 5, 130, 130, 64, True),
+    W("bf16", 3, 32, 8, 200, 200, 128, True),
+    W("bf16", 5, 6, 3, 70, 70, 128, False),
     # head dim 32
     W("bf16", 2, 8, 2, 333, 333, 32, True),
     W("bf16", 1, 4, 4, 200, 260, 32, False),
