@@ -204,10 +204,20 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
     uint8_t* const vbuf0 = lds_v0;
     uint8_t* const vbuf1 = lds_v1;
     // FP8: V is widened to bf16 in registers (exact) and written to LDS by
-    // the threads; 8 values (one 16-byte chunk) per thread and step.
+    // the threads; 8 values (one 16-byte chunk) per thread and step. Thread
+    // tid stages chunk c0 = tid % (D / 8) of rows r0 + u RSTEP of the stage
+    // (u < V_ST); the row step keeps the chunk and the swizzle mask, so the
+    // global and LDS offsets of every u are the thread's offsets for u = 0
+    // plus a constant, and a stage only adds a scalar offset.
     constexpr int NTHR = 64 * NWAVES;
     constexpr int V_ST = Tr::V_DMA ? 1 : (KS * BN * D / 8) / NTHR;
+    constexpr int RSTEP = NTHR / (D / 8);
+    static_assert(Tr::V_DMA || (NTHR % (D / 8) == 0 && RSTEP % 16 == 0), "the V swizzle must repeat over RSTEP rows");
     u32x2 vstage[V_ST];
+    const int v_r0 = tid / (D / 8), v_c0 = tid % (D / 8);
+    const uint32_t v_goff = (uint32_t)v_r0 * (uint32_t)vrow_b + (uint32_t)v_c0 * 8;   // tile byte offset, u = 0
+    const uint32_t v_loff = (uint32_t)(v_r0 * VROWB + ((v_c0 ^ v_swz<NCV>(v_r0)) << 4));
+    const __amdgpu_buffer_rsrc_t v_rs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, -1, kBufferWord3);
     // The copies are split over all waves, or over the first four when a
     // tile has fewer 1 KiB pieces than there are waves.
     // j is a stage (a step of KS tiles); every wave of the workgroup copies.
@@ -224,19 +234,27 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
         if constexpr (Tr::V_DMA) {
             if (NWV == NWAVES || wave_all < NWV) vdma.issue(j * KS * BN, Skv, vt, wave_all);
         } else {
-            for (int u = 0; u < V_ST; ++u) {
-                const int id = u * NTHR + tid;
-                const int r = id / (D / 8), c = id % (D / 8);
-                const int key = min(j * KS * BN + r, Skv - 1);
-                vstage[u] = *(const u32x2*)(vbase + key * vrow_b + c * 8);
+            // Rows past the end of the keys (last stage only) repeat the last
+            // key, as in the tile copies. Byte offsets stay below
+            // Skv * row stride < 2^32.
+            const int key0 = j * KS * BN;
+            const uint32_t t0 = (uint32_t)key0 * (uint32_t)vrow_b;
+            if (key0 + KS * BN <= Skv) {
+                for (int u = 0; u < V_ST; ++u)
+                    vstage[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                        v_rs, v_goff, t0 + (uint32_t)(u * RSTEP) * (uint32_t)vrow_b, 0));
+            } else {
+                for (int u = 0; u < V_ST; ++u) {
+                    const int key = min(key0 + v_r0 + u * RSTEP, Skv - 1);
+                    vstage[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                        v_rs, (uint32_t)key * (uint32_t)vrow_b + (uint32_t)v_c0 * 8, 0, 0));
+                }
             }
         }
     };
     auto finish_v = [&](uint8_t* vt) {   // FP8 only: widen the staged V and write it
         if constexpr (!Tr::V_DMA) {
             for (int u = 0; u < V_ST; ++u) {
-                const int id = u * NTHR + tid;
-                const int r = id / (D / 8), c = id % (D / 8);
                 u32x4 w;
                 // Two E4M3 codes -> two bf16 per instruction (scale 1: exact,
                 // every E4M3 value is a bf16 value; same bits as widening to
@@ -247,7 +265,7 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
                     w[2 * e + 1] = __builtin_bit_cast(
                         uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vstage[u][e], 1.0f, true));
                 }
-                *(u32x4*)(vt + r * VROWB + ((c ^ v_swz<NCV>(r)) * 16)) = w;
+                *(u32x4*)(vt + v_loff + u * RSTEP * VROWB) = w;
             }
         }
     };
