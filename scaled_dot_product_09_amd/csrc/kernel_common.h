@@ -38,7 +38,7 @@ inline FastDiv make_fastdiv(int d) {   // host side, d >= 1
     return f;
 }
 
-__device__ inline int fdiv(int n, FastDiv f) {
+__host__ __device__ inline int fdiv(int n, FastDiv f) {
     const uint32_t hi = (uint32_t)(((uint64_t)(uint32_t)n * f.m) >> 32);
     return (int)((hi + (uint32_t)n) >> f.l);
 }
