@@ -57,7 +57,7 @@ namespace attn {
 // softmax states (running max, weight sum, unnormalised output) of a slot
 // are merged through LDS. For grids too small to give every SIMD two waves.
 template <typename T, int D, int BN, bool CAUSAL, int NWAVES, int RB, int KS = 1>
-__global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfma_kernel(FwdParams p) {
+__global__ __launch_bounds__(64 * NWAVES, RB == 1 ? (BN == 32 ? 3 : 8 / NWAVES) : 1) void fwd_mfma_kernel(FwdParams p) {
     using Tr = Traits<T>;
     using qk_frag = typename Tr::qk_frag;
     using pv_frag = typename Tr::pv_frag;
@@ -578,88 +578,152 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
             if (HAS_NEXT || j + 1 < nt_max) finish_v(vb_next);
     };
 
-    f32x16 s0[RB][NKB], s1[RB][NKB];
-    // Every wave copies its share of each stage, also a key half without
-    // tiles of its own (KS = 2 with a single tile).
-    issue_k(0, kbuf0);
-    issue_v(0, vbuf0);
-    if (nt_max > 1) issue_k(1, kbuf1);
-    finish_v(vbuf0);
-    dma_barrier();
-    if (!wave_idle && n_tiles > 0) {
-        qk_tile(kbuf0, s0);
-        for (int r = 0; r < RB; ++r) {
-            mask_tile(s0[r], 0, r);
-            float mraw = masked;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) mraw = max_piece(s0[r], g, mraw, std::integral_constant<int, 4>{});
-            neg_m[r] = finish_max(mraw, r);
+    // BN = 32: the sequential form for workgroups with few tiles. One score
+    // tile is live per wave (tile j's K and V in the buffers of parity
+    // j & 1, the copies of tile j + 1 issued after the barrier; scores, row
+    // max, weights and P V of tile j in order), so a wave needs 160
+    // registers and a workgroup 32 KiB of LDS: three workgroups per CU, whose
+    // start-up and end hide behind each other where a workgroup's life is
+    // short. With many tiles the pipelined form below (64-key tiles, the
+    // scores of tile j + 1 beside the weights of tile j, two workgroups per
+    // CU) is faster.
+    constexpr bool SEQ = BN == 32;
+    static_assert(!SEQ || (Tr::V_DMA && KS == 1 && RB == 1), "the sequential form is for 16-bit inputs, KS = RB = 1");
+    if constexpr (SEQ) {
+        int wave_tiles = n_tiles;
+        if constexpr (WAVE_SKIP) {
+            const int s_last = 32 * RB * (wave + 1) - 1;
+            const int last_row = min(wi.row_base + slot_row(p, s_last), Sq - 1);
+            const int last_key = last_row + coff;
+            wave_tiles = __builtin_amdgcn_readfirstlane(local_count(last_key < 0 ? 0 : min(nt_glob, last_key / BN + 1)));
         }
-    }
-    if constexpr (!WAVE_SKIP) {
-        if (wave_idle || n_tiles == 0) {
-            // Same copies and barriers as an iteration, no compute.
-            for (int j = 0; j < nt_max; ++j) {
+        issue_k(0, kbuf0);
+        issue_v(0, vbuf0);
+        for (int j = 0; j < nt_max; ++j) {
+            uint8_t* const kt = (j & 1) ? kbuf1 : kbuf0;
+            uint8_t* const vt = (j & 1) ? vbuf1 : vbuf0;
+            dma_barrier();
+            if (j + 1 < nt_max) {
+                issue_k(j + 1, (j & 1) ? kbuf0 : kbuf1);
+                issue_v(j + 1, (j & 1) ? vbuf0 : vbuf1);
+            }
+            if (wave_idle || j >= wave_tiles) continue;
+            f32x16 s[RB][NKB];
+            qk_tile(kt, s);
+            for (int r = 0; r < RB; ++r) {
+                mask_tile(s[r], j, r);
+                float mraw = masked;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) mraw = max_piece(s[r], g, mraw, std::integral_constant<int, 4>{});
+                neg_m[r] = finish_max(mraw, r);
+            }
+            uint32_t pw[RB][NKB][8];
+#pragma unroll
+            for (int r = 0; r < RB; ++r)
+                for (int kb = 0; kb < NKB; ++kb)
+                    for (int i = 0; i < 8; ++i)
+                        pw[r][kb][i] = Tr::pack(__builtin_amdgcn_exp2f(fmaf(s[r][kb][2 * i], c_log2, neg_m[r])),
+                                                __builtin_amdgcn_exp2f(fmaf(s[r][kb][2 * i + 1], c_log2, neg_m[r])));
+            pv_frag vf[2][NDB];
+            for (int db = 0; db < NDB; ++db) vf[0][db] = load_v(vt, 0, 0, db);
+#pragma unroll
+            for (int g = 0; g < NKB * 2; ++g) {
+                const int kb = g / 2, s2 = g % 2;
+                if (g + 1 < NKB * 2)
+                    for (int db = 0; db < NDB; ++db) vf[(g + 1) & 1][db] = load_v(vt, (g + 1) / 2, (g + 1) % 2, db);
+                for (int r = 0; r < RB; ++r) {
+                    const pv_frag pf = __builtin_bit_cast(pv_frag, (u32x4){pw[r][kb][4 * s2], pw[r][kb][4 * s2 + 1],
+                                                                           pw[r][kb][4 * s2 + 2], pw[r][kb][4 * s2 + 3]});
+                    for (int db = 0; db < NDB; ++db) oacc[r][db] = Tr::pv(vf[g & 1][db], pf, oacc[r][db]);
+                    for (int t = 0; t < 4; ++t)
+                        l_part[r][t % NLSUM] = Tr::sum2(pw[r][kb][4 * s2 + t], l_part[r][t % NLSUM]);
+                }
+            }
+        }
+    } else {
+        f32x16 s0[RB][NKB], s1[RB][NKB];
+        // Every wave copies its share of each stage, also a key half without
+        // tiles of its own (KS = 2 with a single tile).
+        issue_k(0, kbuf0);
+        issue_v(0, vbuf0);
+        if (nt_max > 1) issue_k(1, kbuf1);
+        finish_v(vbuf0);
+        dma_barrier();
+        if (!wave_idle && n_tiles > 0) {
+            qk_tile(kbuf0, s0);
+            for (int r = 0; r < RB; ++r) {
+                mask_tile(s0[r], 0, r);
+                float mraw = masked;
+    #pragma unroll
+                for (int g = 0; g < 4; ++g) mraw = max_piece(s0[r], g, mraw, std::integral_constant<int, 4>{});
+                neg_m[r] = finish_max(mraw, r);
+            }
+        }
+        if constexpr (!WAVE_SKIP) {
+            if (wave_idle || n_tiles == 0) {
+                // Same copies and barriers as an iteration, no compute.
+                for (int j = 0; j < nt_max; ++j) {
+                    dma_barrier();
+                    if (j + 1 < nt_max) {
+                        if (j + 2 < nt_max) issue_k(j + 2, (j & 1) ? kbuf1 : kbuf0);
+                        issue_v(j + 1, (j & 1) ? vbuf0 : vbuf1);
+                        finish_v((j & 1) ? vbuf0 : vbuf1);
+                    }
+                }
+            } else {
+                int j = 0;
+                for (; j + 2 < n_tiles; j += 2) {
+                    iteration(std::true_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
+                    iteration(std::true_type{}, j + 1, s1, s0, kbuf1, kbuf0, vbuf1, vbuf0);
+                }
+                if (j + 1 < n_tiles) {
+                    iteration(std::true_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
+                    iteration(std::false_type{}, j + 1, s1, s0, kbuf1, kbuf0, vbuf1, vbuf0);
+                } else {
+                    iteration(std::false_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
+                }
+                // The other key half's last stage, if it has one tile more (no
+                // copies left). The branch above already ran nt_max steps.
+                for (j = n_tiles; j < nt_max; ++j) dma_barrier();
+            }
+        } else {
+            // The wave's own rows need tiles 0 .. wave_tiles - 1 only. Its
+            // highest row is that of its last slot (rows grow with the slot's run
+            // index, and the last slot ends a run); rows past Sq count as row
+            // Sq - 1 (their results are never stored). From tile wave_tiles on,
+            // every score of the wave is masked and every weight 0, so the wave
+            // only copies and keeps the barriers, leaving its SIMD to the other
+            // workgroup's wave. This happens where the waves of a workgroup hold
+            // different rows (several row blocks of one head).
+            const int s_last = 32 * RB * (wave + 1) - 1;
+            const int last_row = min(wi.row_base + slot_row(p, s_last), Sq - 1);
+            const int last_key = last_row + coff;   // from the start of this workgroup's key range
+            const int wave_tiles =
+                __builtin_amdgcn_readfirstlane(local_count(last_key < 0 ? 0 : min(nt_glob, last_key / BN + 1)));
+            int j = 0;
+            if (!wave_idle) {
+                for (; j + 2 < wave_tiles; j += 2) {
+                    iteration(std::true_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
+                    iteration(std::true_type{}, j + 1, s1, s0, kbuf1, kbuf0, vbuf1, vbuf0);
+                }
+                if (j + 1 < wave_tiles) {
+                    iteration(std::true_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
+                    iteration(std::false_type{}, j + 1, s1, s0, kbuf1, kbuf0, vbuf1, vbuf0);
+                    j += 2;
+                } else if (j < wave_tiles) {
+                    iteration(std::false_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
+                    j += 1;
+                }
+            }
+            // Tiles j .. n_tiles - 1: the same copies and barriers, no compute
+            // (and, with KS = 2, the other key half's last step).
+            for (; j < nt_max; ++j) {
                 dma_barrier();
                 if (j + 1 < nt_max) {
                     if (j + 2 < nt_max) issue_k(j + 2, (j & 1) ? kbuf1 : kbuf0);
                     issue_v(j + 1, (j & 1) ? vbuf0 : vbuf1);
                     finish_v((j & 1) ? vbuf0 : vbuf1);
                 }
-            }
-        } else {
-            int j = 0;
-            for (; j + 2 < n_tiles; j += 2) {
-                iteration(std::true_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
-                iteration(std::true_type{}, j + 1, s1, s0, kbuf1, kbuf0, vbuf1, vbuf0);
-            }
-            if (j + 1 < n_tiles) {
-                iteration(std::true_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
-                iteration(std::false_type{}, j + 1, s1, s0, kbuf1, kbuf0, vbuf1, vbuf0);
-            } else {
-                iteration(std::false_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
-            }
-            // The other key half's last stage, if it has one tile more (no
-            // copies left). The branch above already ran nt_max steps.
-            for (j = n_tiles; j < nt_max; ++j) dma_barrier();
-        }
-    } else {
-        // The wave's own rows need tiles 0 .. wave_tiles - 1 only. Its
-        // highest row is that of its last slot (rows grow with the slot's run
-        // index, and the last slot ends a run); rows past Sq count as row
-        // Sq - 1 (their results are never stored). From tile wave_tiles on,
-        // every score of the wave is masked and every weight 0, so the wave
-        // only copies and keeps the barriers, leaving its SIMD to the other
-        // workgroup's wave. This happens where the waves of a workgroup hold
-        // different rows (several row blocks of one head).
-        const int s_last = 32 * RB * (wave + 1) - 1;
-        const int last_row = min(wi.row_base + slot_row(p, s_last), Sq - 1);
-        const int last_key = last_row + coff;   // from the start of this workgroup's key range
-        const int wave_tiles =
-            __builtin_amdgcn_readfirstlane(local_count(last_key < 0 ? 0 : min(nt_glob, last_key / BN + 1)));
-        int j = 0;
-        if (!wave_idle) {
-            for (; j + 2 < wave_tiles; j += 2) {
-                iteration(std::true_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
-                iteration(std::true_type{}, j + 1, s1, s0, kbuf1, kbuf0, vbuf1, vbuf0);
-            }
-            if (j + 1 < wave_tiles) {
-                iteration(std::true_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
-                iteration(std::false_type{}, j + 1, s1, s0, kbuf1, kbuf0, vbuf1, vbuf0);
-                j += 2;
-            } else if (j < wave_tiles) {
-                iteration(std::false_type{}, j, s0, s1, kbuf0, kbuf1, vbuf0, vbuf1);
-                j += 1;
-            }
-        }
-        // Tiles j .. n_tiles - 1: the same copies and barriers, no compute
-        // (and, with KS = 2, the other key half's last step).
-        for (; j < nt_max; ++j) {
-            dma_barrier();
-            if (j + 1 < nt_max) {
-                if (j + 2 < nt_max) issue_k(j + 2, (j & 1) ? kbuf1 : kbuf0);
-                issue_v(j + 1, (j & 1) ? vbuf0 : vbuf1);
-                finish_v((j & 1) ? vbuf0 : vbuf1);
             }
         }
     }
@@ -725,7 +789,12 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? 8 / NWAVES : 1) void fwd_mfm
             if (p.lse && row < Sq && h == 0)
                 p.lse[((size_t)wi.b * p.Hq + hq[0]) * Sq + row] = (m_run[0] + __builtin_amdgcn_logf(l)) * kLn2;
             if constexpr (KS == 1) __syncthreads();
-            uint8_t* const ost = KS == 1 ? (wave < 2 ? lds_v0 : lds_v1) + (wave & 1) * 32 * VROWB : ost_half;
+            // Each wave needs 32 rows of VROWB bytes: two per V buffer when a V
+            // buffer holds 64 rows, else one buffer of the four per wave.
+            static_assert(KS == 2 || VTILE >= 2 * 32 * VROWB || (VTILE >= 32 * VROWB && KTILE >= 32 * VROWB), "");
+            uint8_t* const ost = KS == 2 ? ost_half
+                               : VTILE >= 2 * 32 * VROWB ? (wave < 2 ? lds_v0 : lds_v1) + (wave & 1) * 32 * VROWB
+                               : (wave == 0 ? lds_k0 : wave == 1 ? lds_k1 : wave == 2 ? lds_v0 : lds_v1);
             const int osw_n = k_swz<NCV>(n);
             for (int db = 0; db < NDB; ++db)
                 for (int jj = 0; jj < 4; ++jj) {
@@ -796,12 +865,26 @@ static hipError_t launch_typed(const FwdParams& p0, bool causal, hipStream_t str
     set_divisors(p);
     const int wgs = p.n_units * p.n_row_blocks * p.n_split;
     const bool halves = p.n_split == 1 && wgs * 2 < kComputeUnits * 3 && (p.Skv + BN - 1) / BN >= 8;
+    // Head dim 128 with few 64-key tiles per workgroup (on average; causal
+    // rows see half the keys): the sequential form at three workgroups per
+    // CU (measured: causal S = 512 and 1024 +7 to +15 %; causal S = 2048 and
+    // non-causal S = 1024 3-7 % slower).
+    const int nt64 = (p.Skv + 63) / 64;
+    const int avg_tiles = causal ? (nt64 + 1) / 2 : nt64;
+    const bool seq = D == 128 && Traits<T>::V_DMA && p.n_split == 1 && !halves && avg_tiles <= 9;
     const dim3 grid(wgs), block(64 * (halves ? 8 : 4));
     if (halves) {
         if (causal)
             hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, true, 8, 1, 2>), grid, block, 0, stream, p);
         else
             hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, false, 8, 1, 2>), grid, block, 0, stream, p);
+    } else if (seq) {
+        if constexpr (D == 128 && Traits<T>::V_DMA) {
+            if (causal)
+                hipLaunchKernelGGL((fwd_mfma_kernel<T, D, 32, true, 4, 1>), grid, block, 0, stream, p);
+            else
+                hipLaunchKernelGGL((fwd_mfma_kernel<T, D, 32, false, 4, 1>), grid, block, 0, stream, p);
+        }
     } else if (causal) {
         hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, true, 4, 1>), grid, block, 0, stream, p);
     } else {

@@ -56,6 +56,13 @@ SMALL = [
     W("bf16", 1, 8, 2, 600, 64, 128, True),       # one key tile
     W("bf16", 1, 4, 1, 700, 700, 128, True),      # G = 4, odd tile count
     W("bf16", 1, 8, 8, 1100, 1100, 128, False),   # G = 1: eight row blocks per workgroup
+    # Head dim 128 runs the sequential 32-key form where a workgroup sees few
+    # 64-key tiles (at most 9 on average) and the pipelined form otherwise:
+    # both forms at small, ragged sizes
+    W("bf16", 1, 4, 2, 1300, 1300, 128, True),    # pipelined (causal, 11 tiles on average)
+    W("bf16", 2, 8, 2, 700, 700, 128, False),     # pipelined (11 tiles)
+    W("bf16", 1, 8, 2, 500, 500, 128, False),     # sequential (8 tiles)
+    W("f16", 2, 4, 4, 450, 450, 128, True),       # sequential, f16
     # Workgroup-map divisors that are not powers of two: 45 (batch, KV head,
     # head group) units, Hkv = 5, G = 3; 24 units spread over the 8 XCDs
     # (3 each); 15 units with Hkv = 3
