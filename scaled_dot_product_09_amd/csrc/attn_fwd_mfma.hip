@@ -14,13 +14,17 @@
 // and P V on the bf16 instruction, because E4M3 weights would cost up to
 // 2^-4 relative error per weight on rows that see only a few keys).
 //
-// Design (one workgroup = 4 wavefronts of 64 lanes, two workgroups per CU):
+// Design (one workgroup = 4 wavefronts of 64 lanes, two workgroups per CU;
+// the launcher's shape rule picks the key-half form for very small grids and
+// the sequential 32-key form, three workgroups per CU, for short rows of keys
+// at head dim 128 — see the kernel template and launch_typed):
 //   * Each wave owns 32 query rows of one query head. A workgroup holds
 //     `gpack` query heads that read the same KV head, 4 / gpack row blocks of
 //     32 rows each, so every K/V tile staged in LDS serves 128 query rows.
 //   * K and V tiles go from HBM straight into LDS (buffer loads to LDS,
-//     no register staging), double-buffered: tile j+1 is in flight while
-//     tile j is computed, with one barrier per tile. 16-byte chunks are
+//     no register staging; FP8 V through registers, widened to bf16),
+//     double-buffered: the next tile is in flight while one is computed,
+//     with one barrier per tile. 16-byte chunks are
 //     XOR-swizzled per row so the operand reads below are bank-conflict free.
 //   * Scores are computed transposed, S^T = K Q^T: lane (h = lane / 32,
 //     n = lane % 32) then holds 16 scores of query n per 32-key block, so a
