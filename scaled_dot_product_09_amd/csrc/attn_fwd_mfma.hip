@@ -869,12 +869,13 @@ static hipError_t launch_typed(const FwdParams& p0, bool causal, hipStream_t str
     set_divisors(p);
     const int wgs = p.n_units * p.n_row_blocks * p.n_split;
     const bool halves = p.n_split == 1 && wgs * 2 < kComputeUnits * 3 && (p.Skv + BN - 1) / BN >= 8;
-    // Head dim 128 with few 64-key tiles per workgroup (on average; causal
-    // rows see half the keys): the sequential form at three workgroups per
-    // CU (measured: causal S = 512 and 1024 +7 to +15 %; causal S = 2048 and
-    // non-causal S = 1024 3-7 % slower).
-    const int nt64 = (p.Skv + 63) / 64;
-    const int avg_tiles = causal ? (nt64 + 1) / 2 : nt64;
+    // Head dim 128 with few 64-key tiles per workgroup on average (a masked
+    // row sees causal_off + its index + 1 keys, on average causal_off + Sq / 2):
+    // the sequential form at three workgroups per CU (measured: causal
+    // S = 512 and 1024 +7 to +15 %; causal S = 2048 and non-causal S = 1024
+    // 3-7 % slower).
+    const int64_t vis = causal ? std::min<int64_t>(p.Skv, (int64_t)p.causal_off + (p.Sq + 1) / 2) : p.Skv;
+    const int64_t avg_tiles = (vis + 63) / 64;
     const bool seq = D == 128 && Traits<T>::V_DMA && p.n_split == 1 && !halves && avg_tiles <= 9;
     const dim3 grid(wgs), block(64 * (halves ? 8 : 4));
     if (halves) {
