@@ -472,12 +472,16 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? (BN == 32 ? 3 : 8 / NWAVES) 
             asm volatile("" : "+v"(pw[r][kb][i]));
         };
         // ---- A ---------------------------------------------------------------
-        // Phase A is the one that mixes score MFMAs with the softmax VALU
-        // work; raising the wave's issue priority for it lets it win the
-        // issue arbitration over the SIMD's other wave (usually in its
-        // MFMA-only phase B), which keeps both the matrix core and the VALU
-        // fed. Measured: +2 % (D=128) and +6 % (D=64) over equal priority.
-        __builtin_amdgcn_s_setprio(1);
+        // Phase A mixes the score MFMAs with the softmax VALU work, phase B
+        // is mostly P V MFMAs. One of them runs at raised wave priority, so
+        // that it wins the issue arbitration over the SIMD's other wave: at
+        // D = 128 (matrix-bound) phase A, which keeps both the matrix core and
+        // the VALU fed (+2 % over equal priority); at D = 64 and 32 (vector-
+        // bound) phase B, which keeps the matrix products from queuing behind
+        // the other wave's softmax (+1.6 % causal, +8 % non-causal against
+        // phase A at D = 64; +1.6 % at D = 32).
+        constexpr int PRIO_A = D == 128 ? 1 : 0;
+        __builtin_amdgcn_s_setprio(PRIO_A);
         // With BAL, the exponentials of the last PV group's four weight pairs
         // move from phase A into the first two PV groups of phase B (the last
         // group is the first to need them), which evens out the vector work
@@ -530,7 +534,7 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? (BN == 32 ? 3 : 8 / NWAVES) 
             for (int db = 0; db < NDB; ++db) vf[0][db] = load_v(vb_cur, 0, 0, db);
         }
         // ---- B -----------------------------------------------------------------
-        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_s_setprio(1 - PRIO_A);
         float mraw[RB];
         for (int r = 0; r < RB; ++r) mraw[r] = masked;
 #pragma unroll
