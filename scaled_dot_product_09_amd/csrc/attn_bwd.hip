@@ -259,6 +259,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams bp) {
                 }
             }
         };
+        // A wave in phases 3-4 (the dQ products, with the second block's
+        // weights between them) runs at raised priority, so its products
+        // issue ahead of the score products and weights of the other wave on
+        // the SIMD (1 to 4 % faster than equal priority at D = 32, 64 and
+        // 128, causal or not).
+        __builtin_amdgcn_s_setprio(0);
         // Phases 1-2: u = kb KSTEPS + ks.
         constexpr int U = NKB * KSTEPS;
         constexpr int PER_U = 16 / KSTEPS;
@@ -280,6 +286,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams bp) {
             if (kb == 1) weights(0, ks * PER_U, PER_U);
             __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_s_setprio(1);
         // Phases 3-4: v = (kb 2 + s2) NDB + db.
         constexpr int V = NKB * 2 * NDB;
         constexpr int PER_V = 16 / (2 * NDB);
