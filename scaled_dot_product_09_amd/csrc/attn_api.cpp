@@ -67,6 +67,7 @@ attn::FwdParams make_params(const void* q, const void* k, const void* v, void* o
     // Bottom-right alignment shifts every query to position Skv - Sq + i.
     p.causal_off = causal == 2 ? Skv - Sq : 0;
     p.n_split = 1;
+    p.fold = 0;
     p.part_o = nullptr;
     p.part_ml = nullptr;
     p.lse = nullptr;

@@ -54,8 +54,11 @@ namespace attn {
 // from LDS feeds the MFMAs of both blocks, which halves LDS reads per flop;
 // the doubled accumulators need the whole register file (one wave per SIMD).
 // KS = key halves per workgroup (1 or 2). With KS = 2 the workgroup has
-// twice the waves: waves w and w + NWAVES / 2 own the same query slots and
-// take alternate key tiles (even and odd). Each LDS stage then holds KS
+// twice the waves: waves 2 w and 2 w + 1 own the same query slots and take
+// alternate key tiles (even and odd); the SIMD that runs one of them (waves
+// go round the four SIMDs in order) also runs a half of query wave w + 2,
+// which in a folded workgroup holds the mirror row block, so the causal
+// work of the two blocks shares every SIMD. Each LDS stage then holds KS
 // tiles side by side (a step of KS * BN keys, copied by all waves); half h
 // computes on the tile at rows h * BN of it. At the end the two partial
 // softmax states (running max, weight sum, unnormalised output) of a slot
@@ -89,8 +92,8 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? (BN == 32 ? 3 : 8 / NWAVES) 
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
     const int lane = tid & 63;
     const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wave = KS == 1 ? wave_all : wave_all % NWQ;   // which query slots
-    const int half = KS == 1 ? 0 : wave_all / NWQ;          // which key half
+    const int wave = KS == 1 ? wave_all : wave_all / KS;    // which query slots
+    const int half = KS == 1 ? 0 : wave_all % KS;           // which key half
     const int h = lane >> 5;              // which half of the wave
     const int n = lane & 31;              // query column inside the wave's 32 rows
 
@@ -110,11 +113,11 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? (BN == 32 ? 3 : 8 / NWAVES) 
     for (int r = 0; r < RB; ++r) {
         const int slot = (wave * RB + r) * 32 + n;
         hq[r] = wi.hq0 + slot_head(p, slot);
-        qrow[r] = wi.row_base + slot_row(p, slot);
+        qrow[r] = item_row(p, wi, slot);
     }
     // No slot of this wave holds a query row (its first slot has its
     // smallest row): it only copies tiles and keeps the workgroup's barriers.
-    const bool wave_idle = __builtin_amdgcn_readfirstlane(wi.row_base + slot_row(p, wave * RB * 32)) >= p.Sq;
+    const bool wave_idle = __builtin_amdgcn_readfirstlane(item_row(p, wi, wave * RB * 32)) >= p.Sq;
     const int Sq = p.Sq;
     int Skv = p.Skv;                                   // keys of this workgroup's range, from its start
 
@@ -153,7 +156,7 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? (BN == 32 ? 3 : 8 / NWAVES) 
 
     int n_tiles = (Skv + BN - 1) / BN;
     if (CAUSAL) {
-        const int last_row = min(wi.row_base + p.rows_per_wg, Sq) - 1 + p.causal_off;
+        const int last_row = min(wi.row_end, Sq) - 1 + p.causal_off;
         n_tiles = min(n_tiles, last_row / BN + 1);
     }
     n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
@@ -601,7 +604,7 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? (BN == 32 ? 3 : 8 / NWAVES) 
         int wave_tiles = n_tiles;
         if constexpr (WAVE_SKIP) {
             const int s_last = 32 * RB * (wave + 1) - 1;
-            const int last_row = min(wi.row_base + slot_row(p, s_last), Sq - 1);
+            const int last_row = min(item_row(p, wi, s_last), Sq - 1);
             const int last_key = last_row + coff;
             wave_tiles = __builtin_amdgcn_readfirstlane(local_count(last_key < 0 ? 0 : min(nt_glob, last_key / BN + 1)));
         }
@@ -704,7 +707,7 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? (BN == 32 ? 3 : 8 / NWAVES) 
             // workgroup's wave. This happens where the waves of a workgroup hold
             // different rows (several row blocks of one head).
             const int s_last = 32 * RB * (wave + 1) - 1;
-            const int last_row = min(wi.row_base + slot_row(p, s_last), Sq - 1);
+            const int last_row = min(item_row(p, wi, s_last), Sq - 1);
             const int last_key = last_row + coff;   // from the start of this workgroup's key range
             const int wave_tiles =
                 __builtin_amdgcn_readfirstlane(local_count(last_key < 0 ? 0 : min(nt_glob, last_key / BN + 1)));
@@ -870,9 +873,26 @@ constexpr int kComputeUnits = 256;
 template <typename T, int D, int BN>
 static hipError_t launch_typed(const FwdParams& p0, bool causal, hipStream_t stream) {
     FwdParams p = p0;
-    set_divisors(p);
-    const int wgs = p.n_units * p.n_row_blocks * p.n_split;
+    int wgs = p.n_units * p.n_row_blocks * p.n_split;
     const bool halves = p.n_split == 1 && wgs * 2 < kComputeUnits * 3 && (p.Skv + BN - 1) / BN >= 8;
+    if (halves && causal && Traits<T>::V_DMA && p.head_stride == 32) {
+        // Causal key halves fold the row blocks: blocks of 64 / gpack rows
+        // (gpack at most 2, so a wave still holds 32 rows of one head), two
+        // mirror blocks per workgroup, the same number of workgroups.
+        const int gp = p.gpack < 2 ? p.gpack : 2;
+        const int rpw = 64 / gp;
+        const int R = (p.Sq + rpw - 1) / rpw;
+        if (R >= 2) {
+            p.gpack = gp;
+            p.rows_per_wg = rpw;
+            p.fold = R;
+            p.n_row_blocks = (R + 1) / 2;
+            p.n_units = p.B * p.Hkv * (p.G / gp);
+            p.xcd_remap = p.n_units % 8 == 0 ? 1 : 0;
+            wgs = p.n_units * p.n_row_blocks;
+        }
+    }
+    set_divisors(p);
     // Head dim 128 with few 64-key tiles per workgroup on average (a masked
     // row sees causal_off + its index + 1 keys, on average causal_off + Sq / 2):
     // the sequential form at three workgroups per CU (measured: causal

@@ -81,6 +81,12 @@ struct FwdParams {
     FastDiv div_ranks, div_per, div_units, div_split, div_groups, div_hkv;
     int hs_log2, gpack_log2;
     int unit_major;     // with xcd_remap: an XCD runs its units one after another (see map_workgroup)
+    // 0, or R >= 2: folded row blocks. The workgroup's slots with a row
+    // offset below rows_per_wg hold row block rb of R blocks of rows_per_wg
+    // rows, the others block R - 1 - rb (none when that is rb itself), and
+    // n_row_blocks = ceil(R / 2). Under a causal mask the two blocks' key
+    // counts add up to about the same for every workgroup.
+    int fold;
 };
 
 // Fills the divisor fields from the shape fields (host side; call after the
@@ -159,7 +165,9 @@ struct BwdParams {
 
 struct WorkItem {
     int b, hkv, hq0;    // batch, KV head, first query head of the workgroup
-    int row_base;       // first query row of the workgroup
+    int row_base;       // first query row of the workgroup (of its first row block)
+    int row_hi;         // folded: first row of the second row block minus rows_per_wg; else row_base
+    int row_end;        // one past the workgroup's last query row (not clamped to Sq)
     int split;          // which of the n_split key ranges
 };
 
@@ -205,8 +213,24 @@ __device__ inline WorkItem map_workgroup(const FwdParams& p, bool causal) {
     w.hkv = t - w.b * p.Hkv;
     w.hq0 = w.hkv * p.G + hgrp * p.gpack;
     w.row_base = rb * p.rows_per_wg;
+    w.row_hi = w.row_base;
+    w.row_end = w.row_base + p.rows_per_wg;
+    if (p.fold) {
+        // The mirror block; for the middle block of an odd R the second
+        // half's rows start at Sq (no work).
+        const int rb2 = p.fold - 1 - rb;
+        w.row_hi = (rb2 > rb ? rb2 * p.rows_per_wg : p.Sq) - p.rows_per_wg;
+        if (rb2 > rb) w.row_end = (rb2 + 1) * p.rows_per_wg;
+    }
     w.split = split;
     return w;
+}
+
+// Query row of slot s of a workgroup (see slot_row; slots of the second
+// half of a folded workgroup belong to its second row block).
+__device__ inline int item_row(const FwdParams& p, const WorkItem& w, int s) {
+    const int r = slot_row(p, s);
+    return (r < p.rows_per_wg ? w.row_base : w.row_hi) + r;
 }
 
 // The values of lanes l and l ^ 32 of a 64-wide wavefront, as (a, b) in some

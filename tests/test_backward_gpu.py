@@ -62,6 +62,8 @@ LSE_CASES = [
     W("f16", 1, 8, 2, 100, 100, 128, True),
     W("e4m3", 1, 4, 2, 150, 150, 128, True),
     W("e4m3", 1, 4, 1, 9, 300, 64, "bottom_right"),
+    W("bf16", 1, 4, 2, 600, 600, 128, True),        # forward with folded row blocks
+    W("f16", 1, 2, 2, 700, 900, 64, "bottom_right"),
 ]
 
 

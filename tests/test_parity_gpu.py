@@ -26,7 +26,8 @@ pytestmark = pytest.mark.gpu
 
 
 def W(dtype, B, Hq, Hkv, Sq, Skv, D, causal, seed=7):
-    name = f"{dtype}_b{B}_hq{Hq}_hkv{Hkv}_sq{Sq}_skv{Skv}_d{D}{'_causal' if causal else ''}"
+    tag = {False: "", True: "_causal", "bottom_right": "_br"}[causal]
+    name = f"{dtype}_b{B}_hq{Hq}_hkv{Hkv}_sq{Sq}_skv{Skv}_d{D}{tag}"
     return Workload(name, dtype, B, Hq, Hkv, Sq, Skv, D, causal, seed)
 
 
@@ -85,10 +86,13 @@ SMALL = [
     W("e4m3", 2, 8, 2, 192, 192, 128, True),
     W("f16", 2, 2, 1, 256, 256, 64, False),
     # Grids of fewer than 384 workgroups with at least 8 key tiles run with two
-    # key halves per workgroup (waves w and w + 4 take alternate tiles and merge
-    # at the end): odd and even tile counts, a half without tiles of its own
-    # (top-left causal, 10 rows against 1000 keys: one tile in all), rows of
-    # several heads per wave (decode shapes), E4M3, f16 head dim 32, no mask.
+    # key halves per workgroup (waves 2 w and 2 w + 1 take alternate tiles and
+    # merge at the end): odd and even tile counts, a half without tiles of its
+    # own (top-left causal, 10 rows against 1000 keys: one tile in all), rows
+    # of several heads per wave (decode shapes), E4M3, f16 head dim 32, no
+    # mask. Causal 16-bit shapes with at least 32 rows per head fold the row
+    # blocks (blocks r and R - 1 - r in one workgroup): R even and odd (the
+    # middle workgroup's second block empty), MQA, bottom-right alignment.
     W("bf16", 1, 4, 4, 545, 545, 128, True),       # 9 tiles
     W("bf16", 1, 8, 2, 600, 600, 64, True),
     W("bf16", 1, 4, 2, 10, 1000, 128, True),        # one tile: half 1 idle
@@ -98,6 +102,9 @@ SMALL = [
     W("f16", 1, 4, 4, 600, 600, 32, True),
     W("e4m3", 1, 4, 2, 600, 600, 128, True),
     W("e4m3", 1, 2, 2, 100, 1000, 64, False),
+    W("bf16", 1, 8, 1, 1000, 1000, 128, True),      # folded: 32 blocks of 32 rows x 2 heads
+    W("bf16", 1, 4, 2, 600, 1000, 128, "bottom_right"),   # folded, R = 19
+    W("bf16", 1, 2, 2, 650, 650, 64, True),         # folded, R = 11 (64-row blocks)
 ]
 
 
