@@ -874,8 +874,14 @@ template <typename T, int D, int BN>
 static hipError_t launch_typed(const FwdParams& p0, bool causal, hipStream_t stream) {
     FwdParams p = p0;
     int wgs = p.n_units * p.n_row_blocks * p.n_split;
-    const bool halves = p.n_split == 1 && wgs * 2 < kComputeUnits * 3 && (p.Skv + BN - 1) / BN >= 8;
-    if (halves && causal && Traits<T>::V_DMA && p.head_stride == 32) {
+    // Key tiles of one key range (all of them without a split). Split-key
+    // launches take the key halves only with long ranges (at least 32
+    // tiles): measured on decode shapes (GQA one query against 16K to 64K
+    // keys -4 to -37 %), while 16-tile ranges whose four waves all hold
+    // rows lose up to 9 % to the merge.
+    const int range_tiles = ((p.Skv + BN - 1) / BN + p.n_split - 1) / p.n_split;
+    const bool halves = wgs * 2 < kComputeUnits * 3 && range_tiles >= (p.n_split == 1 ? 8 : 32);
+    if (halves && causal && Traits<T>::V_DMA && p.head_stride == 32 && p.n_split == 1) {
         // Causal key halves fold the row blocks: blocks of 64 / gpack rows
         // (gpack at most 2, so a wave still holds 32 rows of one head), two
         // mirror blocks per workgroup, the same number of workgroups.

@@ -80,6 +80,12 @@ SPLIT = [
     (W("bf16", 1, 4, 1, 64, 640, 128, "bottom_right"), (10, 40)),  # more ranges than some rows have tiles
     (W("f16", 2, 8, 1, 3, 333, 64, "bottom_right"), (3, 6)),
     (W("bf16", 2, 16, 4, 1, 2000, 32, "bottom_right"), (4, 11)),
+    # Small split grids with ranges of at least 32 key tiles take the key
+    # halves (two waves per query slot, merged before the partial is written).
+    (W("bf16", 1, 8, 2, 1, 4500, 128, "bottom_right"), (2, 3)),    # 36 tiles per range at 2, 24 at 3
+    (W("f16", 2, 4, 1, 3, 4200, 64, "bottom_right"), (2,)),
+    (W("bf16", 1, 4, 4, 20, 4100, 32, False), (2,)),
+    (W("bf16", 1, 4, 2, 300, 4400, 128, True), (2,)),    # top-left: the rows see 5 tiles, a half may get none
 ]
 
 
