@@ -865,9 +865,10 @@ __global__ __launch_bounds__(64 * NWAVES, RB == 1 ? (BN == 32 ? 3 : 8 / NWAVES) 
 
 // MI355X has 256 compute units; the four-wave kernel runs two workgroups
 // per CU. A launch with fewer than 1.5 workgroups per CU leaves SIMDs with a
-// single wave (nothing hides its stalls) or none; then, if a row block has
-// at least 8 key tiles, the key halves (KS = 2: eight waves per workgroup,
-// one workgroup per CU, two waves per SIMD) halve each wave's chain of tiles.
+// single wave (nothing hides its stalls) or none; then, if a row block (or,
+// with split keys, a key range) has enough key tiles, the key halves (KS = 2:
+// eight waves per workgroup, one workgroup per CU, two waves per SIMD) halve
+// each wave's chain of tiles.
 constexpr int kComputeUnits = 256;
 
 template <typename T, int D, int BN>
