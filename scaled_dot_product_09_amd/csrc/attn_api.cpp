@@ -67,7 +67,6 @@ attn::FwdParams make_params(const void* q, const void* k, const void* v, void* o
     // Bottom-right alignment shifts every query to position Skv - Sq + i.
     p.causal_off = causal == 2 ? Skv - Sq : 0;
     p.n_split = 1;
-    p.fold = 0;
     p.part_o = nullptr;
     p.part_ml = nullptr;
     p.lse = nullptr;
@@ -75,32 +74,7 @@ attn::FwdParams make_params(const void* q, const void* k, const void* v, void* o
     p.q = q; p.k = k; p.v = v; p.out = out;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Sq = Sq; p.Skv = Skv;
     p.G = Hq / Hkv;
-    // A workgroup of `waves` waves shares one KV head between gpack query
-    // heads and covers rows_per_wave * waves / gpack rows of each. gpack is
-    // the largest of 4, 2, 1 dividing G. The matrix-core kernel
-    // (wide_heads), whose MFMA columns may mix heads, doubles it while G
-    // allows and the heads' Sq rows still fit the workgroup's slots
-    // (gpack * Sq <= rows_per_wave * waves): with few query rows (decode
-    // with GQA / MQA) the slots then hold rows of many heads instead of
-    // empty rows of one.
-    p.gpack = mfma ? ((p.G % 4 == 0) ? 4 : (p.G % 2 == 0) ? 2 : 1) : 1;
-    if (mfma && wide_heads) {
-        const int slots = rows_per_wave * waves;
-        while (p.G % (2 * p.gpack) == 0 && 2 * p.gpack <= slots && (int64_t)2 * p.gpack * Sq <= slots)
-            p.gpack *= 2;
-    }
-    p.rows_per_wg = rows_per_wave * waves / p.gpack;
-    // Slot map of the matrix-core kernel: runs of head_stride
-    // consecutive rows of one head, heads interleaved between runs. 32 (one
-    // head per wave, 32 rows) when there are that many rows; with fewer
-    // rows, the smallest power of two >= Sq, so the rows of all gpack heads
-    // sit in the first waves and the rest have no work.
-    int hs = 1;
-    while (hs < Sq && hs < 32) hs *= 2;
-    p.head_stride = hs < p.rows_per_wg ? hs : p.rows_per_wg;
-    p.n_row_blocks = (Sq + p.rows_per_wg - 1) / p.rows_per_wg;
-    p.n_units = B * Hkv * (p.G / p.gpack);
-    p.xcd_remap = (p.n_units % 8 == 0) ? 1 : 0;
+    attn::set_slot_map(p, mfma, rows_per_wave, waves, wide_heads);
     p.scale_log2 = scale_log2;
     p.out_mul = out_mul;
     return p;

@@ -882,23 +882,10 @@ static hipError_t launch_typed(const FwdParams& p0, bool causal, hipStream_t str
     // rows lose up to 9 % to the merge.
     const int range_tiles = ((p.Skv + BN - 1) / BN + p.n_split - 1) / p.n_split;
     const bool halves = wgs * 2 < kComputeUnits * 3 && range_tiles >= (p.n_split == 1 ? 8 : 32);
-    if (halves && causal && Traits<T>::V_DMA && p.head_stride == 32 && p.n_split == 1) {
-        // Causal key halves fold the row blocks: blocks of 64 / gpack rows
-        // (gpack at most 2, so a wave still holds 32 rows of one head), two
-        // mirror blocks per workgroup, the same number of workgroups.
-        const int gp = p.gpack < 2 ? p.gpack : 2;
-        const int rpw = 64 / gp;
-        const int R = (p.Sq + rpw - 1) / rpw;
-        if (R >= 2) {
-            p.gpack = gp;
-            p.rows_per_wg = rpw;
-            p.fold = R;
-            p.n_row_blocks = (R + 1) / 2;
-            p.n_units = p.B * p.Hkv * (p.G / gp);
-            p.xcd_remap = p.n_units % 8 == 0 ? 1 : 0;
-            wgs = p.n_units * p.n_row_blocks;
-        }
-    }
+    // Causal key halves fold the row blocks (see fold_row_blocks): two mirror
+    // blocks per workgroup, the same number of workgroups.
+    if (halves && causal && Traits<T>::V_DMA && p.n_split == 1 && fold_row_blocks(p))
+        wgs = p.n_units * p.n_row_blocks;
     set_divisors(p);
     // Head dim 128 with few 64-key tiles per workgroup on average (a masked
     // row sees causal_off + its index + 1 keys, on average causal_off + Sq / 2):

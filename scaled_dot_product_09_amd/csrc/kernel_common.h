@@ -89,6 +89,56 @@ struct FwdParams {
     int fold;
 };
 
+// Slot map of a launch (host side; from B, Hkv, G and Sq): a workgroup of
+// `waves` waves of rows_per_wave query slots shares one KV head between
+// gpack query heads and covers rows_per_wave * waves / gpack rows of each.
+// gpack is the largest of 4, 2, 1 dividing G (1 without the matrix cores).
+// The matrix-core kernel (wide_heads), whose MFMA columns may mix heads,
+// doubles it while G allows and the heads' Sq rows still fit the
+// workgroup's slots (gpack * Sq <= rows_per_wave * waves): with few query
+// rows (decode with GQA / MQA) the slots then hold rows of many heads
+// instead of empty rows of one. Slots come in runs of head_stride
+// consecutive rows of one head, heads interleaved between runs: 32 (one
+// head per wave, 32 rows) when there are that many rows; with fewer rows,
+// the smallest power of two >= Sq, so the rows of all gpack heads sit in
+// the first waves and the rest have no work. No folding.
+inline void set_slot_map(FwdParams& p, bool mfma, int rows_per_wave, int waves, bool wide_heads) {
+    p.gpack = mfma ? ((p.G % 4 == 0) ? 4 : (p.G % 2 == 0) ? 2 : 1) : 1;
+    if (mfma && wide_heads) {
+        const int slots = rows_per_wave * waves;
+        while (p.G % (2 * p.gpack) == 0 && 2 * p.gpack <= slots && (int64_t)2 * p.gpack * p.Sq <= slots)
+            p.gpack *= 2;
+    }
+    p.rows_per_wg = rows_per_wave * waves / p.gpack;
+    int hs = 1;
+    while (hs < p.Sq && hs < 32) hs *= 2;
+    p.head_stride = hs < p.rows_per_wg ? hs : p.rows_per_wg;
+    p.n_row_blocks = (p.Sq + p.rows_per_wg - 1) / p.rows_per_wg;
+    p.n_units = p.B * p.Hkv * (p.G / p.gpack);
+    p.xcd_remap = (p.n_units % 8 == 0) ? 1 : 0;
+    p.fold = 0;
+}
+
+// Folded row blocks for the four-query-wave (128-slot) map of set_slot_map
+// (host side): blocks of 64 / gpack rows with gpack at most 2, so that a
+// wave still holds 32 rows of one head, two mirror blocks per workgroup,
+// the same number of workgroups. Needs runs of 32 rows (head_stride 32) and
+// at least two blocks; returns whether it folded.
+inline bool fold_row_blocks(FwdParams& p) {
+    if (p.head_stride != 32 || p.rows_per_wg * p.gpack != 128) return false;
+    const int gp = p.gpack < 2 ? p.gpack : 2;
+    const int rpw = 64 / gp;
+    const int R = (p.Sq + rpw - 1) / rpw;
+    if (R < 2) return false;
+    p.gpack = gp;
+    p.rows_per_wg = rpw;
+    p.fold = R;
+    p.n_row_blocks = (R + 1) / 2;
+    p.n_units = p.B * p.Hkv * (p.G / gp);
+    p.xcd_remap = p.n_units % 8 == 0 ? 1 : 0;
+    return true;
+}
+
 // Fills the divisor fields from the shape fields (host side; call after the
 // last change to n_units, n_split, G, gpack, Hkv or head_stride).
 inline void set_divisors(FwdParams& p) {
@@ -114,10 +164,10 @@ inline void set_divisors(FwdParams& p) {
 // Query slot s of a matrix-core workgroup: head offset (s / HS) % gpack and
 // row offset (s / (HS gpack)) HS + s % HS from the workgroup's first head and
 // row (see the slot map of the kernels; HS = head_stride).
-__device__ inline int slot_head(const FwdParams& p, int s) {
+__host__ __device__ inline int slot_head(const FwdParams& p, int s) {
     return (s >> p.hs_log2) & ((1 << p.gpack_log2) - 1);
 }
-__device__ inline int slot_row(const FwdParams& p, int s) {
+__host__ __device__ inline int slot_row(const FwdParams& p, int s) {
     return ((s >> (p.hs_log2 + p.gpack_log2)) << p.hs_log2) + (s & ((1 << p.hs_log2) - 1));
 }
 
@@ -182,8 +232,7 @@ struct WorkItem {
 // one before the next, so that about one unit's K and V are live in its L2
 // at a time; otherwise it interleaves them (every unit's longest row block
 // first).
-__device__ inline WorkItem map_workgroup(const FwdParams& p, bool causal) {
-    const int pid = (int)__builtin_amdgcn_workgroup_id_x();
+__host__ __device__ inline WorkItem map_item(const FwdParams& p, bool causal, int pid) {
     int rank, unit;
     if (p.xcd_remap) {
         const int per = p.n_units >> 3;
@@ -226,9 +275,14 @@ __device__ inline WorkItem map_workgroup(const FwdParams& p, bool causal) {
     return w;
 }
 
+// The calling workgroup's item.
+__device__ inline WorkItem map_workgroup(const FwdParams& p, bool causal) {
+    return map_item(p, causal, (int)__builtin_amdgcn_workgroup_id_x());
+}
+
 // Query row of slot s of a workgroup (see slot_row; slots of the second
 // half of a folded workgroup belong to its second row block).
-__device__ inline int item_row(const FwdParams& p, const WorkItem& w, int s) {
+__host__ __device__ inline int item_row(const FwdParams& p, const WorkItem& w, int s) {
     const int r = slot_row(p, s);
     return (r < p.rows_per_wg ? w.row_base : w.row_hi) + r;
 }
