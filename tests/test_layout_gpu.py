@@ -94,6 +94,22 @@ def test_strided_matches_dense_bitwise():
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("dtype,D,Sq,Skv,causal", [("bf16", 128, 700, 700, True), ("f16", 64, 600, 900, "bottom_right")])
+def test_strided_small_grid_key_halves(dtype, D, Sq, Skv, causal):
+    """Transposed storage on a grid small enough for the key halves, whose
+    causal form folds the row blocks (mirror blocks in one workgroup): the
+    oracle's result within the bound, and bitwise the dense call's."""
+    B, Hq, Hkv = 1, 4, 2
+    dev = "cuda:0"
+    q = _rand(12, (B, Hq, Sq, D), dtype).to(dev).transpose(1, 2)
+    k = _rand(13, (B, Hkv, Skv, D), dtype).to(dev).transpose(1, 2)
+    v = _rand(14, (B, Hkv, Skv, D), dtype).to(dev).transpose(1, 2)
+    a = _check(dtype, q, k, v, None, causal)
+    b = attn.fwd(q.contiguous(), k.contiguous(), v.contiguous(), causal=causal, scale=1.0 / np.sqrt(D))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
 def test_strided_rejections():
     dev = "cuda:0"
     q = torch.zeros(1, 16, 2, 64, dtype=torch.bfloat16, device=dev)

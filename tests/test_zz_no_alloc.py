@@ -48,6 +48,8 @@ CASES = [
     (Workload("mqa_decode", "bf16", 32, 32, 1, 4, 8192, 128, "bottom_right", 21), 8),
     (Workload("gqa_small", "bf16", 2, 8, 2, 3, 1000, 128, "bottom_right", 22), 3),
     (Workload("mha_f16_d64", "f16", 1, 4, 4, 70, 700, 64, True, 23), 2),
+    # two ranges of 36 key tiles on a four-workgroup grid: the key halves
+    (Workload("gqa_long_ranges", "bf16", 1, 8, 2, 1, 4500, 128, "bottom_right", 24), 2),
 ]
 
 
